@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's routed-expert MoE layer (forward + backward).
+
+One step is the whole path over one batch of synthetic tokens, as a sequence
+of C-ABI calls on one stream: route -> permute -> grouped GEMM forward (fc1 +
+SwiGLU, fc2) [+ shared expert] -> weighted combine -> combine backward
+(scaled permute of dY) -> grouped GEMM backward (dgrad fc2 + SwiGLU backward,
+dgrad fc1, wgrad fc2, wgrad fc1) [+ shared expert] -> un-permute of dXp.
+Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the layer's algorithmic GEMM TFLOP/s over
+the whole step (18*d*f per routed row, plus the shared expert).  `roofline`
+is for the grouped-GEMM kernel (all its launches in a step): algorithmic
+flop / their summed duration, measured with HIP events on the launch stream.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE layer fwd+bwd TFLOPS/GPU & % MFMA peak; permute/combine HBM GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_step(wl, inp):
+    import torch
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd.buffers import layer_buffers
+
+    sh, b, wsf, _ = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp)
+    shared = None
+    if wl.f_shared:
+        fs = wl.f_shared
+        sh_s = tre.make_shape(wl.T, wl.d, 1, 1, fs, 0, wl.dtype)
+        off_s = torch.tensor([0, wl.T], dtype=torch.int32, device="cuda")
+        shared = (sh_s, off_s)
+
+    def step(ev):
+        ev[0].record()
+        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        ev[1].record()
+        tre.moe_permute(sh, b["x"], b["topk_idx"], None, 1, b["counts"], b["offsets"], b["row_of"],
+                        b["token_of"], b["xp"], wsf)
+        ev[2].record()
+        tre.moe_grouped_gemm_fwd(sh, b["offsets"], b["xp"], b["W1"], b["W3"], b["W2"], b["ab"],
+                                 b["h"], b["o"])
+        if shared:
+            tre.moe_grouped_gemm_fwd(shared[0], shared[1], b["x"], b["Ws1"], b["Ws3"], b["Ws2"],
+                                     b["s_ab"], b["s_h"], b["ys"])
+        ev[3].record()
+        tre.moe_unpermute(sh, b["o"], b["row_of"], b["topk_prob"], b.get("ys"), b["y"])
+        ev[4].record()
+        tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
+                        b["dO"], None)
+        ev[5].record()
+        tre.moe_grouped_gemm_bwd(sh, b["offsets"], b["xp"], b["ab"], b["h"], b["dO"], b["W1"],
+                                 b["W3"], b["W2"], b["dab"], b["dXp"], b["dW1"], b["dW3"], b["dW2"])
+        if shared:
+            tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
+                                     b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
+                                     b["dWs3"], b["dWs2"])
+        ev[6].record()
+        tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
+        ev[7].record()
+
+    return step
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The fp64 oracle, unchanged, on a bounded sample: routing and the
+    permutation map of all T tokens, then the SwiGLU forward and backward of
+    whole experts in index order until `budget_s` seconds of expert compute."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from moe_workloads import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L = inp["logits"].cpu().numpy()
+    t0 = time.perf_counter()
+    idx, p = oracle.route(L, wl.k)
+    counts, offsets, row_of, token_of = oracle.permute_map(idx, wl.E)
+    t_route = time.perf_counter() - t0
+    p_rows = p.reshape(-1)[np.argsort(row_of.reshape(-1))]
+    flops = 0.0
+    t_exp = 0.0
+    n_exp = 0
+    rows_done = 0
+    for e in range(wl.E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        toks = torch.from_numpy(token_of[r0:r1]).to(inp["x"].device)
+        X = to_f64(inp["x"][toks])
+        dO = p_rows[r0:r1, None] * to_f64(inp["dY"][toks])
+        W1, W3, W2 = (to_f64(inp[n][e]) for n in ("W1", "W3", "W2"))
+        t0 = time.perf_counter()
+        a, b, h, o = oracle.swiglu_fwd(X, W1, W3, W2)
+        oracle.swiglu_bwd(X, a, b, h, dO, W1, W3, W2)
+        t_exp += time.perf_counter() - t0
+        flops += 18.0 * wl.d * wl.f * (r1 - r0)
+        n_exp += 1
+        rows_done += r1 - r0
+        if t_exp >= budget_s:
+            break
+    return {
+        "value": round(flops / t_exp / 1e12, 6) if t_exp > 0 else None,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: route + permutation map of all {wl.T} tokens "
+                   f"({t_route:.2f} s), then SwiGLU fwd+bwd of experts 0..{n_exp - 1} "
+                   f"({rows_done} of {wl.P} routed rows) in {t_exp:.1f} s; host has "
+                   f"{len(os.sched_getaffinity(0))} usable cores"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log(f"bench.py: this library is one GPU's share of the layer; --gpus {args.gpus} is not "
+            "supported (run with --gpus 1)")
+        sys.exit(2)
+
+    import torch
+
+    from moe_workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    if wl.dtype not in MFMA_PEAK_TFLOPS:
+        log(f"bench.py: workload {wl.name} ({wl.dtype}) is not supported by this build")
+        sys.exit(2)
+    log(f"bench: {wl}")
+    inp = make_inputs(wl, seed=0, device="cuda")
+    step = build_step(wl, inp)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    log(f"bench: warmup done ({args.warmup} steps)")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(ev[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    log(f"bench: timed {args.steps} steps, {ms_step:.3f} ms/step")
+
+    def seg(a, b_):
+        return sum(e[a].elapsed_time(e[b_]) for e in ev) / args.steps
+
+    t_route, t_perm, t_gf, t_comb, t_permb, t_gb, t_unp = (seg(i, i + 1) for i in range(7))
+    s = 4 if wl.dtype == "f32" else 2
+    flops = wl.flops_fwd_bwd()
+    gemm_ms = t_gf + t_gb
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    move_bytes = (wl.T * wl.d + wl.P * wl.d) * s
+    perm_gbs = (move_bytes + 16 * wl.P) / (t_perm * 1e-3) / 1e9
+    comb_gbs = (move_bytes + 8 * wl.P + (wl.T * wl.d * s if wl.f_shared else 0)) / (t_comb * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) logits and activations, N(0,1/fan_in) weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "f": wl.f,
+                   "f_shared": wl.f_shared},
+        "roofline": {"kernel": "grouped GEMM (all fwd+bwd launches of a step)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+        "breakdown_ms": {"route": round(t_route, 4), "permute": round(t_perm, 4),
+                         "gemm_fwd": round(t_gf, 4), "combine": round(t_comb, 4),
+                         "combine_bwd_permute": round(t_permb, 4), "gemm_bwd": round(t_gb, 4),
+                         "unpermute": round(t_unp, 4)},
+        "hbm": {"permute_GBps": round(perm_gbs, 1), "combine_GBps": round(comb_gbs, 1),
+                "permute_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
+                "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+/*
+ * moe.h -- C ABI of one GPU's routed-expert (mixture-of-experts) layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Scalable Training of Mixture-of-Experts Models with Megatron Core"
+ * (gist.science technical summaries).  The Spanish summary, section 2.1
+ * ("Arquitectura de la capa MoE"), splits the layer into four steps: route
+ * each token to its k best experts, dispatch the tokens to their experts,
+ * run the experts as grouped GEMMs, combine the results.  On one GPU dispatch
+ * and combine are a local permutation and a weighted un-permutation.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, row-major,
+ *    16-byte aligned, and not aliased with each other unless stated.  The
+ *    library never allocates or frees memory and keeps no state between
+ *    calls; scratch space is the caller's `ws` buffer of `ws_bytes` bytes
+ *    (size from moe_workspace_bytes).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return: no host synchronisation, no copy of
+ *    per-expert counts to the host (the German summary, section 2 D, and the
+ *    Spanish summary, section 2.3 C: kernels read shape information from GPU
+ *    memory, so dropless routing needs no CPU-GPU sync).  Calls are safe to
+ *    capture into a HIP graph.
+ *  - Return value: a moe_status.  Arguments are validated before anything is
+ *    enqueued; MOE_ERR_HIP reports a launch failure.  Faults inside kernels
+ *    surface at the caller's next synchronisation.  Nothing aborts or prints.
+ *  - Shapes: T tokens, d hidden size, E experts, k experts per token, f
+ *    expert FFN width, P = T*k routed rows (dropless: every assignment gets a
+ *    row, so permuted buffers always have exactly P rows -- the worst case is
+ *    known on the host; cf. the hyper.ai article on Hybrid-EP, which reserves
+ *    buffers for the worst case).  Limits: 1 <= k <= E <= 256, T >= 1,
+ *    P < 2^31.  The bf16 expert GEMMs need d and f to be multiples of 128.
+ *  - Expert weights: W1, W3 are [E][d][f], W2 is [E][f][d]; expert e maps a
+ *    row x to o = (silu(x W1_e) * (x W3_e)) W2_e with silu(z) = z / (1+e^-z).
+ *  - Dtypes: MOE_F32 (every tensor fp32) or MOE_BF16 (x, weights, outputs and
+ *    saved activations bf16, fp32 accumulation, one round-to-nearest-even per
+ *    output element).  Router logits and probabilities are always fp32
+ *    (German summary, section 2 E: the router stays in high precision).
+ */
+#ifndef TRE_MOE_H
+#define TRE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* null pointer, inconsistent or out-of-range sizes */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits (dtype, alignment) */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+  int64_t T, d, E, k, f;
+  int64_t f_shared;  /* width of an always-on shared expert, 0 = none */
+  int32_t dtype;     /* moe_dtype of x, weights, activations and outputs */
+  int32_t reserved;  /* must be 0 */
+} moe_shape;
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+  MOE_WS_PERMUTE = 0,
+  MOE_WS_GEMM_FWD = 1,
+  MOE_WS_GEMM_BWD = 2,
+  MOE_WS_LAYER_FWD = 3,
+  MOE_WS_LAYER_BWD = 4
+} moe_ws_kind;
+
+/*
+ * moe_route -- top-k routing (Spanish summary, section 2.1: a router assigns
+ * each token to its k best experts).
+ *   logits    fp32 [T][E], finite values (behaviour on NaN is unspecified).
+ *   topk_idx  out int32 [T][k]: the k largest logits of the token in
+ *             descending order; equal logits (IEEE equality, -0 == +0) are
+ *             ordered by lower expert index first.
+ *   topk_prob out fp32 [T][k]: softmax over the k selected logits,
+ *             p_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), summed in j order.
+ * Errors: MOE_ERR_INVALID for null pointers, T < 1, k < 1, k > E, E > 256.
+ */
+int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
+              int32_t* topk_idx, float* topk_prob, void* stream);
+
+/*
+ * moe_permute -- dispatch on one GPU: copy every token row to one row per
+ * assignment, in expert-contiguous order (Spanish summary, section 2.1,
+ * dispatch; German summary, section 1: dropless routing).
+ *   build_map = 1: from topk_idx [T][k] computes
+ *       counts   out int32 [E]   rows per expert;
+ *       offsets  out int32 [E+1] exclusive prefix sum, offsets[E] = P;
+ *       row_of   out int32 [T][k] destination row of assignment (t, j);
+ *       token_of out int32 [P]   source token of each row;
+ *     rows of one expert ascend by token index (a stable counting sort), so
+ *     the map is unique.  Needs ws_bytes >= moe_workspace_bytes(sh,
+ *     MOE_WS_PERMUTE).
+ *   build_map = 0: uses the caller's row_of; counts, offsets, token_of, ws
+ *     may be NULL.
+ *   src [T][d] and dst [P][d] are in sh->dtype.  row_scale NULL: dst rows are
+ *   bit copies of src rows.  row_scale fp32 [T][k] non-NULL: dst[row_of[t][j]]
+ *   = round(row_scale[t][j] * src[t]) computed in fp32 (the backward of the
+ *   weighted combine, dO = p * dY).
+ */
+int moe_permute(const moe_shape* sh, const void* src, const int32_t* topk_idx,
+                const float* row_scale, int build_map, int32_t* counts, int32_t* offsets,
+                int32_t* row_of, int32_t* token_of, void* dst, void* ws, size_t ws_bytes,
+                void* stream);
+
+/*
+ * moe_unpermute -- combine on one GPU (Spanish summary, section 2.1):
+ *   dst[t] = round( sum_{j=0..k-1} w[t][j] * src[row_of[t][j]] + add[t] )
+ * with the sum in fp32 in j order, w = topk_prob (fp32 [T][k]) or 1 when
+ * topk_prob is NULL (the backward of moe_permute), add [T][d] optional
+ * (NULL = none; used for the shared expert).  src [P][d], dst [T][d] in
+ * sh->dtype.  dst must not alias src.
+ */
+int moe_unpermute(const moe_shape* sh, const void* src, const int32_t* row_of,
+                  const float* topk_prob, const void* add, void* dst, void* stream);
+
+/*
+ * moe_grouped_gemm_fwd -- the experts' forward as grouped GEMMs over the
+ * expert-contiguous rows (German summary, section 2 D, and Spanish summary,
+ * section 2.3 C: one grouped GEMM bundles the many small expert GEMMs).
+ * For expert e and its rows r in [offsets[e], offsets[e+1]):
+ *   a = xp_r W1_e, b = xp_r W3_e           saved: ab [P][2f] = [a | b]
+ *   h = silu(a) * b                        saved: h  [P][f]
+ *   o = h W2_e                             out:   o  [P][d]
+ * offsets int32 [E+1] lives on the device (typically from moe_permute); the
+ * kernels read it there.  Rows of experts with no tokens are not touched.
+ * ws may be NULL (current kernels need no workspace).
+ */
+int moe_grouped_gemm_fwd(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                         const void* W1, const void* W3, const void* W2, void* ab, void* h,
+                         void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd -- data and weight gradients of moe_grouped_gemm_fwd,
+ * as separate products (German summary, section 2 C: W/D split).  Inputs are
+ * the forward's xp, ab, h and the upstream gradient dO [P][d]; outputs:
+ *   dab [P][2f] = [da | db],  dH = dO W2_e^T, s = sigmoid(a),
+ *                 da = dH * b * s * (1 + a (1 - s)), db = dH * silu(a)
+ *   dXp [P][d]  = da W1_e^T + db W3_e^T
+ *   dW2 [E][f][d] = h_e^T dO_e, dW1 = xp_e^T da_e, dW3 = xp_e^T db_e
+ * (each accumulated in fp32 over all of the expert's rows, rounded once).
+ * Experts with no rows get all-zero dW1, dW3, dW2.
+ */
+int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                         const void* ab, const void* h, const void* dO, const void* W1,
+                         const void* W3, const void* W2, void* dab, void* dXp, void* dW1,
+                         void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Buffers of a whole layer.  Inputs are read-only; "saved" buffers are
+ * written by moe_layer_fwd and read by moe_layer_bwd; the rest are outputs.
+ * Shared-expert pointers are ignored when f_shared == 0.
+ */
+typedef struct {
+  /* inputs */
+  const float* logits;                    /* fp32 [T][E] */
+  const void* x;                          /* [T][d] */
+  const void *W1, *W3, *W2;               /* [E][d][f], [E][d][f], [E][f][d] */
+  const void *Ws1, *Ws3, *Ws2;            /* shared expert [d][fs], [d][fs], [fs][d] */
+  const void* dY;                         /* [T][d], backward only */
+  /* routing (written by fwd) */
+  int32_t* topk_idx;                      /* [T][k] */
+  float* topk_prob;                       /* [T][k] */
+  int32_t *counts, *offsets;              /* [E], [E+1] */
+  int32_t *row_of, *token_of;             /* [T][k], [P] */
+  /* saved activations (written by fwd) */
+  void *xp, *ab, *h, *o;                  /* [P][d], [P][2f], [P][f], [P][d] */
+  void *s_ab, *s_h, *ys;                  /* shared expert: [T][2fs], [T][fs], [T][d] */
+  /* forward output */
+  void* y;                                /* [T][d] */
+  /* backward scratch and outputs */
+  void *dO, *dab, *dXp;                   /* [P][d], [P][2f], [P][d] */
+  void *s_dab, *dXs;                      /* shared expert: [T][2fs], [T][d] */
+  void* dX;                               /* [T][d] */
+  void *dW1, *dW3, *dW2;                  /* like W1, W3, W2 */
+  void *dWs1, *dWs3, *dWs2;               /* like Ws1, Ws3, Ws2 */
+} moe_layer_io;
+
+/*
+ * moe_layer_fwd -- route, permute, expert forward (+ shared expert applied to
+ * every token with weight 1), weighted combine into y.  Same as calling
+ * moe_route, moe_permute(build_map=1), moe_grouped_gemm_fwd and
+ * moe_unpermute in sequence on one stream.
+ */
+int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * moe_layer_bwd -- backward of moe_layer_fwd for upstream gradient dY:
+ * dO = p * dY permuted, expert backward, dX = un-permuted sum of dXp (+ the
+ * shared expert's dXs), and all weight gradients.  No gradient flows to the
+ * logits, which are an input of the layer.
+ */
+int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
+size_t moe_workspace_bytes(const moe_shape* sh, int kind);
+
+/* Static, NUL-terminated name of a moe_status value. */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRE_MOE_H */

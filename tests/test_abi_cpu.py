@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, and rejects bad arguments before touching the device."""
+import ctypes as C
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from token_routed_expert_amd import _native as N
+from token_routed_expert_amd import make_shape, moe_status_str, moe_workspace_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_unpermute", "moe_grouped_gemm_fwd",
+            "moe_grouped_gemm_bwd", "moe_layer_fwd", "moe_layer_bwd"} <= names
+    lib = N.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(N.exported_names()) == names
+
+
+def test_library_carries_gfx950_code_objects():
+    assert b"amdgcn-amd-amdhsa--gfx950" in open(N.LIB_PATH, "rb").read()
+
+
+def test_status_strings():
+    assert moe_status_str(0) == "MOE_OK"
+    assert moe_status_str(2) == "MOE_ERR_UNSUPPORTED"
+    assert moe_status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    sh = make_shape(8192, 4096, 128, 8, 1536)
+    assert moe_workspace_bytes(sh, N.MOE_WS_PERMUTE) == 128 * 32 * 4
+    assert moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD) == 128 * 32 * 4 + 256
+    assert moe_workspace_bytes(sh, N.MOE_WS_GEMM_FWD) == 0
+    bad = make_shape(8192, 4096, 128, 200, 1536)           # k > E
+    assert moe_workspace_bytes(bad, N.MOE_WS_PERMUTE) == 0
+
+
+P = C.c_void_p(16)  # a non-null dummy: the calls below must fail before any use
+
+
+@pytest.mark.parametrize("T,E,k,expect", [(0, 8, 2, 1), (4, 8, 0, 1), (4, 8, 9, 1), (4, 300, 2, 2)])
+def test_route_rejects(T, E, k, expect):
+    assert N.lib().moe_route(P, T, E, k, P, P, None) == expect
+
+
+def test_route_rejects_null():
+    assert N.lib().moe_route(None, 4, 8, 2, P, P, None) == N.MOE_ERR_INVALID
+
+
+@pytest.mark.parametrize("shape,expect", [
+    (dict(T=4, d=128, E=8, k=2, f=128, dtype="bf16"), None),
+    (dict(T=4, d=100, E=8, k=2, f=128, dtype="bf16"), N.MOE_ERR_UNSUPPORTED),   # 16-byte rows
+    (dict(T=4, d=128, E=8, k=9, f=128, dtype="bf16"), N.MOE_ERR_INVALID),
+    (dict(T=4, d=128, E=512, k=2, f=128, dtype="bf16"), N.MOE_ERR_UNSUPPORTED),
+])
+def test_permute_validation(shape, expect):
+    sh = make_shape(**shape)
+    lib = N.lib()
+    st = lib.moe_permute(C.byref(sh), P, P, None, 1, P, P, P, P, P, P, 0, None)
+    assert st == (N.MOE_ERR_WORKSPACE if expect is None else expect)
+    assert lib.moe_permute(C.byref(sh), None, P, None, 0, None, None, P, None, P, None, 0, None) in (
+        N.MOE_ERR_INVALID, expect)
+
+
+def test_gemm_validation():
+    lib = N.lib()
+    sh = make_shape(64, 256, 8, 2, 200, 0, "bf16")                 # f not a multiple of 128
+    assert lib.moe_grouped_gemm_fwd(C.byref(sh), P, P, P, P, P, P, P, P, None, 0, None) == \
+        N.MOE_ERR_UNSUPPORTED
+    sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    assert lib.moe_grouped_gemm_fwd(C.byref(sh), None, P, P, P, P, P, P, P, None, 0, None) == \
+        N.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_bwd(C.byref(sh), P, P, P, P, P, P, P, P, P, P, P, P, None, None, 0,
+                                    None) == N.MOE_ERR_INVALID
+    bad = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    bad.reserved = 1
+    assert lib.moe_grouped_gemm_fwd(C.byref(bad), P, P, P, P, P, P, P, P, None, 0, None) == \
+        N.MOE_ERR_INVALID
+    bad = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    bad.dtype = 7
+    assert lib.moe_unpermute(C.byref(bad), P, P, None, None, P, None) == N.MOE_ERR_UNSUPPORTED
+
+
+def test_layer_validation():
+    lib = N.lib()
+    sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    io = N.moe_layer_io()
+    assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 20, None) == N.MOE_ERR_INVALID
+    assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 20, None) == N.MOE_ERR_INVALID
+    for name in N.IO_FIELDS:
+        setattr(io, name, 16)
+    assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 8, None) == N.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), None, 0, None) == N.MOE_ERR_WORKSPACE
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The package and the oracle share no code and neither imports the other."""
+    pkg = os.path.join(ROOT, "token_routed_expert_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
+            assert "oracle" not in open(path).read().replace("oracles", ""), path
+    for path in glob.glob(os.path.join(ROOT, "oracle", "*.py")):
+        assert "token_routed_expert_amd" not in open(path).read(), path

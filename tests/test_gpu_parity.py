@@ -1,0 +1,265 @@
+"""GPU path vs the oracle, through the C ABI, on seeded synthetic inputs.
+
+Small workloads are compared element by element on every output; the
+full-size workloads (the launch configuration the benchmark times) compare
+routing and permutation in full and the floating-point outputs on sampled
+tokens and experts, which the oracle computes one by one.
+Tolerances (max over rows of max|gpu-ref| / max|ref|): fp32 1e-4, bf16 2e-2;
+routing indices, counts, offsets, row maps and permuted rows bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_workloads import WORKLOADS, Workload, make_inputs, skew_bias, tied_logits, to_f64
+
+from gpu_common import (PROB_TOL, TOL, announce, assert_close, bits, check_routing_and_map,
+                        host_inputs, need_gpu, oracle_layer, run_layer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu(request):
+    need_gpu()
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (3, 2), (5, 5), (8, 2), (16, 4), (33, 7), (64, 8),
+                                 (100, 8), (128, 8), (200, 6), (256, 8), (256, 1)])
+@pytest.mark.parametrize("tied", [False, True])
+def test_route_bit_exact(E, k, tied):
+    import token_routed_expert_amd as tre
+    T = 1000
+    L = tied_logits(T, E, levels=3, seed=E) if tied else torch.randn(
+        T, E, generator=torch.Generator().manual_seed(E))
+    if tied:
+        L[::7] = 0.0
+        L[3::7, :] = -0.0       # +0 / -0 ties
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    prob = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    tre.moe_route(L.cuda(), k, idx, prob)
+    ridx, rp = oracle.route(L.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(prob.cpu().numpy() - rp).max() <= PROB_TOL
+
+
+# ---------------------------------------------------------------- permute / combine
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,E,k,d", [(1, 4, 2, 64), (257, 8, 2, 128), (1000, 128, 8, 256),
+                                     (513, 256, 8, 64), (300, 16, 16, 32)])
+def test_permute_unpermute(dtype, T, E, k, d):
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    sh = tre.make_shape(T, d, E, k, 128, 0, dtype)
+    g = torch.Generator().manual_seed(T + E)
+    L = torch.randn(T, E, generator=g)
+    L[:, 0] -= 100.0                                        # expert 0 gets no rows
+    x = torch.randn(T, d, generator=g).to(dt)
+    dY = torch.randn(T, d, generator=g).to(dt)
+    ridx, rp = oracle.route(L.numpy(), k)
+    counts, offsets, row_of, token_of = oracle.permute_map(ridx, E)
+    idx = torch.from_numpy(ridx).cuda()
+    P = T * k
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    r = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    tk = torch.empty(P, dtype=torch.int32, device="cuda")
+    xp = torch.empty(P, d, dtype=dt, device="cuda")
+    ws = torch.empty(tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE), dtype=torch.uint8, device="cuda")
+    tre.moe_permute(sh, x.cuda(), idx, None, 1, c, o, r, tk, xp, ws)
+    assert np.array_equal(c.cpu().numpy(), counts) and np.array_equal(o.cpu().numpy(), offsets)
+    assert np.array_equal(r.cpu().numpy(), row_of) and np.array_equal(tk.cpu().numpy(), token_of)
+    assert np.array_equal(bits(xp), oracle.permute_rows(bits(x), token_of))
+    # scaled permute (backward of the weighted combine), reusing the map
+    p = torch.from_numpy(rp.astype(np.float32)).cuda()
+    dO = torch.empty(P, d, dtype=dt, device="cuda")
+    tre.moe_permute(sh, dY.cuda(), None, p, 0, None, None, r, None, dO, None)
+    ref = oracle.permute_scaled(to_f64(dY), row_of, p.cpu().numpy().astype(np.float64))
+    assert_close("dO", to_f64(dO), ref, TOL[dtype] / 4)
+    # weighted combine of the permuted rows is the identity (probabilities sum to 1)
+    y = torch.empty(T, d, dtype=dt, device="cuda")
+    tre.moe_unpermute(sh, xp, r, p, None, y)
+    assert_close("identity combine", to_f64(y), to_f64(x), 1e-6)
+    if dtype == "bf16":
+        assert torch.equal(y.cpu(), x)                       # bit-exact in bf16
+    # unit-weight combine with an added tensor
+    src = torch.randn(P, d, generator=g).to(dt)
+    add = torch.randn(T, d, generator=g).to(dt)
+    tre.moe_unpermute(sh, src.cuda(), r, None, add.cuda(), y)
+    ref = oracle.combine(to_f64(src), row_of, None, to_f64(add))
+    assert_close("unit combine", to_f64(y), ref, TOL[dtype] / 4)
+    tre.moe_unpermute(sh, src.cuda(), r, p, None, y)
+    ref = oracle.combine(to_f64(src), row_of, p.cpu().numpy().astype(np.float64))
+    assert_close("weighted combine", to_f64(y), ref, TOL[dtype] / 4)
+
+
+# ---------------------------------------------------------------- grouped GEMM entry points
+@pytest.mark.parametrize("wl", [
+    Workload("gg_bf16", T=600, d=384, E=6, k=2, f=384),
+    Workload("gg_f32", T=300, d=96, E=5, k=3, f=80, dtype="f32"),
+], ids=lambda w: w.name)
+def test_grouped_gemm_entry_points(wl):
+    import token_routed_expert_amd as tre
+    inp = make_inputs(wl, seed=3)
+    h = host_inputs(inp)
+    ridx, rp = oracle.route(h["logits"], wl.k)
+    counts, offsets, row_of, token_of = oracle.permute_map(ridx, wl.E)
+    xp = oracle.permute_rows(h["x"], token_of)
+    a, b, hh, o = oracle.experts_fwd(xp, offsets, h["W1"], h["W3"], h["W2"])
+    dO = oracle.permute_scaled(h["dY"], row_of, rp)
+    dXp, dW1, dW3, dW2, da, db = oracle.experts_bwd(dO, xp, a, b, hh, offsets, h["W1"], h["W3"], h["W2"])
+    dt = inp["x"].dtype
+    dev = {k: v.cuda() for k, v in inp.items()}
+    P, f, d = wl.P, wl.f, wl.d
+    sh = tre.make_shape(wl.T, d, wl.E, wl.k, f, 0, wl.dtype)
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    xp_d = torch.from_numpy(xp).to(dt).cuda()
+    ab_d = torch.empty(P, 2 * f, dtype=dt, device="cuda")
+    h_d = torch.empty(P, f, dtype=dt, device="cuda")
+    o_d = torch.empty(P, d, dtype=dt, device="cuda")
+    tre.moe_grouped_gemm_fwd(sh, off, xp_d, dev["W1"], dev["W3"], dev["W2"], ab_d, h_d, o_d)
+    tol = TOL[wl.dtype]
+    assert_close("ab", to_f64(ab_d), np.concatenate([a, b], 1), tol)
+    assert_close("h", to_f64(h_d), hh, tol)
+    assert_close("o", to_f64(o_d), o, tol)
+    dO_d = torch.from_numpy(dO).to(dt).cuda()
+    dab_d = torch.empty(P, 2 * f, dtype=dt, device="cuda")
+    dXp_d = torch.empty(P, d, dtype=dt, device="cuda")
+    dW1_d, dW3_d = torch.empty_like(dev["W1"]), torch.empty_like(dev["W3"])
+    dW2_d = torch.empty_like(dev["W2"])
+    tre.moe_grouped_gemm_bwd(sh, off, xp_d, ab_d, h_d, dO_d, dev["W1"], dev["W3"], dev["W2"], dab_d,
+                             dXp_d, dW1_d, dW3_d, dW2_d)
+    assert_close("dab", to_f64(dab_d), np.concatenate([da, db], 1), tol)
+    assert_close("dXp", to_f64(dXp_d), dXp, tol)
+    assert_close("dW1", to_f64(dW1_d), dW1, tol)
+    assert_close("dW3", to_f64(dW3_d), dW3, tol)
+    assert_close("dW2", to_f64(dW2_d), dW2, tol)
+
+
+# ---------------------------------------------------------------- whole layer, small
+SMALL = [
+    WORKLOADS["tiny_f32"],
+    Workload("tiny_bf16", T=256, d=128, E=8, k=2, f=128),
+    Workload("small_bf16", T=512, d=256, E=8, k=2, f=256),
+    Workload("multitile_bf16", T=1100, d=512, E=4, k=2, f=640),
+    Workload("ragged_skew_bf16", T=700, d=384, E=16, k=4, f=384, skew=True),
+    Workload("shared_bf16", T=300, d=256, E=8, k=2, f=128, f_shared=256),
+    Workload("wide_e_bf16", T=512, d=128, E=256, k=8, f=128),
+    Workload("dense_bf16", T=200, d=256, E=1, k=1, f=384),
+    Workload("k_eq_E_bf16", T=64, d=128, E=4, k=4, f=128),
+    Workload("one_token_bf16", T=1, d=128, E=8, k=2, f=128),
+    Workload("ragged_skew_f32", T=333, d=96, E=16, k=3, f=80, dtype="f32", skew=True),
+    Workload("shared_f32", T=100, d=32, E=4, k=2, f=48, f_shared=24, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_layer_small(wl):
+    inp = make_inputs(wl, seed=0, device="cuda")
+    b = run_layer(wl, inp)
+    h = host_inputs(inp)
+    st, g = oracle_layer(wl, h)
+    check_routing_and_map(wl, b, inp, st)
+    tol = TOL[wl.dtype]
+    assert_close("ab", to_f64(b["ab"]), np.concatenate([st["a"], st["b"]], 1), tol)
+    assert_close("h", to_f64(b["h"]), st["h"], tol)
+    assert_close("o", to_f64(b["o"]), st["o"], tol)
+    assert_close("y", to_f64(b["y"]), st["y"], tol)
+    assert_close("dXp", to_f64(b["dXp"]), g["dXp"], tol)
+    assert_close("dX", to_f64(b["dX"]), g["dX"], tol)
+    for n in ("dW1", "dW3", "dW2") + (("dWs1", "dWs3", "dWs2") if wl.f_shared else ()):
+        assert_close(n, to_f64(b[n]), g[n], tol)
+    for e in np.nonzero(st["counts"] == 0)[0]:                  # empty experts: exact zeros
+        assert not b["dW1"][e].any() and not b["dW3"][e].any() and not b["dW2"][e].any()
+
+
+def test_one_expert_takes_all_tokens():
+    wl = Workload("all_to_one_bf16", T=700, d=256, E=8, k=1, f=256)
+    inp = make_inputs(wl, seed=1, device="cuda")
+    inp["logits"][:, 5] += 50.0
+    b = run_layer(wl, inp)
+    st, g = oracle_layer(wl, host_inputs(inp))
+    assert st["counts"][5] == 700
+    check_routing_and_map(wl, b, inp, st)
+    assert_close("y", to_f64(b["y"]), st["y"], TOL["bf16"])
+    assert_close("dX", to_f64(b["dX"]), g["dX"], TOL["bf16"])
+    for n in ("dW1", "dW3", "dW2"):
+        assert_close(n, to_f64(b[n]), g[n], TOL["bf16"])
+
+
+def test_layer_is_deterministic():
+    wl = Workload("det_bf16", T=900, d=256, E=16, k=4, f=256)
+    inp = make_inputs(wl, seed=2, device="cuda")
+    b1 = run_layer(wl, inp)
+    b2 = run_layer(wl, inp)
+    for n in ("y", "dX", "dW1", "dW3", "dW2", "xp", "ab", "h", "row_of", "token_of"):
+        assert torch.equal(b1[n], b2[n]), n
+
+
+# ---------------------------------------------------------------- full size, sampled
+FULL = [WORKLOADS["mixtral_bf16"], WORKLOADS["qwen3_bf16"], WORKLOADS["deepseek_v3_bf16"],
+        WORKLOADS["skewed_fp8"].with_(name="skewed_bf16", dtype="bf16")]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_layer_full_size_sampled(wl):
+    announce(f"{wl.name}: inputs")
+    inp = make_inputs(wl, seed=0, device="cuda")
+    announce(f"{wl.name}: layer fwd+bwd")
+    b = run_layer(wl, inp)
+    announce(f"{wl.name}: oracle routing/permutation")
+    L = inp["logits"].cpu().numpy()
+    idx, p = oracle.route(L, wl.k)
+    counts, offsets, row_of, token_of = oracle.permute_map(idx, wl.E)
+    st = dict(idx=idx, p=p, counts=counts, offsets=offsets, row_of=row_of, token_of=token_of)
+    check_routing_and_map(wl, b, inp, st)
+    if wl.skew:
+        assert (counts == 0).sum() >= 10
+    tol = TOL[wl.dtype]
+    W = {n: inp[n] for n in ("W1", "W3", "W2")}
+    shared = None
+    if wl.f_shared:
+        shared = tuple(to_f64(inp[n]) for n in ("Ws1", "Ws3", "Ws2"))
+    rng = np.random.default_rng(0)
+    tokens = [0, wl.T - 1] + list(rng.choice(wl.T, 2, replace=False))
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            if len(cache) > 12:
+                cache.clear()
+            cache[e] = tuple(to_f64(W[n][e]) for n in ("W1", "W3", "W2"))
+        return cache[e]
+
+    x_h = inp["x"]
+    dY_h = inp["dY"]
+    announce(f"{wl.name}: oracle on sampled tokens {tokens}")
+    for t in tokens:
+        Ws = [expert(int(e)) for e in idx[t]]
+        W1s = {int(e): w[0] for e, w in zip(idx[t], Ws)}
+        W3s = {int(e): w[1] for e, w in zip(idx[t], Ws)}
+        W2s = {int(e): w[2] for e, w in zip(idx[t], Ws)}
+        y_t, dX_t = oracle.token_fwd_bwd(to_f64(x_h[t]), to_f64(dY_h[t]), idx[t], p[t], W1s, W3s,
+                                         W2s, shared)
+        assert_close(f"y[{t}]", to_f64(b["y"][t])[None], y_t[None], tol)
+        assert_close(f"dX[{t}]", to_f64(b["dX"][t])[None], dX_t[None], tol)
+    announce(f"{wl.name}: oracle weight gradients of sampled experts")
+    nonempty = np.nonzero(counts)[0]
+    for e in [int(nonempty[0]), int(nonempty[len(nonempty) // 2]), int(np.argmax(counts))]:
+        rows = slice(int(offsets[e]), int(offsets[e + 1]))
+        toks = token_of[rows]
+        pe = p.reshape(-1)[np.argsort(row_of.reshape(-1))][rows]
+        dO_e = pe[:, None] * to_f64(dY_h[torch.from_numpy(toks).cuda()])
+        dW1, dW3, dW2 = oracle.expert_wgrad(to_f64(x_h[torch.from_numpy(toks).cuda()]), dO_e,
+                                            *expert(e))
+        assert_close(f"dW1[{e}]", to_f64(b["dW1"][e]), dW1, tol)
+        assert_close(f"dW3[{e}]", to_f64(b["dW3"][e]), dW3, tol)
+        assert_close(f"dW2[{e}]", to_f64(b["dW2"][e]), dW2, tol)
+    for e in np.nonzero(counts == 0)[0][:4]:
+        assert not b["dW1"][int(e)].any() and not b["dW2"][int(e)].any()

@@ -1,0 +1,37 @@
+"""Device buffers of one layer, allocated with torch (memory plumbing only)."""
+from __future__ import annotations
+
+import torch
+
+from . import _native as N
+from .ops import make_shape, moe_workspace_bytes
+
+
+def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None):
+    """Every buffer moe_layer_fwd/bwd touch, as a dict keyed like moe_layer_io.
+
+    `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
+    Returns (shape, buffers, ws_fwd, ws_bwd).
+    """
+    sh = make_shape(T, d, E, k, f, f_shared, dtype)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    P = T * k
+    b = dict(inputs or {})
+
+    def z(*shape, dtype=dt):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+    b.update(topk_idx=z(T, k, dtype=torch.int32), topk_prob=z(T, k, dtype=torch.float32),
+             counts=z(E, dtype=torch.int32), offsets=z(E + 1, dtype=torch.int32),
+             row_of=z(T, k, dtype=torch.int32), token_of=z(P, dtype=torch.int32),
+             xp=z(P, d), ab=z(P, 2 * f), h=z(P, f), o=z(P, d), y=z(T, d),
+             dO=z(P, d), dab=z(P, 2 * f), dXp=z(P, d), dX=z(T, d),
+             dW1=z(E, d, f), dW3=z(E, d, f), dW2=z(E, f, d))
+    if f_shared:
+        b.update(s_ab=z(T, 2 * f_shared), s_h=z(T, f_shared), ys=z(T, d), s_dab=z(T, 2 * f_shared),
+                 dXs=z(T, d), dWs1=z(d, f_shared), dWs3=z(d, f_shared), dWs2=z(f_shared, d))
+    ws_f = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)), dtype=torch.uint8,
+                       device=device)
+    ws_b = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD)), dtype=torch.uint8,
+                       device=device)
+    return sh, b, ws_f, ws_b
