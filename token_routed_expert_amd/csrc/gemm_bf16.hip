@@ -23,17 +23,28 @@
 // E x (M/BM) x (N/BN) tiles; K is the expert's row count, 0 for an empty
 // expert, which then writes zeros.
 //
-// Block tile BM x BN x 64 with 4 wavefronts in a 2x2 grid, each owning a
-// (BM/2) x (BN/2) sub-tile of 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16).
-// Operands are staged through LDS in a K-contiguous layout with a 16-byte row
-// pad (144-byte pitch: conflict-free 16-byte fragment reads for any group of
-// 16 lanes), double buffered: the global loads of stage k+1 are in flight
-// while stage k is multiplied.  Operands that are MN-contiguous in memory are
-// loaded as 8x8 element blocks and transposed in registers before the LDS
-// store.  The MFMA computes C^T = B^T A^T so that each lane ends with four
-// consecutive columns of one row: the epilogue stores 8 bytes per lane.
-// The FC1_FWD tile interleaves W1 and W3 columns in groups of 16, so a lane
-// holds a and b of the same element and applies SwiGLU in registers.
+// Block tile 256 x 256, 4 wavefronts in a 2x2 grid, each owning a 128 x 128
+// sub-tile of 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, fp32 accumulators
+// in AGPRs).  K advances in stages of 32 through a 4-deep LDS ring (32 KB per
+// stage): every operand byte is moved by buffer_load ... lds (global -> LDS
+// without registers; rows past an expert's end or past K are zero-filled by
+// the buffer range check), issued three stages ahead.  LDS layouts:
+//  * K-contiguous operands: 256 rows of 64 bytes; 16-byte chunk c of row r is
+//    stored at chunk c ^ kc_swz(r), so that a fragment read (ds_read_b128,
+//    one chunk of 16 consecutive rows) is free of bank conflicts;
+//  * MN-contiguous operands (forward weights, both weight-gradient operands):
+//    two halves of [32 k][128 mn] (256-byte rows); 32-byte unit u of k-row k
+//    is stored at unit u ^ f(k), f(k) = (k & 3) | ((k >> 3) & 1) << 2.  A
+//    fragment is two ds_read_b64_tr_b16 (each 16-lane group transposes a
+//    4 x 16 block), which turns the MN-contiguous tile into the K-contiguous
+//    8-element vectors the MFMA takes.
+// For fc1 the two halves of the B tile are the same 128 f-columns of W1 and
+// of W3; a wavefront's B fragments 0..3 come from W1 and 4..7 from the same
+// columns of W3, so a lane holds a and b of one element (accumulators j and
+// j + 4) and applies SwiGLU in the epilogue.
+// One barrier per stage sits in the middle of the stage's MFMAs, after which
+// the next stage's fragments are prefetched; the MFMA computes C^T = B^T A^T
+// so that a lane ends with four consecutive columns of one row.
 #include "common.h"
 #include "internal.h"
 #include "schedule.h"
@@ -42,48 +53,115 @@ namespace tre {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int PITCH = BK + 8;  // bf16 elements per LDS row
+constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int NTHREADS = 256;
-
-// 8x8 transpose of bf16: in[j] holds 8 elements along MN at K row j; out[i]
-// holds the 8 K elements of MN column i.
-__device__ __forceinline__ void transpose8x8(const u32x4_t* in, u32x4_t* out) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int wsel = i >> 1;
-    uint32_t r[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = in[2 * p][wsel], hi = in[2 * p + 1][wsel];
-      r[p] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    out[i] = u32x4_t{r[0], r[1], r[2], r[3]};
-  }
-}
+constexpr int OPND_BYTES = 256 * BK * 2;         // one operand of one stage (16 KB)
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // A then B
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 16 one-KB DMA instructions
+constexpr int DMA_PER_WAVE = DMA_PER_OPND / 4;   // 4 per wavefront per operand
+constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE;
 
 template <int OP>
 struct OpTraits {
-  static constexpr bool ragged_m = OP <= OP_FC2_WGRAD - 1;          // ops 0..3
-  static constexpr bool a_kcontig = OP <= OP_FC1_DGRAD;             // ops 0..3
+  static constexpr bool ragged_m = OP <= OP_FC1_DGRAD;             // ops 0..3
+  static constexpr bool a_kcontig = OP <= OP_FC1_DGRAD;            // ops 0..3
   static constexpr bool b_kcontig = OP == OP_FC2_DGRAD || OP == OP_FC1_DGRAD;
 };
 
-template <int OP, int BM, int BN>
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+// Compile-time loop: f(IntC<B>), ..., f(IntC<E-1>); indices stay constants.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer resource, 4 SGPRs
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero.  Word 3 selects the 32-bit data format that raw loads need.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from `r` at byte offset `voff` into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the LDS address).  Issued through
+// inline assembly so that the compiler does not treat it as an LDS store it
+// must drain before every LDS read: the kernel orders these loads with its own
+// s_waitcnt vmcnt + s_barrier.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, const void* lds) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(size_t)LDS_PTR(lds));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0)
+               : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load); the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt on the vector-memory counter only.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Chunk swizzle of K-contiguous LDS rows (64 bytes = 4 chunks of 16 bytes).
+// A fragment read takes one chunk from 16 consecutive rows; with chunk c of
+// row r stored at c ^ kc_swz(r) every 8 consecutive rows cover all 32 banks
+// and every 16 rows all 64 (the swizzle uses only bits 1..3 of r, so it is
+// the same for any 16-row aligned group).
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8_t lds_b128(const char* p) {
+  return *(const __attribute__((address_space(3))) bf16x8_t*)(p);
+}
+
+// Two transposing reads (k rows kr..kr+3 and kr+4..kr+7) -> one fragment.
+__device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p + 4 * 256));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int OP>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WM = BM / 2, WN = BN / 2;       // wavefront sub-tile
   constexpr int FM = WM / 16, FN = WN / 16;     // 16x16 MFMA blocks per wavefront
-  constexpr int STAGE = (BM + BN) * PITCH;
-  constexpr int A_KROWS = BM * BK / 8 / NTHREADS;       // 16-byte chunks per thread (K-contig A)
-  constexpr int B_KROWS = BN * BK / 8 / NTHREADS;
-  constexpr int A_TBLK = (BM / 8) * (BK / 8) / NTHREADS;  // 8x8 blocks per thread (MN-contig A)
-  constexpr int B_TBLK = (BN / 8) * (BK / 8) / NTHREADS;
-  static_assert(A_KROWS >= 1 && B_KROWS >= 1, "tile too small for 256 threads");
-  static_assert(A_TBLK >= 1 && B_TBLK >= 1, "tile too small for transposed loads");
   using TR = OpTraits<OP>;
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
+  __shared__ int sched[8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = uniform(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
   const int d = args.d, f = args.f;
 
@@ -91,11 +169,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
   TileInfo ti;
   int K, M, N;
   if constexpr (TR::ragged_m) {
-    if (!decode_ragged_m<BM>(args.offsets, args.E, NT, (int*)lds, ti)) return;
+    if (!decode_ragged_m<BM>(args.offsets, args.E, NT, sched, ti)) return;
     ti.n0 *= BN;
     K = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
     N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
-    M = ti.rows;
   } else {
     const int total = args.E * MT * NT;
     if ((int)blockIdx.x >= total) return;
@@ -107,162 +184,151 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
     ti.row0 = args.offsets[ti.e];
     ti.rows = args.offsets[ti.e + 1] - ti.row0;
     K = ti.rows;
-    M = (OP == OP_FC2_WGRAD) ? f : d;
     N = (OP == OP_FC2_WGRAD) ? d : 2 * f;
   }
+  ti.e = uniform(ti.e);
+  ti.row0 = uniform(ti.row0);
+  ti.rows = uniform(ti.rows);
+  ti.m0 = uniform(ti.m0);
+  ti.n0 = uniform(ti.n0);
+  M = TR::ragged_m ? ti.rows : ((OP == OP_FC2_WGRAD) ? f : d);
   const size_t e = (size_t)ti.e;
   const int KT = (K + BK - 1) / BK;
 
-  // ---------------------------------------------------------------- loaders
-  // A K-contig: chunk q = tid + 256*i -> tile row q>>3, 8-element chunk q&7
-  const bf16_t* a_src = nullptr;
-  int lda = 0;
-  if constexpr (TR::a_kcontig) {
-    a_src = (const bf16_t*)(OP == OP_FC1_FWD ? args.xp
-                            : OP == OP_FC2_FWD ? args.h
-                            : OP == OP_FC2_DGRAD ? args.dO : args.dab);
-    lda = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
+  // ---------------------------------------------------------------- operands
+  // A: K-contig rows of xp/h/dO/dab (ragged M; rows past the expert read as
+  // zero), or M-contig rows of h/xp (wgrad; K = the expert's rows, past them zero)
+  rsrc_t a_src;
+  uint32_t a_ld;
+  {
+    const bf16_t* base;
+    int ld;
+    if constexpr (OP == OP_FC1_FWD) { base = (const bf16_t*)args.xp; ld = d; }
+    else if constexpr (OP == OP_FC2_FWD) { base = (const bf16_t*)args.h; ld = f; }
+    else if constexpr (OP == OP_FC2_DGRAD) { base = (const bf16_t*)args.dO; ld = d; }
+    else if constexpr (OP == OP_FC1_DGRAD) { base = (const bf16_t*)args.dab; ld = 2 * f; }
+    else if constexpr (OP == OP_FC2_WGRAD) { base = (const bf16_t*)args.h; ld = f; }
+    else { base = (const bf16_t*)args.xp; ld = d; }
+    a_ld = (uint32_t)ld * 2u;
+    a_src = make_rsrc(base + (size_t)ti.row0 * ld, (uint32_t)ti.rows * a_ld);
+  }
+  // B: weight rows (K-contig, dgrad), weight columns (N-contig, forward) or
+  // rows of dO/dab (N-contig, wgrad).  b_src2 is the second source when the
+  // tile draws from two matrices (fc1: W3 beside W1).
+  rsrc_t b_src, b_src2;
+  uint32_t b_ld;
+  if constexpr (OP == OP_FC1_FWD) {
+    b_ld = (uint32_t)f * 2u;
+    b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * b_ld);
+    b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * b_ld);
+  } else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_DGRAD) {
+    b_ld = (uint32_t)d * 2u;
+    b_src = make_rsrc((const bf16_t*)args.W2 + e * (size_t)f * d, (uint32_t)f * b_ld);
+    b_src2 = b_src;
+  } else if constexpr (OP == OP_FC1_DGRAD) {
+    b_ld = (uint32_t)f * 2u;
+    b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * b_ld);
+    b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * b_ld);
+  } else if constexpr (OP == OP_FC2_WGRAD) {
+    b_ld = (uint32_t)d * 2u;
+    b_src = make_rsrc((const bf16_t*)args.dO + (size_t)ti.row0 * d, (uint32_t)ti.rows * b_ld);
+    b_src2 = b_src;
   } else {
-    a_src = (const bf16_t*)(OP == OP_FC2_WGRAD ? args.h : args.xp);
-    lda = (OP == OP_FC2_WGRAD) ? f : d;
+    b_ld = (uint32_t)f * 4u;
+    b_src = make_rsrc((const bf16_t*)args.dab + (size_t)ti.row0 * 2 * f, (uint32_t)ti.rows * b_ld);
+    b_src2 = b_src;
   }
 
-  u32x4_t ra[TR::a_kcontig ? A_KROWS : 8 * A_TBLK];
-  u32x4_t rb[TR::b_kcontig ? B_KROWS : 8 * B_TBLK];
-
-  auto load_a = [&](int k0) {
-    if constexpr (TR::a_kcontig) {
-#pragma unroll
-      for (int i = 0; i < A_KROWS; ++i) {
-        const int q = tid + NTHREADS * i;
-        const int r = min(q >> 3, M - 1);  // clamp rows past the expert's end
-        const bf16_t* p = a_src + (size_t)(ti.row0 + r) * lda + k0 + (q & 7) * 8;
-        ra[i] = *(const u32x4_t*)p;
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < A_TBLK; ++b) {
-        const int blk = tid + NTHREADS * b;
-        const int kb = blk & 7, mb = blk >> 3;
-        const int mcol = min(ti.m0 + mb * 8, M - 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kr = k0 + kb * 8 + j;
-          if (kr < K) {
-            ra[8 * b + j] = *(const u32x4_t*)(a_src + (size_t)(ti.row0 + kr) * lda + mcol);
-          } else {
-            ra[8 * b + j] = u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-    }
+  // ---- DMA lane offsets (bytes, without the stage's k offset) -----------
+  // K-contig operand: instruction t (0..15) covers tile rows 16t..16t+15;
+  // lane -> row 16t + lane/4, stored chunk lane%4 holds logical chunk
+  // (lane%4) ^ ((row >> 2) & 3).
+  // MN-contig operand: instruction t covers half t>>3, k-rows 4(t&7)..+3;
+  // lane -> k-row 4(t&7) + lane/16, stored 16-byte unit lane%16, i.e. 32-byte
+  // unit (lane%16)/2 holding logical unit ((lane%16)/2) ^ f(k).
+  uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
+  auto kc_off = [&](int t, int row_base_mn, uint32_t ld) __attribute__((always_inline)) -> uint32_t {
+    const int row = 16 * t + (lane >> 2);
+    const int c = (lane & 3) ^ kc_swz(row);
+    return (uint32_t)(row_base_mn + row) * ld + (uint32_t)c * 16u;
   };
-
-  auto load_b = [&](int k0) {
-    if constexpr (OP == OP_FC2_DGRAD || OP == OP_FC1_DGRAD) {
-      // B[k][n] = W[n][k]: rows of the weight matrix, K contiguous
-      const bf16_t* wsrc;
-      int ldw, kk;
-      if constexpr (OP == OP_FC2_DGRAD) {
-        wsrc = (const bf16_t*)args.W2 + e * (size_t)f * d;
-        ldw = d;
-        kk = k0;
-      } else {
-        const bool first = k0 < f;
-        wsrc = (const bf16_t*)(first ? args.W1 : args.W3) + e * (size_t)d * f;
-        ldw = f;
-        kk = first ? k0 : k0 - f;
-      }
-#pragma unroll
-      for (int i = 0; i < B_KROWS; ++i) {
-        const int q = tid + NTHREADS * i;
-        const int n = min(ti.n0 + (q >> 3), N - 1);
-        rb[i] = *(const u32x4_t*)(wsrc + (size_t)n * ldw + kk + (q & 7) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < B_TBLK; ++b) {
-        const int blk = tid + NTHREADS * b;
-        const int kb = blk & 7, nb = blk >> 3;
-        const bf16_t* src;
-        size_t ld;
-        int col;
-        bool kmask;
-        if constexpr (OP == OP_FC1_FWD) {
-          // tile column group of 16: even -> W1, odd -> W3, same f-columns
-          const int sub16 = nb >> 1;
-          const bf16_t* W = (const bf16_t*)((sub16 & 1) ? args.W3 : args.W1);
-          src = W + e * (size_t)d * f;
-          ld = f;
-          col = ti.n0 / 2 + (sub16 >> 1) * 16 + (nb & 1) * 8;
-          kmask = false;
-        } else if constexpr (OP == OP_FC2_FWD) {
-          src = (const bf16_t*)args.W2 + e * (size_t)f * d;
-          ld = d;
-          col = min(ti.n0 + nb * 8, N - 8);
-          kmask = false;
-        } else if constexpr (OP == OP_FC2_WGRAD) {
-          src = (const bf16_t*)args.dO + (size_t)ti.row0 * d;
-          ld = d;
-          col = min(ti.n0 + nb * 8, N - 8);
-          kmask = true;
-        } else {  // OP_FC1_WGRAD
-          src = (const bf16_t*)args.dab + (size_t)ti.row0 * (2 * f);
-          ld = 2 * (size_t)f;
-          col = min(ti.n0 + nb * 8, N - 8);
-          kmask = true;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kr = k0 + kb * 8 + j;
-          if (!kmask || kr < K) {
-            rb[8 * b + j] = *(const u32x4_t*)(src + (size_t)kr * ld + col);
-          } else {
-            rb[8 * b + j] = u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-    }
+  auto mc_off = [&](int t, int col_base, uint32_t ld) __attribute__((always_inline)) -> uint32_t {
+    const int k = 4 * (t & 7) + (lane >> 4);
+    const int fk = (k & 3) | (((k >> 3) & 1) << 2);
+    const int unit = ((lane & 15) >> 1) ^ fk;
+    return (uint32_t)k * ld + (uint32_t)(col_base + unit * 16 + (lane & 1) * 8) * 2u;
   };
-
-  auto store_a = [&](bf16_t* As) {
-    if constexpr (TR::a_kcontig) {
 #pragma unroll
-      for (int i = 0; i < A_KROWS; ++i) {
-        const int q = tid + NTHREADS * i;
-        *(u32x4_t*)(As + (q >> 3) * PITCH + (q & 7) * 8) = ra[i];
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < A_TBLK; ++b) {
-        const int blk = tid + NTHREADS * b;
-        const int kb = blk & 7, mb = blk >> 3;
-        u32x4_t t[8];
-        transpose8x8(&ra[8 * b], t);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4_t*)(As + (mb * 8 + i) * PITCH + kb * 8) = t[i];
-      }
-    }
-  };
-
-  auto store_b = [&](bf16_t* Bs) {
+  for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    const int t = wid * DMA_PER_WAVE + q;
+    if constexpr (TR::a_kcontig) a_off[q] = kc_off(t, 0, a_ld);
+    else a_off[q] = mc_off(t, min(ti.m0 + (t >> 3) * 128, M - 128), a_ld);
     if constexpr (TR::b_kcontig) {
-#pragma unroll
-      for (int i = 0; i < B_KROWS; ++i) {
-        const int q = tid + NTHREADS * i;
-        *(u32x4_t*)(Bs + (q >> 3) * PITCH + (q & 7) * 8) = rb[i];
-      }
+      b_off[q] = kc_off(t, ti.n0, b_ld);
+    } else if constexpr (OP == OP_FC1_FWD) {
+      b_off[q] = mc_off(t, ti.n0 / 2, b_ld);          // both halves: the tile's f-columns
     } else {
+      b_off[q] = mc_off(t, min(ti.n0 + (t >> 3) * 128, N - 128), b_ld);
+    }
+  }
+
+  auto issue_stage = [&](int kt, char* __restrict__ base) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
 #pragma unroll
-      for (int b = 0; b < B_TBLK; ++b) {
-        const int blk = tid + NTHREADS * b;
-        const int kb = blk & 7, nb = blk >> 3;
-        u32x4_t t[8];
-        transpose8x8(&rb[8 * b], t);
+    for (int q = 0; q < DMA_PER_WAVE; ++q) {
+      const int t = wid * DMA_PER_WAVE + q;
+      const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
+      dma16(a_src, a_off[q] + ka, base + t * 1024);
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4_t*)(Bs + (nb * 8 + i) * PITCH + kb * 8) = t[i];
+    for (int q = 0; q < DMA_PER_WAVE; ++q) {
+      const int t = wid * DMA_PER_WAVE + q;
+      char* dst = base + OPND_BYTES + t * 1024;
+      if constexpr (OP == OP_FC1_DGRAD) {
+        // K = [da | db]: the first f columns multiply W1, the rest W3
+        const bool first = k0 < f;
+        dma16(first ? b_src : b_src2, b_off[q] + (uint32_t)(first ? k0 : k0 - f) * 2u, dst);
+      } else if constexpr (OP == OP_FC1_FWD) {
+        dma16((t >> 3) ? b_src2 : b_src, b_off[q] + (uint32_t)k0 * b_ld, dst);
+      } else if constexpr (TR::b_kcontig) {
+        dma16(b_src, b_off[q] + (uint32_t)k0 * 2u, dst);
+      } else {
+        dma16(b_src, b_off[q] + (uint32_t)k0 * b_ld, dst);
       }
     }
+  };
+
+  // ---- fragment addresses (bytes inside a stage) -------------------------
+  // K-contig: row = base + 16*blk + lane%16, chunk lane/16 (swizzled)
+  const uint32_t kc_frag = (uint32_t)(lane & 15) * 64u + (uint32_t)((lane >> 4) ^ kc_swz(lane & 15)) * 16u;
+  // MN-contig: lane group g = lane/16, s = lane%16: k-row 8g + s/4, 8-byte
+  // column piece s%4; unit swizzle f = (s/4) | (g&1) << 2
+  const int g = lane >> 4, sl = lane & 15;
+  const uint32_t mc_row = (uint32_t)(8 * g + (sl >> 2)) * 256u + (uint32_t)(sl & 3) * 8u;
+  const int mc_f = ((sl >> 2) & 3) | ((g & 1) << 2);
+  auto a_frag_addr = [&](int i) __attribute__((always_inline)) -> uint32_t {   // A fragment i of this wavefront
+    if constexpr (TR::a_kcontig) return (uint32_t)(wm * WM + 16 * i) * 64u + kc_frag;
+    else return (uint32_t)wm * 8192u + mc_row + (uint32_t)((i ^ mc_f) * 32);
+  };
+  auto b_frag_addr = [&](int j) __attribute__((always_inline)) -> uint32_t {   // B fragment j of this wavefront
+    if constexpr (TR::b_kcontig) return OPND_BYTES + (uint32_t)(wn * WN + 16 * j) * 64u + kc_frag;
+    else if constexpr (OP == OP_FC1_FWD)   // j < 4: W1 columns; j + 4: the same columns of W3
+      return OPND_BYTES + (uint32_t)(j >> 2) * 8192u + mc_row +
+             (uint32_t)((((wn * 4) + (j & 3)) ^ mc_f) * 32);
+    else return OPND_BYTES + (uint32_t)wn * 8192u + mc_row + (uint32_t)((j ^ mc_f) * 32);
+  };
+  uint32_t afa[FM], bfa[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) afa[i] = a_frag_addr(i);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bfa[j] = b_frag_addr(j);
+  auto read_a = [&](const char* st, int i) __attribute__((always_inline)) -> bf16x8_t {
+    if constexpr (TR::a_kcontig) return lds_b128(st + afa[i]);
+    else return lds_tr_pair(st + afa[i]);
+  };
+  auto read_b = [&](const char* st, int j) __attribute__((always_inline)) -> bf16x8_t {
+    if constexpr (TR::b_kcontig) return lds_b128(st + bfa[j]);
+    else return lds_tr_pair(st + bfa[j]);
   };
 
   // ---------------------------------------------------------------- main loop
@@ -272,122 +338,151 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // the schedule scratch lived in lds
+  // Per stage (FM = FN = 8 fragments each) both halves walk the 8 A
+  // fragments i-major against four B fragments held in registers: B
+  // fragments 0..3 (b0, read during the previous stage) in the first half,
+  // 4..7 (b1, read at the start of the first half) in the second.  The wait
+  // + barrier that releases the next stage (and frees the oldest buffer for
+  // stage kt+3) sits between the halves; right after it b0 is refilled with
+  // the next stage's fragments 0..3, and every A fragment is replaced by the
+  // next stage's as soon as its MFMAs are issued.  LDS reads return in
+  // order, so reads are issued in the order their data is needed.
+  static_assert(FM == 8 && FN == 8, "schedule written for 8 x 8 fragments per wavefront");
+  bf16x8_t af[FM], b0[4], b1[4];
   if (KT > 0) {
-    load_a(0);
-    load_b(0);
-    store_a(lds);
-    store_b(lds + BM * PITCH);
+    // stages 0..2 in flight; wait for stage 0, make it visible, read its fragments
+    issue_stage(0, lds);
+    issue_stage(1, lds + STAGE_BYTES);
+    issue_stage(2, lds + 2 * STAGE_BYTES);
+    wait_vmcnt<2 * LOADS_PER_STAGE>();
+    block_barrier();
+    static_for<0, FM>([&](auto i) __attribute__((always_inline)) { af[i.value] = read_a(lds, i.value); });
+    static_for<0, 4>([&](auto j) __attribute__((always_inline)) { b0[j.value] = read_b(lds, j.value); });
   }
-  __syncthreads();
-
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const bf16_t* As = lds + (kt & 1) * STAGE;
-    const bf16_t* Bs = As + BM * PITCH;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a((kt + 1) * BK);
-      load_b((kt + 1) * BK);
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8_t*)(As + (wm * WM + i * 16 + frag_row) * PITCH + ks * 32 + frag_k);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *(const bf16x8_t*)(Bs + (wn * WN + j * 16 + frag_row) * PITCH + ks * 32 + frag_k);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      bf16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-      store_a(nxt);
-      store_b(nxt + BM * PITCH);
-    }
-    __syncthreads();
-  }
+  // The three stage buffers a stage touches are distinct; passing them as
+  // restrict pointers tells the compiler that reads of the current and next
+  // stage cannot alias the DMA into the refilled buffer, so it does not
+  // drain the DMA queue before them (the explicit waits above order them).
+  auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst,
+                        char* __restrict__ refill) __attribute__((always_inline)) {
+    // B fragments 4..7 for the second half: issued first, needed last
+    static_for<0, 4>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, 4 + U.value); });
+    static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U.value;
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2 * u, 2 * u + 2>([&](auto I) __attribute__((always_inline)) {
+        static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+          acc[I.value][J.value] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              b0[J.value], af[I.value], acc[I.value][J.value], 0, 0, 0);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // stage kt+1 has landed for this wavefront; after the barrier it has for
+    // all, and every wavefront is done with stage kt-1, whose buffer now
+    // takes stage kt+3
+    wait_vmcnt<LOADS_PER_STAGE>();
+    block_barrier();
+    issue_stage(kt + 3, refill);
+    // next stage's B fragments 0..3 first: the next first half starts with them
+    static_for<0, 4>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
+    static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U.value;
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2 * u, 2 * u + 2>([&](auto I) __attribute__((always_inline)) {
+        static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+          acc[I.value][4 + J.value] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              b1[J.value], af[I.value], acc[I.value][4 + J.value], 0, 0, 0);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      af[2 * u] = read_a(nst, 2 * u);
+      af[2 * u + 1] = read_a(nst, 2 * u + 1);
+    });
+  };
+  for (int kt = 0; kt < KT; ++kt)
+    stage_body(kt, lds + (kt & (NSTAGE - 1)) * STAGE_BYTES,
+               lds + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES,
+               lds + ((kt + 3) & (NSTAGE - 1)) * STAGE_BYTES);
+  wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
 
   // ---------------------------------------------------------------- epilogue
   // lane holds C[m][n + 0..3] with m = wm*WM + i*16 + (lane & 15),
   // n = wn*WN + j*16 + 4*(lane >> 4)
   const int lm = lane & 15, ln = (lane >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = I.value;
     const int m = wm * WM + i * 16 + lm;
-    if constexpr (TR::ragged_m) {
-      if (m >= ti.rows) continue;
-    } else {
-      if (ti.m0 + m >= M) continue;
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    const bool row_ok = TR::ragged_m ? (m < ti.rows) : (ti.m0 + m < M);
+    static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J.value;
       const f32x4_t c = acc[i][j];
       const int n = wn * WN + j * 16 + ln;
       if constexpr (OP == OP_FC1_FWD) {
-        if (j & 1) continue;
-        const f32x4_t bb = acc[i][j + 1];
-        const int sub16 = (wn * WN) / 16 + j;
-        const int fcol = ti.n0 / 2 + (sub16 >> 1) * 16 + ln;
-        const size_t row = (size_t)(ti.row0 + m);
-        bf16_t* ab = (bf16_t*)args.ab_out + row * (2 * (size_t)f);
-        bf16_t* h = (bf16_t*)args.h_out + row * (size_t)f;
-        float hv[4];
+        if constexpr (j < 4) {
+          const f32x4_t bb = acc[i][j + 4];
+          const int fcol = ti.n0 / 2 + (wn * 4 + j) * 16 + ln;
+          if (row_ok) {
+            const size_t row = (size_t)(ti.row0 + m);
+            bf16_t* ab = (bf16_t*)args.ab_out + row * (2 * (size_t)f);
+            bf16_t* h = (bf16_t*)args.h_out + row * (size_t)f;
+            float hv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[q] = silu_f32(c[q]) * bb[q];
-        *(uint2*)(ab + fcol) = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
-        *(uint2*)(ab + f + fcol) = make_uint2(pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3]));
-        *(uint2*)(h + fcol) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            for (int q = 0; q < 4; ++q) hv[q] = silu_f32(c[q]) * bb[q];
+            *(uint2*)(ab + fcol) = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+            *(uint2*)(ab + f + fcol) =
+                make_uint2(pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3]));
+            *(uint2*)(h + fcol) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+        }
       } else if constexpr (OP == OP_FC2_FWD || OP == OP_FC1_DGRAD) {
         const int col = ti.n0 + n;
-        if (col >= N) continue;
-        bf16_t* out = (bf16_t*)(OP == OP_FC2_FWD ? args.o_out : args.dXp_out);
-        *(uint2*)(out + (size_t)(ti.row0 + m) * d + col) =
-            make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        if (row_ok && col < N) {
+          bf16_t* out = (bf16_t*)(OP == OP_FC2_FWD ? args.o_out : args.dXp_out);
+          *(uint2*)(out + (size_t)(ti.row0 + m) * d + col) =
+              make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        }
       } else if constexpr (OP == OP_FC2_DGRAD) {
         const int col = ti.n0 + n;
-        if (col >= N) continue;
-        const size_t row = (size_t)(ti.row0 + m);
-        const bf16_t* abr = (const bf16_t*)args.ab + row * (2 * (size_t)f);
-        const uint2 av = *(const uint2*)(abr + col);
-        const uint2 bv = *(const uint2*)(abr + f + col);
-        const float a4[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
-                             __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
-        const float b4[4] = {__uint_as_float(bv.x << 16), __uint_as_float(bv.x & 0xffff0000u),
-                             __uint_as_float(bv.y << 16), __uint_as_float(bv.y & 0xffff0000u)};
-        float da[4], db[4];
+        if (row_ok && col < N) {
+          const size_t row = (size_t)(ti.row0 + m);
+          const bf16_t* abr = (const bf16_t*)args.ab + row * (2 * (size_t)f);
+          const uint2 av = *(const uint2*)(abr + col);
+          const uint2 bv = *(const uint2*)(abr + f + col);
+          const float a4[4] = {lo_bf16(av.x), hi_bf16(av.x), lo_bf16(av.y), hi_bf16(av.y)};
+          const float b4[4] = {lo_bf16(bv.x), hi_bf16(bv.x), lo_bf16(bv.y), hi_bf16(bv.y)};
+          float da[4], db[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float s = sigmoid_f32(a4[q]);
-          da[q] = c[q] * b4[q] * s * (1.0f + a4[q] * (1.0f - s));
-          db[q] = c[q] * a4[q] * s;
+          for (int q = 0; q < 4; ++q) {
+            const float s = sigmoid_f32(a4[q]);
+            da[q] = c[q] * b4[q] * s * (1.0f + a4[q] * (1.0f - s));
+            db[q] = c[q] * a4[q] * s;
+          }
+          bf16_t* dab = (bf16_t*)args.dab_out + row * (2 * (size_t)f);
+          *(uint2*)(dab + col) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+          *(uint2*)(dab + f + col) =
+              make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
         }
-        bf16_t* dab = (bf16_t*)args.dab_out + row * (2 * (size_t)f);
-        *(uint2*)(dab + col) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
-        *(uint2*)(dab + f + col) = make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
       } else if constexpr (OP == OP_FC2_WGRAD) {
         const int col = ti.n0 + n;
-        if (col >= N) continue;
-        bf16_t* out = (bf16_t*)args.dW2 + e * (size_t)f * d + (size_t)(ti.m0 + m) * d + col;
-        *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        if (row_ok && col < N) {
+          bf16_t* out = (bf16_t*)args.dW2 + e * (size_t)f * d + (size_t)(ti.m0 + m) * d + col;
+          *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        }
       } else {  // OP_FC1_WGRAD
         const int col = ti.n0 + n;
-        if (col >= N) continue;
-        bf16_t* base = (bf16_t*)(col < f ? args.dW1 : args.dW3);
-        const int cc = col < f ? col : col - f;
-        bf16_t* out = base + e * (size_t)d * f + (size_t)(ti.m0 + m) * f + cc;
-        *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        if (row_ok && col < N) {
+          bf16_t* base = (bf16_t*)(col < f ? args.dW1 : args.dW3);
+          const int cc = col < f ? col : col - f;
+          bf16_t* out = base + e * (size_t)d * f + (size_t)(ti.m0 + m) * f + cc;
+          *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        }
       }
-    }
-  }
+    });
+  });
 }
 
-template <int OP, int BM, int BN>
+template <int OP>
 int launch(const GemmArgs& a, hipStream_t s) {
   int NT, MT = 0;
   int64_t grid;
@@ -406,7 +501,7 @@ int launch(const GemmArgs& a, hipStream_t s) {
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  gemm_bf16_kernel<OP, BM, BN><<<(unsigned)grid, NTHREADS, 0, s>>>(a, NT, MT);
+  gemm_bf16_kernel<OP><<<(unsigned)grid, NTHREADS, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -415,12 +510,12 @@ int launch(const GemmArgs& a, hipStream_t s) {
 
 int gemm_bf16_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_FC1_FWD: return launch<OP_FC1_FWD, 256, 256>(a, s);
-    case OP_FC2_FWD: return launch<OP_FC2_FWD, 256, 256>(a, s);
-    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, 256, 256>(a, s);
-    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, 256, 256>(a, s);
-    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, 256, 256>(a, s);
-    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, 256, 256>(a, s);
+    case OP_FC1_FWD: return launch<OP_FC1_FWD>(a, s);
+    case OP_FC2_FWD: return launch<OP_FC2_FWD>(a, s);
+    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD>(a, s);
+    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD>(a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD>(a, s);
   }
   return MOE_ERR_INVALID;
 }

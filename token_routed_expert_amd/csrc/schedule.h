@@ -33,7 +33,7 @@ struct TileInfo {
 // `scratch` is >= 8 ints of shared memory.  Returns false (uniformly for the
 // block) when the block id is past the device-side tile count.
 template <int BM>
-__device__ bool decode_ragged_m(const int32_t* __restrict__ offsets, int E, int NT, int* scratch,
+__device__ __forceinline__ bool decode_ragged_m(const int32_t* __restrict__ offsets, int E, int NT, int* scratch,
                                 TileInfo& ti) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int c = 0, o0 = 0, o1 = 0;
