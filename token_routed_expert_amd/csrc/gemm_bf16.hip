@@ -54,12 +54,9 @@ namespace tre {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
-constexpr int NTHREADS = 256;
 constexpr int OPND_BYTES = 256 * BK * 2;         // one operand of one stage (16 KB)
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // A then B
 constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 16 one-KB DMA instructions
-constexpr int DMA_PER_WAVE = DMA_PER_OPND / 4;   // 4 per wavefront per operand
-constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE;
 
 template <int OP>
 struct OpTraits {
@@ -97,14 +94,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// 16 bytes per lane from `r` at byte offset `voff` into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 ... lds; M0 holds the LDS address).  Issued through
-// inline assembly so that the compiler does not treat it as an LDS store it
-// must drain before every LDS read: the kernel orders these loads with its own
-// s_waitcnt vmcnt + s_barrier.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, const void* lds) {
-  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(size_t)LDS_PTR(lds));
+// 16 bytes per lane from `r` at byte offset `voff` into LDS at byte address
+// m0 + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS address).
+// Issued through inline assembly so that the compiler does not treat it as
+// an LDS store it must drain before every LDS read: the kernel orders these
+// loads with its own s_waitcnt vmcnt + s_barrier.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(m0)
@@ -152,24 +147,33 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int OP>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
-  constexpr int WM = BM / 2, WN = BN / 2;       // wavefront sub-tile
-  constexpr int FM = WM / 16, FN = WN / 16;     // 16x16 MFMA blocks per wavefront
+// NW wavefronts per block in a 2 x (NW/2) grid: NW = 4 gives 128 x 128
+// wavefront tiles (one wavefront per SIMD), NW = 8 gives 128 x 64 (two per
+// SIMD, so one wavefront's stalls leave the matrix core to the other).
+template <int OP, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
+  constexpr int WAVES_N = NW / 2;
+  constexpr int WM = BM / 2, WN = BN / WAVES_N;  // wavefront sub-tile
+  constexpr int FM = WM / 16, FN = WN / 16;      // 16x16 MFMA blocks per wavefront
+  constexpr int HB = FN / 2;                     // B fragments per half stage
+  constexpr int DMA_PER_WAVE = DMA_PER_OPND / NW;  // per operand per stage
+  constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE;
+  constexpr int DMA_STEP = 4 / DMA_PER_WAVE;       // MFMA steps per DMA instruction
+  static_assert(FM == 8 && HB * 2 == FN && DMA_STEP * DMA_PER_WAVE == 4, "tile shape");
   using TR = OpTraits<OP>;
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
-  __shared__ int sched[8];
+  __shared__ int sched[NW + 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int d = args.d, f = args.f;
 
   // ---------------------------------------------------------------- tile
   TileInfo ti;
   int K, M, N;
   if constexpr (TR::ragged_m) {
-    if (!decode_ragged_m<BM>(args.offsets, args.E, NT, sched, ti)) return;
+    if (!decode_ragged_m<BM, NW>(args.offsets, args.E, NT, sched, ti)) return;
     ti.n0 *= BN;
     K = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
     N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
@@ -272,30 +276,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
     }
   }
 
-  auto issue_stage = [&](int kt, char* __restrict__ base) __attribute__((always_inline)) {
+  // LDS byte address of the stage ring (M0 values are this plus constants)
+  const uint32_t lds_base =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)LDS_PTR(lds));
+  // DMA instruction q of this wavefront (q < DMA_PER_WAVE: A operand, else B) for stage kt
+  auto issue_one = [&](int kt, int q) __attribute__((always_inline)) {
+    const uint32_t st_base = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
     const int k0 = kt * BK;
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    if (q < DMA_PER_WAVE) {
       const int t = wid * DMA_PER_WAVE + q;
       const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
-      dma16(a_src, a_off[q] + ka, base + t * 1024);
-    }
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q) {
-      const int t = wid * DMA_PER_WAVE + q;
-      char* dst = base + OPND_BYTES + t * 1024;
+      dma16(a_src, a_off[q] + ka, st_base + (uint32_t)(t * 1024));
+    } else {
+      const int qq = q - DMA_PER_WAVE;
+      const int t = wid * DMA_PER_WAVE + qq;
+      const uint32_t dst = st_base + (uint32_t)(OPND_BYTES + t * 1024);
       if constexpr (OP == OP_FC1_DGRAD) {
         // K = [da | db]: the first f columns multiply W1, the rest W3
         const bool first = k0 < f;
-        dma16(first ? b_src : b_src2, b_off[q] + (uint32_t)(first ? k0 : k0 - f) * 2u, dst);
+        dma16(first ? b_src : b_src2, b_off[qq] + (uint32_t)(first ? k0 : k0 - f) * 2u, dst);
       } else if constexpr (OP == OP_FC1_FWD) {
-        dma16((t >> 3) ? b_src2 : b_src, b_off[q] + (uint32_t)k0 * b_ld, dst);
+        dma16((t >> 3) ? b_src2 : b_src, b_off[qq] + (uint32_t)k0 * b_ld, dst);
       } else if constexpr (TR::b_kcontig) {
-        dma16(b_src, b_off[q] + (uint32_t)k0 * 2u, dst);
+        dma16(b_src, b_off[qq] + (uint32_t)k0 * 2u, dst);
       } else {
-        dma16(b_src, b_off[q] + (uint32_t)k0 * b_ld, dst);
+        dma16(b_src, b_off[qq] + (uint32_t)k0 * b_ld, dst);
       }
     }
+  };
+  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2 * DMA_PER_WAVE; ++q) issue_one(kt, q);
   };
 
   // ---- fragment addresses (bytes inside a stage) -------------------------
@@ -311,11 +322,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
     else return (uint32_t)wm * 8192u + mc_row + (uint32_t)((i ^ mc_f) * 32);
   };
   auto b_frag_addr = [&](int j) __attribute__((always_inline)) -> uint32_t {   // B fragment j of this wavefront
-    if constexpr (TR::b_kcontig) return OPND_BYTES + (uint32_t)(wn * WN + 16 * j) * 64u + kc_frag;
-    else if constexpr (OP == OP_FC1_FWD)   // j < 4: W1 columns; j + 4: the same columns of W3
-      return OPND_BYTES + (uint32_t)(j >> 2) * 8192u + mc_row +
-             (uint32_t)((((wn * 4) + (j & 3)) ^ mc_f) * 32);
-    else return OPND_BYTES + (uint32_t)wn * 8192u + mc_row + (uint32_t)((j ^ mc_f) * 32);
+    if constexpr (TR::b_kcontig) {
+      return OPND_BYTES + (uint32_t)(wn * WN + 16 * j) * 64u + kc_frag;
+    } else if constexpr (OP == OP_FC1_FWD) {  // j < HB: W1 columns; j + HB: the same columns of W3
+      return OPND_BYTES + (uint32_t)(j / HB) * 8192u + mc_row +
+             (uint32_t)((((wn * HB) + (j % HB)) ^ mc_f) * 32);
+    } else {
+      const int col = wn * WN + 16 * j;           // tile column of the fragment
+      return OPND_BYTES + (uint32_t)(col >> 7) * 8192u + mc_row +
+             (uint32_t)((((col & 127) >> 4) ^ mc_f) * 32);
+    }
   };
   uint32_t afa[FM], bfa[FN];
 #pragma unroll
@@ -338,72 +354,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Per stage (FM = FN = 8 fragments each) both halves walk the 8 A
-  // fragments i-major against four B fragments held in registers: B
-  // fragments 0..3 (b0, read during the previous stage) in the first half,
-  // 4..7 (b1, read at the start of the first half) in the second.  The wait
-  // + barrier that releases the next stage (and frees the oldest buffer for
-  // stage kt+3) sits between the halves; right after it b0 is refilled with
-  // the next stage's fragments 0..3, and every A fragment is replaced by the
-  // next stage's as soon as its MFMAs are issued.  LDS reads return in
-  // order, so reads are issued in the order their data is needed.
-  static_assert(FM == 8 && FN == 8, "schedule written for 8 x 8 fragments per wavefront");
-  bf16x8_t af[FM], b0[4], b1[4];
+  // Per stage both halves walk the FM = 8 A fragments i-major against HB B
+  // fragments held in registers: B fragments 0..HB-1 (b0, read during the
+  // previous stage) in the first half, HB..FN-1 (b1, read at the start of
+  // the first half) in the second.  The wait + barrier that releases the
+  // next stage (and frees the oldest buffer for stage kt+3) sits between the
+  // halves; right after it b0 is refilled with the next stage's fragments,
+  // and every A fragment is replaced by the next stage's as soon as its
+  // MFMAs are issued.  LDS reads return in order, so reads are issued in the
+  // order their data is needed.  The refill of a freed buffer (16 one-KB DMA
+  // instructions per operand, spread over the wavefronts) is issued evenly
+  // over the second half of stage kt (A operand of stage kt+3) and the first
+  // half of stage kt+1 (its B operand): issued in a burst they stall the
+  // wavefront's instruction issue.
+  bf16x8_t af[FM], b0[HB], b1[HB];
   if (KT > 0) {
     // stages 0..2 in flight; wait for stage 0, make it visible, read its fragments
-    issue_stage(0, lds);
-    issue_stage(1, lds + STAGE_BYTES);
-    issue_stage(2, lds + 2 * STAGE_BYTES);
-    wait_vmcnt<2 * LOADS_PER_STAGE>();
+    issue_stage(0);
+    issue_stage(1);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q) issue_one(2, q);   // stage 2's B half follows in stage 0
+    wait_vmcnt<LOADS_PER_STAGE + DMA_PER_WAVE>();
     block_barrier();
     static_for<0, FM>([&](auto i) __attribute__((always_inline)) { af[i.value] = read_a(lds, i.value); });
-    static_for<0, 4>([&](auto j) __attribute__((always_inline)) { b0[j.value] = read_b(lds, j.value); });
+    static_for<0, HB>([&](auto j) __attribute__((always_inline)) { b0[j.value] = read_b(lds, j.value); });
   }
-  // The three stage buffers a stage touches are distinct; passing them as
-  // restrict pointers tells the compiler that reads of the current and next
-  // stage cannot alias the DMA into the refilled buffer, so it does not
-  // drain the DMA queue before them (the explicit waits above order them).
-  auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst,
-                        char* __restrict__ refill) __attribute__((always_inline)) {
-    // B fragments 4..7 for the second half: issued first, needed last
-    static_for<0, 4>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, 4 + U.value); });
+  // st and nst are distinct stage buffers (restrict lets the compiler keep
+  // their reads apart).
+  auto stage_body = [&](int kt, const char* __restrict__ st,
+                        const char* __restrict__ nst) __attribute__((always_inline)) {
+    // B fragments HB..FN-1 for the second half: issued first, needed last
+    static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, HB + U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
       constexpr int u = U.value;
       __builtin_amdgcn_sched_barrier(0);
       static_for<2 * u, 2 * u + 2>([&](auto I) __attribute__((always_inline)) {
-        static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+        static_for<0, HB>([&](auto J) __attribute__((always_inline)) {
           acc[I.value][J.value] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               b0[J.value], af[I.value], acc[I.value][J.value], 0, 0, 0);
         });
       });
       __builtin_amdgcn_sched_barrier(0);
+      // second (B-operand) half of stage kt+2's refill; its buffer was freed
+      // by the previous stage's barrier
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 2, DMA_PER_WAVE + u / DMA_STEP);
     });
     // stage kt+1 has landed for this wavefront; after the barrier it has for
     // all, and every wavefront is done with stage kt-1, whose buffer now
     // takes stage kt+3
     wait_vmcnt<LOADS_PER_STAGE>();
     block_barrier();
-    issue_stage(kt + 3, refill);
-    // next stage's B fragments 0..3 first: the next first half starts with them
-    static_for<0, 4>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
+    // next stage's B fragments 0..HB-1 first: the next first half starts with them
+    static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
       constexpr int u = U.value;
       __builtin_amdgcn_sched_barrier(0);
       static_for<2 * u, 2 * u + 2>([&](auto I) __attribute__((always_inline)) {
-        static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
-          acc[I.value][4 + J.value] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              b1[J.value], af[I.value], acc[I.value][4 + J.value], 0, 0, 0);
+        static_for<0, HB>([&](auto J) __attribute__((always_inline)) {
+          acc[I.value][HB + J.value] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              b1[J.value], af[I.value], acc[I.value][HB + J.value], 0, 0, 0);
         });
       });
       __builtin_amdgcn_sched_barrier(0);
       af[2 * u] = read_a(nst, 2 * u);
       af[2 * u + 1] = read_a(nst, 2 * u + 1);
+      // first (A-operand) half of stage kt+3's refill into the buffer stage
+      // kt-1 used; one DMA instruction per step keeps the address unit from
+      // stalling the issue of the MFMAs
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 3, u / DMA_STEP);
     });
   };
   for (int kt = 0; kt < KT; ++kt)
     stage_body(kt, lds + (kt & (NSTAGE - 1)) * STAGE_BYTES,
-               lds + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES,
-               lds + ((kt + 3) & (NSTAGE - 1)) * STAGE_BYTES);
+               lds + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES);
   wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
 
   // ---------------------------------------------------------------- epilogue
@@ -419,9 +442,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
       const f32x4_t c = acc[i][j];
       const int n = wn * WN + j * 16 + ln;
       if constexpr (OP == OP_FC1_FWD) {
-        if constexpr (j < 4) {
-          const f32x4_t bb = acc[i][j + 4];
-          const int fcol = ti.n0 / 2 + (wn * 4 + j) * 16 + ln;
+        if constexpr (j < HB) {
+          const f32x4_t bb = acc[i][j + HB];
+          const int fcol = ti.n0 / 2 + (wn * HB + j) * 16 + ln;
           if (row_ok) {
             const size_t row = (size_t)(ti.row0 + m);
             bf16_t* ab = (bf16_t*)args.ab_out + row * (2 * (size_t)f);
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs args, i
   });
 }
 
-template <int OP>
+template <int OP, int NW>
 int launch(const GemmArgs& a, hipStream_t s) {
   int NT, MT = 0;
   int64_t grid;
@@ -501,21 +524,24 @@ int launch(const GemmArgs& a, hipStream_t s) {
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  gemm_bf16_kernel<OP><<<(unsigned)grid, NTHREADS, 0, s>>>(a, NT, MT);
+  gemm_bf16_kernel<OP, NW><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
 
 }  // namespace
 
+#ifndef GEMM_NW
+#define GEMM_NW 8
+#endif
 int gemm_bf16_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_FC1_FWD: return launch<OP_FC1_FWD>(a, s);
-    case OP_FC2_FWD: return launch<OP_FC2_FWD>(a, s);
-    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD>(a, s);
-    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD>(a, s);
-    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD>(a, s);
-    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD>(a, s);
+    case OP_FC1_FWD: return launch<OP_FC1_FWD, GEMM_NW>(a, s);
+    case OP_FC2_FWD: return launch<OP_FC2_FWD, GEMM_NW>(a, s);
+    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, GEMM_NW>(a, s);
+    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, GEMM_NW>(a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, GEMM_NW>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, GEMM_NW>(a, s);
   }
   return MOE_ERR_INVALID;
 }

@@ -21,7 +21,7 @@ template <int OP>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args, int NT, int MT) {
   __shared__ float As[BKF][BM + 1];
   __shared__ float Bs[BKF][BN + 1];
-  __shared__ int scratch[8];
+  __shared__ int scratch[8];  // >= 4 wavefronts + 4
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int d = args.d, f = args.f;
   constexpr bool ragged = OP <= OP_FC1_DGRAD;

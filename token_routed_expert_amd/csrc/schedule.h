@@ -28,13 +28,14 @@ struct TileInfo {
   int n0;    // N-tile index (scaled to columns by the caller)
 };
 
-// Ragged-M decode for a 256-thread block and E <= 256 experts: expert e owns
-// ceil(m_e / BM) M-tiles; tiles are numbered expert-major, N fastest.
-// `scratch` is >= 8 ints of shared memory.  Returns false (uniformly for the
-// block) when the block id is past the device-side tile count.
-template <int BM>
-__device__ __forceinline__ bool decode_ragged_m(const int32_t* __restrict__ offsets, int E, int NT, int* scratch,
-                                TileInfo& ti) {
+// Ragged-M decode for a block of NWAVES wavefronts and E <= 64 * NWAVES
+// experts: expert e owns ceil(m_e / BM) M-tiles; tiles are numbered
+// expert-major.  `scratch` is >= NWAVES + 4 ints of shared memory.
+// Returns false (uniformly for the block) when the block id is past the
+// device-side tile count.
+template <int BM, int NWAVES = 4>
+__device__ __forceinline__ bool decode_ragged_m(const int32_t* __restrict__ offsets, int E, int NT,
+                                                int* scratch, TileInfo& ti) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int c = 0, o0 = 0, o1 = 0;
   if (tid < E) {
@@ -50,24 +51,34 @@ __device__ __forceinline__ bool decode_ragged_m(const int32_t* __restrict__ offs
   }
   if (lane == 63) scratch[w] = incl;
   __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += scratch[i];
-  const int total = (scratch[0] + scratch[1] + scratch[2] + scratch[3]) * NT;
+  int before = 0, total_m = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    if (i < w) before += scratch[i];
+    total_m += scratch[i];
+  }
+  const int total = total_m * NT;
   if ((int)blockIdx.x >= total) return false;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int g = logical / NT;
+  // expert e owns logical tiles [excl * NT, (excl + c) * NT), N-tile-major
+  // with the M-tile fastest: tiles that share an expert's weight strip run
+  // side by side, and a split across dispatch rounds re-reads the (smaller)
+  // activation rows rather than the weights
   const int excl = before + incl - c;
-  if (c > 0 && g >= excl && g < excl + c) {
-    scratch[4] = tid;
-    scratch[5] = o0 + (g - excl) * BM;
-    scratch[6] = min(BM, o1 - (o0 + (g - excl) * BM));
+  if (c > 0 && logical >= excl * NT && logical < (excl + c) * NT) {
+    const int local = logical - excl * NT;
+    const int mt = local % c;
+    scratch[NWAVES] = tid;
+    scratch[NWAVES + 1] = o0 + mt * BM;
+    scratch[NWAVES + 2] = min(BM, o1 - (o0 + mt * BM));
+    scratch[NWAVES + 3] = local / c;
   }
   __syncthreads();
-  ti.e = scratch[4];
-  ti.row0 = scratch[5];
-  ti.rows = scratch[6];
+  ti.e = scratch[NWAVES];
+  ti.row0 = scratch[NWAVES + 1];
+  ti.rows = scratch[NWAVES + 2];
   ti.m0 = 0;
-  ti.n0 = logical % NT;
+  ti.n0 = scratch[NWAVES + 3];
   return true;
 }
 
