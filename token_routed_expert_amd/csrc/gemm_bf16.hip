@@ -134,6 +134,37 @@ __device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3)
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// v_permlane16_swap on two registers: x keeps lanes 0-15 and 32-47 and takes
+// y's lanes 0-15 / 32-47 into its lanes 16-31 / 48-63; y receives the rest.
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+// Two 16x16 accumulator fragments x (columns 0-15) and y (columns 16-31) with
+// lane l holding columns 4(l >> 4)..+3 of row l & 15 -> the lane's 8
+// consecutive columns pc..pc+7 (pc = 16((l >> 4) & 1) + 8(l >> 5)) as bf16.
+__device__ __forceinline__ u32x4_t pair_bf16(const f32x4_t& x, const f32x4_t& y) {
+  uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
+  uint32_t y0 = pack_bf16x2(y[0], y[1]), y1 = pack_bf16x2(y[2], y[3]);
+  swap16(x0, y0);
+  swap16(x1, y1);
+  return u32x4_t{x0, x1, y0, y1};
+}
+
+// The same redistribution in fp32: afterwards x holds columns pc..pc+3 and
+// y columns pc+4..pc+7.
+__device__ __forceinline__ void pair_f32(f32x4_t& x, f32x4_t& y) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t a = __float_as_uint(x[q]), b = __float_as_uint(y[q]);
+    swap16(a, b);
+    x[q] = __uint_as_float(a);
+    y[q] = __uint_as_float(b);
+  }
+}
+
 __device__ __forceinline__ bf16x8_t lds_b128(const char* p) {
   return *(const __attribute__((address_space(3))) bf16x8_t*)(p);
 }
@@ -431,77 +462,89 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
 
   // ---------------------------------------------------------------- epilogue
   // lane holds C[m][n + 0..3] with m = wm*WM + i*16 + (lane & 15),
-  // n = wn*WN + j*16 + 4*(lane >> 4)
-  const int lm = lane & 15, ln = (lane >> 4) * 4;
+  // n = wn*WN + j*16 + 4*(lane >> 4).  Fragments are taken in pairs (j, j+1):
+  // v_permlane16_swap leaves each lane with 8 consecutive columns of the
+  // 32-column pair, starting at column pc, so every store is 16 bytes and a
+  // row receives 64 contiguous bytes per instruction.
+  const int lm = lane & 15;
+  const int pc = ((lane >> 4) & 1) * 16 + (lane >> 5) * 8;
   static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = I.value;
-    const int m = wm * WM + i * 16 + lm;
+    const int m = wm * WM + i * 16 + lm;  // row within the tile
     const bool row_ok = TR::ragged_m ? (m < ti.rows) : (ti.m0 + m < M);
-    static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
-      constexpr int j = J.value;
-      const f32x4_t c = acc[i][j];
-      const int n = wn * WN + j * 16 + ln;
-      if constexpr (OP == OP_FC1_FWD) {
-        if constexpr (j < HB) {
-          const f32x4_t bb = acc[i][j + HB];
-          const int fcol = ti.n0 / 2 + (wn * HB + j) * 16 + ln;
-          if (row_ok) {
-            const size_t row = (size_t)(ti.row0 + m);
-            bf16_t* ab = (bf16_t*)args.ab_out + row * (2 * (size_t)f);
-            bf16_t* h = (bf16_t*)args.h_out + row * (size_t)f;
-            float hv[4];
+    if constexpr (OP == OP_FC1_FWD) {
+      // pairs jp < HB/2 hold W1 columns (a), pair jp + HB/2 the same W3 columns (b)
+      static_for<0, HB / 2>([&](auto JP) __attribute__((always_inline)) {
+        constexpr int j0 = 2 * JP.value;
+        const f32x4_t a0 = acc[i][j0], a1 = acc[i][j0 + 1];
+        const f32x4_t b0v = acc[i][j0 + HB], b1v = acc[i][j0 + HB + 1];
+        f32x4_t h0, h1;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hv[q] = silu_f32(c[q]) * bb[q];
-            *(uint2*)(ab + fcol) = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
-            *(uint2*)(ab + f + fcol) =
-                make_uint2(pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3]));
-            *(uint2*)(h + fcol) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          }
+        for (int q = 0; q < 4; ++q) {
+          h0[q] = silu_f32(a0[q]) * b0v[q];
+          h1[q] = silu_f32(a1[q]) * b1v[q];
         }
-      } else if constexpr (OP == OP_FC2_FWD || OP == OP_FC1_DGRAD) {
-        const int col = ti.n0 + n;
-        if (row_ok && col < N) {
-          bf16_t* out = (bf16_t*)(OP == OP_FC2_FWD ? args.o_out : args.dXp_out);
-          *(uint2*)(out + (size_t)(ti.row0 + m) * d + col) =
-              make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
-        }
-      } else if constexpr (OP == OP_FC2_DGRAD) {
-        const int col = ti.n0 + n;
-        if (row_ok && col < N) {
+        const u32x4_t av = pair_bf16(a0, a1), bv = pair_bf16(b0v, b1v), hv = pair_bf16(h0, h1);
+        const int fcol = ti.n0 / 2 + (wn * HB + j0) * 16 + pc;
+        if (row_ok) {
           const size_t row = (size_t)(ti.row0 + m);
-          const bf16_t* abr = (const bf16_t*)args.ab + row * (2 * (size_t)f);
-          const uint2 av = *(const uint2*)(abr + col);
-          const uint2 bv = *(const uint2*)(abr + f + col);
-          const float a4[4] = {lo_bf16(av.x), hi_bf16(av.x), lo_bf16(av.y), hi_bf16(av.y)};
-          const float b4[4] = {lo_bf16(bv.x), hi_bf16(bv.x), lo_bf16(bv.y), hi_bf16(bv.y)};
-          float da[4], db[4];
+          bf16_t* ab = (bf16_t*)args.ab_out + row * (2 * (size_t)f);
+          *(u32x4_t*)(ab + fcol) = av;
+          *(u32x4_t*)(ab + f + fcol) = bv;
+          *(u32x4_t*)((bf16_t*)args.h_out + row * (size_t)f + fcol) = hv;
+        }
+      });
+    } else {
+      static_for<0, FN / 2>([&](auto JP) __attribute__((always_inline)) {
+        constexpr int j0 = 2 * JP.value;
+        const int col0 = ti.n0 + wn * WN + j0 * 16;  // first column of the pair (uniform)
+        if (col0 < N) {
+          const int col = col0 + pc;
+          if constexpr (OP == OP_FC2_DGRAD) {
+            f32x4_t x = acc[i][j0], y = acc[i][j0 + 1];
+            pair_f32(x, y);  // dh at columns col + 0..3 (x), col + 4..7 (y)
+            if (row_ok) {
+              const size_t row = (size_t)(ti.row0 + m);
+              const bf16_t* abr = (const bf16_t*)args.ab + row * (2 * (size_t)f);
+              const u32x4_t av = *(const u32x4_t*)(abr + col);
+              const u32x4_t bv = *(const u32x4_t*)(abr + f + col);
+              float da[8], db[8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float s = sigmoid_f32(a4[q]);
-            da[q] = c[q] * b4[q] * s * (1.0f + a4[q] * (1.0f - s));
-            db[q] = c[q] * a4[q] * s;
+              for (int q = 0; q < 8; ++q) {
+                const uint32_t aw = av[q >> 1], bw = bv[q >> 1];
+                const float aq = (q & 1) ? hi_bf16(aw) : lo_bf16(aw);
+                const float bq = (q & 1) ? hi_bf16(bw) : lo_bf16(bw);
+                const float c = q < 4 ? x[q] : y[q - 4];
+                const float sg = sigmoid_f32(aq);
+                da[q] = c * bq * sg * (1.0f + aq * (1.0f - sg));
+                db[q] = c * aq * sg;
+              }
+              bf16_t* dab = (bf16_t*)args.dab_out + row * (2 * (size_t)f);
+              *(u32x4_t*)(dab + col) = u32x4_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]),
+                                               pack_bf16x2(da[4], da[5]), pack_bf16x2(da[6], da[7])};
+              *(u32x4_t*)(dab + f + col) = u32x4_t{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]),
+                                                   pack_bf16x2(db[4], db[5]), pack_bf16x2(db[6], db[7])};
+            }
+          } else {
+            const u32x4_t v = pair_bf16(acc[i][j0], acc[i][j0 + 1]);
+            if (row_ok) {
+              bf16_t* out;
+              if constexpr (OP == OP_FC2_FWD || OP == OP_FC1_DGRAD) {
+                out = (bf16_t*)(OP == OP_FC2_FWD ? args.o_out : args.dXp_out) +
+                      (size_t)(ti.row0 + m) * d + col;
+              } else if constexpr (OP == OP_FC2_WGRAD) {
+                out = (bf16_t*)args.dW2 + e * (size_t)f * d + (size_t)(ti.m0 + m) * d + col;
+              } else {  // OP_FC1_WGRAD: the pair lies wholly in dW1 or in dW3 (f % 32 == 0)
+                const bool first = col0 < f;
+                out = (bf16_t*)(first ? args.dW1 : args.dW3) + e * (size_t)d * f +
+                      (size_t)(ti.m0 + m) * f + (first ? col : col - f);
+              }
+              *(u32x4_t*)out = v;
+            }
           }
-          bf16_t* dab = (bf16_t*)args.dab_out + row * (2 * (size_t)f);
-          *(uint2*)(dab + col) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
-          *(uint2*)(dab + f + col) =
-              make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
         }
-      } else if constexpr (OP == OP_FC2_WGRAD) {
-        const int col = ti.n0 + n;
-        if (row_ok && col < N) {
-          bf16_t* out = (bf16_t*)args.dW2 + e * (size_t)f * d + (size_t)(ti.m0 + m) * d + col;
-          *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
-        }
-      } else {  // OP_FC1_WGRAD
-        const int col = ti.n0 + n;
-        if (row_ok && col < N) {
-          bf16_t* base = (bf16_t*)(col < f ? args.dW1 : args.dW3);
-          const int cc = col < f ? col : col - f;
-          bf16_t* out = base + e * (size_t)d * f + (size_t)(ti.m0 + m) * f + cc;
-          *(uint2*)out = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
-        }
-      }
-    });
+      });
+    }
   });
 }
 
