@@ -18,6 +18,8 @@ workload.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +35,46 @@ METRIC = "MoE layer fwd+bwd TFLOPS/GPU & % MFMA peak; permute/combine HBM GB/s"
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of every HIP source and header of the library: a traffic record
+    taken from hardware counters is valid only for the sources it was taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "token_routed_expert_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic(wl):
+    """HBM bytes per step of the grouped-GEMM launches, from the counter record
+    under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+    counter reads for a device copy of known size), or None when there is no
+    record or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{wl.name}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.loads("".join(ln for ln in fh if not ln.startswith("#")))
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        log(f"bench: {os.path.basename(path)} was taken on other kernel sources; traffic = null")
+        return None
+    return int(rec["hbm_bytes_per_step"])
+
+
+def copy_calibration():
+    """Two device copies of 1 GiB each, so that a counter run records what its
+    FETCH_SIZE / WRITE_SIZE read for a known number of bytes."""
+    import torch
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def build_step(wl, inp):
@@ -141,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run two 1 GiB device copies first (for hardware-counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py: this library is one GPU's share of the layer; --gpus {args.gpus} is not "
@@ -156,6 +200,8 @@ def main():
         log(f"bench.py: workload {wl.name} ({wl.dtype}) is not supported by this build")
         sys.exit(2)
     log(f"bench: {wl}")
+    if args.copy_calibration:
+        copy_calibration()
     inp = make_inputs(wl, seed=0, device="cuda")
     step = build_step(wl, inp)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
@@ -203,7 +249,8 @@ def main():
                    "f_shared": wl.f_shared},
         "roofline": {"kernel": "grouped GEMM (all fwd+bwd launches of a step)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4), "traffic": gemm_traffic(wl),
+                     "traffic_unit": "bytes per step (all grouped-GEMM launches)"},
         "breakdown_ms": {"route": round(t_route, 4), "permute": round(t_perm, 4),
                          "gemm_fwd": round(t_gf, 4), "combine": round(t_comb, 4),
                          "combine_bwd_permute": round(t_permb, 4), "gemm_bwd": round(t_gb, 4),
