@@ -28,7 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
 HBM_PEAK_GBS = 8000.0
 METRIC = "MoE layer fwd+bwd TFLOPS/GPU & % MFMA peak; permute/combine HBM GB/s"
 
@@ -80,9 +80,11 @@ def copy_calibration():
 def build_step(wl, inp):
     import torch
     import token_routed_expert_amd as tre
-    from token_routed_expert_amd.buffers import layer_buffers
+    from token_routed_expert_amd.buffers import layer_buffers, requantize_weights
 
-    sh, b, wsf, _ = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp)
+    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp)
+    if wl.dtype == "e4m3":
+        return build_step_e4m3(wl, inp, sh, b, wsf, wsb)
     shared = None
     if wl.f_shared:
         fs = wl.f_shared
@@ -117,8 +119,69 @@ def build_step(wl, inp):
         ev[6].record()
         tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
         ev[7].record()
+        ev[8].record()
 
     return step
+
+
+def build_step_e4m3(wl, inp, sh, b, wsf, wsb):
+    """The e4m3 step: the expert weights are re-quantised from their fp32
+    masters (as after an optimizer step), x is quantised in 1 x 128 blocks
+    and its codes permuted; the GEMM calls quantise h, dO, [da|db] and the
+    weight-gradient token blocks themselves."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd.buffers import requantize_weights
+    from token_routed_expert_amd import _native as N
+
+    wq = b["wq"]
+    pws = tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE)
+    ws_perm = wsf[:max(256, pws)]
+    ws_gf = wsf[pws:]
+    W = (inp["W1"], inp["W3"], inp["W2"])
+
+    def step(ev):
+        ev[0].record()
+        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        ev[1].record()
+        tre.moe_quantize_rows(b["x"], b["xq"], b["xs"])
+        tre.moe_permute_e4m3(sh, b["xq"], b["xs"], b["topk_idx"], 1, b["counts"], b["offsets"],
+                             b["row_of"], b["token_of"], b["xpq"], b["xps"], ws_perm)
+        ev[2].record()
+        tre.moe_grouped_gemm_fwd_e4m3(sh, b["offsets"], b["xpq"], b["xps"], wq, b["ab"], b["h"],
+                                      b["o"], ws_gf)
+        ev[3].record()
+        tre.moe_unpermute(sh, b["o"], b["row_of"], b["topk_prob"], None, b["y"])
+        ev[4].record()
+        tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
+                        b["dO"], None)
+        ev[5].record()
+        tre.moe_grouped_gemm_bwd_e4m3(sh, b["offsets"], b["token_of"], b["x"], b["ab"], b["h"],
+                                      b["dO"], wq, b["dab"], b["dXp"], b["dW1"], b["dW3"],
+                                      b["dW2"], wsb)
+        ev[6].record()
+        tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, None, b["dX"])
+        ev[7].record()
+        requantize_weights(wq, *W)
+        ev[8].record()
+
+    return step
+
+
+def e4m3_expert_fwd_bwd(oracle, X, dO, W1, W3, W2):
+    """One expert's e4m3 forward and backward with the oracle's functions:
+    weight tiles and activation rows quantised, products in fp64."""
+    import numpy as np
+    one = np.array([0, X.shape[0]])
+    Wd = [oracle.dequant_expert_weights(*oracle.quant_expert_weights(W[None])) for W in (W1, W3, W2)]
+    xq, xs = oracle.quant_rows(X)
+    a, b = oracle.fc1_fwd_e4m3(xq, xs, one, Wd[0], Wd[1])
+    h = oracle.silu(a) * b
+    oracle.fc2_fwd_e4m3(h, one, Wd[2])
+    da, db = oracle.fc2_dgrad_e4m3(dO, a, b, one, Wd[2])
+    dab = np.concatenate([da, db], axis=1)
+    oracle.fc1_dgrad_e4m3(dab, one, Wd[0], Wd[1])
+    oracle.wgrad_e4m3(h, dO, one)
+    oracle.wgrad_e4m3(X, dab, one)
 
 
 def cpu_baseline(wl, inp, budget_s: float):
@@ -153,11 +216,17 @@ def cpu_baseline(wl, inp, budget_s: float):
         toks = torch.from_numpy(token_of[r0:r1]).to(inp["x"].device)
         X = to_f64(inp["x"][toks])
         dO = p_rows[r0:r1, None] * to_f64(inp["dY"][toks])
-        W1, W3, W2 = (to_f64(inp[n][e]) for n in ("W1", "W3", "W2"))
-        t0 = time.perf_counter()
-        a, b, h, o = oracle.swiglu_fwd(X, W1, W3, W2)
-        oracle.swiglu_bwd(X, a, b, h, dO, W1, W3, W2)
-        t_exp += time.perf_counter() - t0
+        if wl.dtype == "e4m3":
+            Wm = [inp[n][e].cpu().numpy() for n in ("W1", "W3", "W2")]
+            t0 = time.perf_counter()
+            e4m3_expert_fwd_bwd(oracle, X, dO, *Wm)
+            t_exp += time.perf_counter() - t0
+        else:
+            W1, W3, W2 = (to_f64(inp[n][e]) for n in ("W1", "W3", "W2"))
+            t0 = time.perf_counter()
+            a, b, h, o = oracle.swiglu_fwd(X, W1, W3, W2)
+            oracle.swiglu_bwd(X, a, b, h, dO, W1, W3, W2)
+            t_exp += time.perf_counter() - t0
         flops += 18.0 * wl.d * wl.f * (r1 - r0)
         n_exp += 1
         rows_done += r1 - r0
@@ -168,7 +237,8 @@ def cpu_baseline(wl, inp, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: route + permutation map of all {wl.T} tokens "
+        "sample": (f"fp64 NumPy oracle{' (e4m3 chain: quantise, dequantise, fp64 products)' if wl.dtype == 'e4m3' else ''}: "
+                   f"route + permutation map of all {wl.T} tokens "
                    f"({t_route:.2f} s), then SwiGLU fwd+bwd of experts 0..{n_exp - 1} "
                    f"({rows_done} of {wl.P} routed rows) in {t_exp:.1f} s; host has "
                    f"{len(os.sched_getaffinity(0))} usable cores"),
@@ -204,8 +274,8 @@ def main():
         copy_calibration()
     inp = make_inputs(wl, seed=0, device="cuda")
     step = build_step(wl, inp)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
@@ -223,13 +293,17 @@ def main():
     def seg(a, b_):
         return sum(e[a].elapsed_time(e[b_]) for e in ev) / args.steps
 
-    t_route, t_perm, t_gf, t_comb, t_permb, t_gb, t_unp = (seg(i, i + 1) for i in range(7))
+    t_route, t_perm, t_gf, t_comb, t_permb, t_gb, t_unp, t_wq = (seg(i, i + 1) for i in range(8))
     s = 4 if wl.dtype == "f32" else 2
     flops = wl.flops_fwd_bwd()
     gemm_ms = t_gf + t_gb
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     move_bytes = (wl.T * wl.d + wl.P * wl.d) * s
+    if wl.dtype == "e4m3":
+        # quantise x (read bf16, write codes + scales), then move codes + scales
+        qx = wl.T * wl.d * (2 + 1) + wl.T * (wl.d // 128) * 4
+        move_bytes = qx + (wl.T + wl.P) * (wl.d + (wl.d // 128) * 4)
     perm_gbs = (move_bytes + 16 * wl.P) / (t_perm * 1e-3) / 1e9
     comb_gbs = (move_bytes + 8 * wl.P + (wl.T * wl.d * s if wl.f_shared else 0)) / (t_comb * 1e-3) / 1e9
     out = {
@@ -247,14 +321,17 @@ def main():
         "data": "synthetic (seeded N(0,1) logits and activations, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "f": wl.f,
                    "f_shared": wl.f_shared},
-        "roofline": {"kernel": "grouped GEMM (all fwd+bwd launches of a step)", "bound": "mfma",
+        "roofline": {"kernel": ("grouped GEMM (all fwd+bwd launches of a step)" if wl.dtype != "e4m3"
+                                else "e4m3 grouped-GEMM calls (fwd+bwd, with the h, dO, dab and "
+                                     "token-block quantisations they run)"), "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": gemm_traffic(wl),
                      "traffic_unit": "bytes per step (all grouped-GEMM launches)"},
         "breakdown_ms": {"route": round(t_route, 4), "permute": round(t_perm, 4),
                          "gemm_fwd": round(t_gf, 4), "combine": round(t_comb, 4),
                          "combine_bwd_permute": round(t_permb, 4), "gemm_bwd": round(t_gb, 4),
-                         "unpermute": round(t_unp, 4)},
+                         "unpermute": round(t_unp, 4),
+                         "quantize_weights": round(t_wq, 4)},
         "hbm": {"permute_GBps": round(perm_gbs, 1), "combine_GBps": round(comb_gbs, 1),
                 "permute_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
                 "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},

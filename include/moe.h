@@ -33,10 +33,13 @@
  *    P < 2^31.  The bf16 expert GEMMs need d and f to be multiples of 128.
  *  - Expert weights: W1, W3 are [E][d][f], W2 is [E][f][d]; expert e maps a
  *    row x to o = (silu(x W1_e) * (x W3_e)) W2_e with silu(z) = z / (1+e^-z).
- *  - Dtypes: MOE_F32 (every tensor fp32) or MOE_BF16 (x, weights, outputs and
+ *  - Dtypes: MOE_F32 (every tensor fp32), MOE_BF16 (x, weights, outputs and
  *    saved activations bf16, fp32 accumulation, one round-to-nearest-even per
- *    output element).  Router logits and probabilities are always fp32
- *    (German summary, section 2 E: the router stays in high precision).
+ *    output element) or MOE_E4M3 (the expert GEMMs take OCP E4M3FN operands
+ *    with fp32 block scales -- see "e4m3 expert GEMMs" below -- while x, dY,
+ *    y, dX, the saved activations and the weight gradients are bf16).  Router
+ *    logits and probabilities are always fp32 (German summary, section 2 E:
+ *    the router stays in high precision).
  */
 #ifndef TRE_MOE_H
 #define TRE_MOE_H
@@ -56,7 +59,7 @@ typedef enum {
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
 
 typedef struct {
   int64_t T, d, E, k, f;
@@ -183,13 +186,23 @@ typedef struct {
   void* dX;                               /* [T][d] */
   void *dW1, *dW3, *dW2;                  /* like W1, W3, W2 */
   void *dWs1, *dWs3, *dWs2;               /* like Ws1, Ws3, Ws2 */
+  /* e4m3 layers only (sh->dtype == MOE_E4M3; ignored otherwise): the
+     quantised weights replace W1, W3, W2, which may be NULL; xp is not
+     used (the backward reads x and token_of instead) */
+  const struct moe_e4m3_weights* wq;
+  uint8_t* xq;                            /* [T][d] codes of x */
+  float* xs;                              /* [T][d/128] scales of x */
+  uint8_t* xpq;                           /* [P][d] permuted codes */
+  float* xps;                             /* [P][d/128] permuted scales */
 } moe_layer_io;
 
 /*
  * moe_layer_fwd -- route, permute, expert forward (+ shared expert applied to
  * every token with weight 1), weighted combine into y.  Same as calling
  * moe_route, moe_permute(build_map=1), moe_grouped_gemm_fwd and
- * moe_unpermute in sequence on one stream.
+ * moe_unpermute in sequence on one stream.  For MOE_E4M3: moe_route,
+ * moe_quantize_rows of x into xq/xs, moe_permute_e4m3 into xpq/xps,
+ * moe_grouped_gemm_fwd_e4m3, moe_unpermute.
  */
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -198,10 +211,115 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
  * moe_layer_bwd -- backward of moe_layer_fwd for upstream gradient dY:
  * dO = p * dY permuted, expert backward, dX = un-permuted sum of dXp (+ the
  * shared expert's dXs), and all weight gradients.  No gradient flows to the
- * logits, which are an input of the layer.
+ * logits, which are an input of the layer.  For MOE_E4M3 the expert backward
+ * is moe_grouped_gemm_bwd_e4m3.
  */
 int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
+
+/*
+ * e4m3 expert GEMMs
+ * -----------------
+ * The pages train the experts in FP8 with blockwise scaling on Hopper and
+ * quantise weights straight from fp32 masters, keeping the router in high
+ * precision (German technical summary, section 2 E; French summary, section
+ * 2 E).  The quantiser used for every block B of values:
+ *   amax = max |v| over B; scale = 1 if amax == 0 else fp32(amax / 448);
+ *   code = OCP E4M3FN(fp32(v / scale)) rounded to nearest even, saturating
+ *   at +-448, subnormals kept, -0 and tiny negatives -> 0x80; an all-zero
+ *   block has every code +0.  A code stands for code * scale.
+ * Block shapes: 1 x 128 along the contraction for activations and
+ * gradients (xp, h, dO, da|db), 128 x 128 tiles for expert weights, and for
+ * the weight-gradient products (contraction over an expert's rows) 128
+ * consecutive rows of one expert per column, the expert's last block short.
+ * The GEMMs accumulate in fp32: each 128-long block product is added times
+ * the product of its two scales.  Outputs are bf16.  d and f must be
+ * multiples of 128; e4m3 layers have no shared expert.
+ */
+
+/* Quantised expert weights as written by moe_quantize_weights. */
+typedef struct moe_e4m3_weights {
+  const uint8_t *W1, *W3, *W2;    /* codes [E][d][f], [E][d][f], [E][f][d] */
+  const uint8_t *W1t, *W3t, *W2t; /* transposed codes [E][f][d], [E][f][d], [E][d][f] */
+  const float *W1s, *W3s, *W2s;   /* tile scales [E][d/128][f/128] (W1, W3), [E][f/128][d/128] (W2) */
+} moe_e4m3_weights;
+
+/*
+ * moe_quantize_rows -- 1 x 128 blocks along each row of src [rows][cols]
+ * (src_dtype MOE_BF16 or MOE_F32, cols a multiple of 128):
+ *   codes  out uint8 [rows][cols];  scales out fp32 [rows][cols/128].
+ */
+int moe_quantize_rows(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                      uint8_t* codes, float* scales, void* stream);
+
+/*
+ * moe_quantize_weights -- 128 x 128 tiles of E fp32 matrices W [E][R][C]
+ * (R, C multiples of 128):
+ *   codes   out uint8 [E][R][C];
+ *   codes_t out uint8 [E][C][R], the same codes transposed (may be NULL);
+ *   scales  out fp32 [E][R/128][C/128].
+ * For a layer: W1 and W3 with (R, C) = (d, f), W2 with (f, d).
+ */
+int moe_quantize_weights(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                         uint8_t* codes_t, float* scales, void* stream);
+
+/* Number of 128-row blocks that P rows over E experts can need at most
+ * (P/128 + E); the token-block buffers below are sized with it. */
+int64_t moe_token_block_capacity(int64_t P, int64_t E);
+
+/*
+ * moe_quantize_token_blocks -- the weight-gradient operand blocks: for every
+ * expert e (rows offsets[e] .. offsets[e+1]-1 of a [P][C] matrix) and each
+ * of its 128-row blocks b (the last one short), one block per column.
+ * Row r of the matrix is row src_row[r] of src (src_row NULL: row r), src
+ * bf16 [.][C], C a multiple of 128.  With cap = moe_token_block_capacity:
+ *   blk     out int32 [E+1]: first block of each expert, blk[E] = blocks used;
+ *   codes_t out uint8 [C][128 * cap]: codes transposed; row r of expert e
+ *           sits at column 128 * blk[e] + (r - offsets[e]); columns of a
+ *           short block past the expert's rows, and unused blocks, hold 0
+ *           (unused blocks are not written);
+ *   scales  out fp32 [cap][C]: scale of block b at row b.
+ */
+int moe_quantize_token_blocks(const int32_t* offsets, int64_t E, int64_t P, const void* src,
+                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes_t,
+                              float* scales, void* stream);
+
+/*
+ * moe_permute_e4m3 -- moe_permute for rows of e4m3 codes: codes [T][d] and
+ * their scales [T][d/128] (from moe_quantize_rows of x) are copied bit for
+ * bit to dst_codes [P][d] and dst_scales [P][d/128] at row row_of[t][j];
+ * build_map and the map arguments as in moe_permute (quantising before the
+ * permutation gives the same rows as after it, as scales are per row).
+ */
+int moe_permute_e4m3(const moe_shape* sh, const uint8_t* codes, const float* scales,
+                     const int32_t* topk_idx, int build_map, int32_t* counts, int32_t* offsets,
+                     int32_t* row_of, int32_t* token_of, uint8_t* dst_codes, float* dst_scales,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm_fwd_e4m3 -- moe_grouped_gemm_fwd with e4m3 operands:
+ * [a|b] = xp W{1,3} from xpq [P][d] / xps [P][d/128] and the weight codes;
+ * ab and h = silu(a) * b are stored bf16; h is quantised (1 x 128 along f)
+ * into the workspace and o = h W2 is stored bf16.  sh->dtype == MOE_E4M3;
+ * ws_bytes >= moe_workspace_bytes(sh, MOE_WS_GEMM_FWD).
+ */
+int moe_grouped_gemm_fwd_e4m3(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq,
+                              const float* xps, const moe_e4m3_weights* w, void* ab, void* h,
+                              void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd_e4m3 -- moe_grouped_gemm_bwd with e4m3 operands.
+ * dO (bf16 [P][d]) is quantised 1 x 128 along d; dab = [da|db] is stored
+ * bf16 and quantised 1 x 128 along 2f for dXp = da W1^T + db W3^T; the
+ * weight gradients take token blocks of h, dO, dab and of the permuted x
+ * (row r is x[token_of[r]], x bf16 [T][d]).  All outputs bf16.
+ * ws_bytes >= moe_workspace_bytes(sh, MOE_WS_GEMM_BWD).
+ */
+int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
+                              const int32_t* token_of, const void* x, const void* ab,
+                              const void* h, const void* dO, const moe_e4m3_weights* w, void* dab,
+                              void* dXp, void* dW1, void* dW3, void* dW2, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);

@@ -4,10 +4,14 @@ The compute path is the HIP library libtre_moe.so (C ABI in include/moe.h);
 this package only marshals torch tensors into its calls.
 """
 from . import _native
-from .ops import (MoeError, make_shape, moe_grouped_gemm_bwd, moe_grouped_gemm_fwd,
-                  moe_layer_bwd, moe_layer_fwd, moe_permute, moe_route, moe_status_str,
-                  moe_unpermute, moe_workspace_bytes)
+from .ops import (E4M3Weights, MoeError, make_shape, moe_grouped_gemm_bwd,
+                  moe_grouped_gemm_bwd_e4m3, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_e4m3,
+                  moe_layer_bwd, moe_layer_fwd, moe_permute, moe_permute_e4m3,
+                  moe_quantize_rows, moe_quantize_token_blocks, moe_quantize_weights, moe_route,
+                  moe_status_str, moe_token_block_capacity, moe_unpermute, moe_workspace_bytes)
 
 __all__ = ["MoeError", "make_shape", "moe_route", "moe_permute", "moe_unpermute",
            "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_layer_fwd", "moe_layer_bwd",
-           "moe_workspace_bytes", "moe_status_str", "_native"]
+           "moe_workspace_bytes", "moe_status_str", "moe_quantize_rows", "moe_quantize_weights",
+           "moe_token_block_capacity", "moe_quantize_token_blocks", "moe_permute_e4m3",
+           "moe_grouped_gemm_fwd_e4m3", "moe_grouped_gemm_bwd_e4m3", "E4M3Weights", "_native"]

@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtre_moe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 (MOE_WS_PERMUTE, MOE_WS_GEMM_FWD, MOE_WS_GEMM_BWD, MOE_WS_LAYER_FWD,
  MOE_WS_LAYER_BWD) = range(5)
 
@@ -30,11 +30,20 @@ _IO_FIELDS = [
 ]
 
 
+# e4m3 layers: `wq` points to a moe_e4m3_weights struct; the rest are tensors
+_IO_FIELDS_E4M3 = ["wq", "xq", "xs", "xpq", "xps"]
+
+
 class moe_layer_io(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in _IO_FIELDS]
+    _fields_ = [(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3]
 
 
-IO_FIELDS = tuple(_IO_FIELDS)
+IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:])
+
+
+class moe_e4m3_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("W1", "W3", "W2", "W1t", "W3t", "W2t", "W1s", "W3s", "W2s")]
 
 _P = C.c_void_p
 _I64 = C.c_int64
@@ -48,6 +57,17 @@ _PROTOS = {
                                        _P, C.c_size_t, _P]),
     "moe_layer_fwd": (C.c_int, [_SH, C.POINTER(moe_layer_io), _P, C.c_size_t, _P]),
     "moe_layer_bwd": (C.c_int, [_SH, C.POINTER(moe_layer_io), _P, C.c_size_t, _P]),
+    "moe_quantize_rows": (C.c_int, [_P, C.c_int32, _I64, _I64, _P, _P, _P]),
+    "moe_quantize_weights": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "moe_token_block_capacity": (C.c_int64, [_I64, _I64]),
+    "moe_quantize_token_blocks": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "moe_permute_e4m3": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
+                                   C.c_size_t, _P]),
+    "moe_grouped_gemm_fwd_e4m3": (C.c_int, [_SH, _P, _P, _P, C.POINTER(moe_e4m3_weights), _P, _P,
+                                            _P, _P, C.c_size_t, _P]),
+    "moe_grouped_gemm_bwd_e4m3": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P,
+                                            C.POINTER(moe_e4m3_weights), _P, _P, _P, _P, _P, _P,
+                                            C.c_size_t, _P]),
     "moe_workspace_bytes": (C.c_size_t, [_SH, C.c_int]),
     "moe_status_str": (C.c_char_p, [C.c_int]),
 }

@@ -4,7 +4,7 @@ from __future__ import annotations
 import torch
 
 from . import _native as N
-from .ops import make_shape, moe_workspace_bytes
+from .ops import E4M3Weights, make_shape, moe_quantize_weights, moe_workspace_bytes
 
 
 def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None):
@@ -14,7 +14,7 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """
     sh = make_shape(T, d, E, k, f, f_shared, dtype)
-    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16  # e4m3 layers: bf16 activations
     P = T * k
     b = dict(inputs or {})
 
@@ -27,6 +27,13 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
              xp=z(P, d), ab=z(P, 2 * f), h=z(P, f), o=z(P, d), y=z(T, d),
              dO=z(P, d), dab=z(P, 2 * f), dXp=z(P, d), dX=z(T, d),
              dW1=z(E, d, f), dW3=z(E, d, f), dW2=z(E, f, d))
+    if dtype == "e4m3":
+        u8 = torch.uint8
+        b.pop("xp")
+        b.update(xq=z(T, d, dtype=u8), xs=z(T, d // 128, dtype=torch.float32),
+                 xpq=z(P, d, dtype=u8), xps=z(P, d // 128, dtype=torch.float32))
+        if "W1" in b and b["W1"].dtype == torch.float32:
+            b["wq"] = quantized_weights(b["W1"], b["W3"], b["W2"])
     if f_shared:
         b.update(s_ab=z(T, 2 * f_shared), s_h=z(T, f_shared), ys=z(T, d), s_dab=z(T, 2 * f_shared),
                  dXs=z(T, d), dWs1=z(d, f_shared), dWs3=z(d, f_shared), dWs2=z(f_shared, d))
@@ -35,3 +42,24 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     ws_b = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD)), dtype=torch.uint8,
                        device=device)
     return sh, b, ws_f, ws_b
+
+
+def quantized_weights(W1, W3, W2, stream=None) -> E4M3Weights:
+    """e4m3 codes, transposed codes and 128 x 128 scales of fp32 expert weights
+    (W1, W3 [E][d][f], W2 [E][f][d]), made by moe_quantize_weights."""
+    E, d, f = W1.shape
+    dev = W1.device
+    t = {}
+    for name, W, R, Cc in (("W1", W1, d, f), ("W3", W3, d, f), ("W2", W2, f, d)):
+        t[name] = torch.empty(E, R, Cc, dtype=torch.uint8, device=dev)
+        t[name + "t"] = torch.empty(E, Cc, R, dtype=torch.uint8, device=dev)
+        t[name + "s"] = torch.empty(E, R // 128, Cc // 128, dtype=torch.float32, device=dev)
+    wq = E4M3Weights(t)
+    requantize_weights(wq, W1, W3, W2, stream)
+    return wq
+
+
+def requantize_weights(wq: E4M3Weights, W1, W3, W2, stream=None):
+    """Refresh wq from the fp32 masters (e.g. after an optimizer step)."""
+    for name, W in (("W1", W1), ("W3", W3), ("W2", W2)):
+        moe_quantize_weights(W, wq[name], wq[name + "t"], wq[name + "s"], stream)

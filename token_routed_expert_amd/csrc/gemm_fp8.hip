@@ -1,0 +1,353 @@
+// Grouped expert GEMMs with e4m3 operands and fp32 block scales on CDNA4
+// matrix cores, fp32 accumulation, bf16 outputs.
+//
+// The pages run the expert GEMMs in FP8 with blockwise scaling (German
+// technical summary of "Scalable Training of Mixture-of-Experts Models with
+// Megatron Core", section 2 E; French summary, section 2 E); the block shapes
+// are 1 x 128 along the contraction for activations, 128 x 128 for weights,
+// and 128 tokens per column for the operands of the weight gradients.  Every
+// scale block spans exactly 128 values of the contraction axis, which is the
+// K of one v_mfma_f32_16x16x128_f8f6f4: each MFMA yields the exact partial
+// product of one scale block, and the lane adds it to its fp32 accumulator
+// times the two block scales (scale promotion per 128-K block).
+//
+// All six products read both operands with the contraction axis contiguous
+// (C[m][n] = sum_k A[m][k] B[n][k]): the weight quantiser stores transposed
+// codes for the forward products and the token-block quantiser stores the
+// weight-gradient operands transposed, so one LDS layout serves every op:
+//
+//   op          A (rows x K)                 B (rows x K)               K
+//   FC1_FWD     xp codes [P][d]              W1^T, W3^T codes [f][d]    d
+//   FC2_FWD     h codes  [P][f]              W2^T codes [d][f]          f
+//   FC2_DGRAD   dO codes [P][d]              W2 codes [f][d]            d
+//   FC1_DGRAD   dab codes [P][2f]            W1 | W3 codes [d][f]       2f
+//   FC2_WGRAD   h^T token blocks [f][.]      dO^T token blocks [d][.]   128 * blocks
+//   FC1_WGRAD   xp^T token blocks [d][.]     dab^T token blocks [2f][.] of the expert
+//
+// Tiles, schedule and epilogues are those of the bf16 kernels (256 x 256
+// block tile, 8 wavefronts of 128 x 64, device-side ragged-M schedule, fused
+// SwiGLU forward / backward epilogues, bf16 stores).  K advances 128 per
+// stage through a 2-deep LDS ring (64 KB per stage) filled by buffer_load ...
+// lds; a K-contiguous LDS row is 128 bytes (8 chunks of 16) with chunk c of
+// row r stored at c ^ ((r >> 1) & 7), so the 16 rows of a fragment read hit
+// all 64 banks.  A fragment (32 consecutive K bytes of one row per lane) is
+// two ds_read_b128.
+#include "gemm_common.h"
+
+namespace tre {
+
+namespace {
+using namespace gemm;
+
+constexpr int BM = 256, BN = 256, BK = 128, NSTAGE = 2, NW = 8;
+constexpr int OPND_BYTES = 256 * BK;            // 32 KB of codes per operand and stage
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;     // A then B
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 32 one-KB DMA instructions
+constexpr int DMA_PER_WAVE = DMA_PER_OPND / NW;  // 4 per operand and stage
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int c0, int sw) {
+  const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((c0 ^ sw) << 4));
+  const i32x4_t hi =
+      *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((c0 + 1) ^ sw) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& b, const i32x8_t& a) {
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, z, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ f32x4_t buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int OP>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
+  constexpr int WAVES_N = NW / 2;
+  constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
+  constexpr int FM = WM / 16, FN = WN / 16;      // 8 x 4 MFMA blocks
+  constexpr bool RAGGED = OP <= OP_FC1_DGRAD;
+  constexpr bool WGRAD = !RAGGED;
+
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
+  __shared__ int sched[NW + 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = uniform(tid >> 6);
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int d = args.d, f = args.f;
+
+  // ---------------------------------------------------------------- tile
+  TileInfo ti;
+  int K, M, N, kb0 = 0;
+  if constexpr (RAGGED) {
+    if (!decode_ragged_m<BM, NW>(args.offsets, args.E, NT, sched, ti)) return;
+    ti.n0 *= BN;
+    K = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
+    N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
+  } else {
+    const int total = args.E * MT * NT;
+    if ((int)blockIdx.x >= total) return;
+    const int logical = xcd_remap(blockIdx.x, total);
+    ti.e = logical / (MT * NT);
+    const int rem = logical % (MT * NT);
+    ti.m0 = (rem / NT) * BM;
+    ti.n0 = (rem % NT) * BN;
+    ti.row0 = args.offsets[ti.e];
+    ti.rows = args.offsets[ti.e + 1] - ti.row0;
+    kb0 = args.blk[ti.e];
+    K = (args.blk[ti.e + 1] - kb0) * BK;  // the expert's token blocks, zero-padded
+    N = (OP == OP_FC2_WGRAD) ? d : 2 * f;
+  }
+  ti.e = uniform(ti.e);
+  ti.row0 = uniform(ti.row0);
+  ti.rows = uniform(ti.rows);
+  ti.m0 = uniform(ti.m0);
+  ti.n0 = uniform(ti.n0);
+  kb0 = uniform(kb0);
+  K = uniform(K);
+  M = RAGGED ? ti.rows : ((OP == OP_FC2_WGRAD) ? f : d);
+  const size_t e = (size_t)ti.e;
+  const int KT = K / BK;
+
+  // ---------------------------------------------------------------- operands
+  rsrc_t a_src, b_src, b_src2;
+  uint32_t a_ld, b_ld;
+  if constexpr (RAGGED) {
+    a_ld = (uint32_t)K;
+    a_src = make_rsrc(args.a_q + (size_t)ti.row0 * K, (uint32_t)ti.rows * a_ld);
+  } else {
+    a_ld = (uint32_t)args.ldt;
+    a_src = make_rsrc(args.a_q + (size_t)ti.m0 * args.ldt + (size_t)kb0 * BK,
+                      (uint32_t)(M - ti.m0) * a_ld);
+  }
+  if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
+    b_ld = (uint32_t)d;
+    const size_t off = e * (size_t)f * d + (size_t)(ti.n0 / 2) * d;
+    b_src = make_rsrc(args.b_q + off, 128u * b_ld);
+    b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
+  } else if constexpr (OP == OP_FC2_FWD) {  // W2^T [d][f]
+    b_ld = (uint32_t)f;
+    b_src = make_rsrc(args.b_q + e * (size_t)d * f + (size_t)ti.n0 * f, (uint32_t)(d - ti.n0) * b_ld);
+    b_src2 = b_src;
+  } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 [f][d]
+    b_ld = (uint32_t)d;
+    b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0 * d, (uint32_t)(f - ti.n0) * b_ld);
+    b_src2 = b_src;
+  } else if constexpr (OP == OP_FC1_DGRAD) {  // W1 | W3 [d][f], K = 2f
+    b_ld = (uint32_t)f;
+    const size_t off = e * (size_t)d * f + (size_t)ti.n0 * f;
+    b_src = make_rsrc(args.b_q + off, (uint32_t)(d - ti.n0) * b_ld);
+    b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)(d - ti.n0) * b_ld);
+  } else {  // wgrad: token-block operand [N][ldt]
+    b_ld = (uint32_t)args.ldt;
+    b_src = make_rsrc(args.b_q + (size_t)ti.n0 * args.ldt + (size_t)kb0 * BK,
+                      (uint32_t)(N - ti.n0) * b_ld);
+    b_src2 = b_src;
+  }
+
+  // DMA: instruction tt (0..31) of an operand covers tile rows 8tt..8tt+7;
+  // lane -> row 8tt + lane/8, LDS chunk lane%8 holding K chunk (lane%8) ^ swz(row).
+  // This wavefront issues tt = wid*4 + t, t < 4, for A and for B.
+  uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int tt = wid * DMA_PER_WAVE + t;
+    const int row = 8 * tt + (lane >> 3);
+    const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
+    a_off[t] = (uint32_t)row * a_ld + ch;
+    const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
+    b_off[t] = (uint32_t)brow * b_ld + ch;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t st = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
+    const uint32_t ka = (uint32_t)kt * BK;
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int tt = wid * DMA_PER_WAVE + t;
+      dma16(a_src, a_off[t] + ka, st + tt * 1024);
+    }
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int tt = wid * DMA_PER_WAVE + t;
+      const uint32_t m0 = st + OPND_BYTES + tt * 1024;
+      if constexpr (OP == OP_FC1_FWD) {
+        dma16(tt < 16 ? b_src : b_src2, b_off[t] + ka, m0);
+      } else if constexpr (OP == OP_FC1_DGRAD) {
+        const bool second = (int)ka >= f;
+        dma16(second ? b_src2 : b_src, b_off[t] + (second ? ka - (uint32_t)f : ka), m0);
+      } else {
+        dma16(b_src, b_off[t] + ka, m0);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- scales
+  // sa[i]: scale of the A block of fragment row m = wm*WM + 16 i + (lane & 15);
+  // ragged ops: a_s[(row0 + m) * K/128 + kt] (0 past the expert's rows);
+  // wgrad: a_s[(kb0 + kt) * M_total + m0 + m].
+  const int lm = lane & 15, lg = lane >> 4;
+  __amdgpu_buffer_rsrc_t sa_src, sb_src;
+  uint32_t sa_stride;  // bytes between the scales of consecutive stages
+  uint32_t sa_off0;
+  if constexpr (RAGGED) {
+    sa_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_s + (size_t)ti.row0 * (K / BK)), 0,
+                                               ti.rows * (K / BK) * 4, 0x00020000);
+    sa_stride = 4;
+    sa_off0 = (uint32_t)(wm * WM + lm) * (uint32_t)(K / BK) * 4u;
+  } else {
+    const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
+    sa_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_s + (size_t)kb0 * Mt), 0,
+                                               (K / BK) * Mt * 4, 0x00020000);
+    sa_stride = (uint32_t)Mt * 4u;
+    sa_off0 = (uint32_t)(ti.m0 + wm * WM + lm) * 4u;
+    sb_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_s + (size_t)kb0 * N), 0,
+                                               (K / BK) * N * 4, 0x00020000);
+  }
+  const uint32_t sa_istep = RAGGED ? 16u * (uint32_t)(K / BK) * 4u : 64u;  // 16 rows
+  auto load_sa = [&](int kt, float (&sa)[FM]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sa[i] = buf_f32(sa_src, sa_off0 + (uint32_t)i * sa_istep + (uint32_t)kt * sa_stride);
+  };
+  // wgrad: sb[j] = scales of columns n0 + wn*WN + 16 j + 4 (lane >> 4) + 0..3
+  auto load_sb = [&](int kt, f32x4_t (&sb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      sb[j] = buf_f32x4(sb_src, ((uint32_t)kt * N + ti.n0 + wn * WN + 16 * j + 4 * lg) * 4u);
+  };
+  // ragged ops: the weight block scale is one value per wavefront and stage
+  // (fc1 forward: one for the W1 half, one for the W3 half).  nbw: the
+  // wavefront's 128-column block of B rows, clamped for wavefronts past N in
+  // a last, half-filled N-tile (their columns are never stored).
+  const int nbw = min((ti.n0 + wn * WN) / 128, (N - 1) / 128);
+  auto weight_scale = [&](int kt, int half) __attribute__((always_inline)) -> float {
+    if constexpr (OP == OP_FC1_FWD) {  // W1s / W3s [E][d/128][f/128], block (kt, f-block)
+      const float* s = half ? args.b_s2 : args.b_s;
+      return s[(e * (d / 128) + kt) * (f / 128) + (ti.n0 / 2) / 128];
+    } else if constexpr (OP == OP_FC2_FWD) {  // W2s [E][f/128][d/128], block (kt, d-block)
+      return args.b_s[(e * (f / 128) + kt) * (d / 128) + nbw];
+    } else if constexpr (OP == OP_FC2_DGRAD) {  // W2s, block (f-block of n, kt)
+      return args.b_s[(e * (f / 128) + nbw) * (d / 128) + kt];
+    } else {  // FC1_DGRAD: W1s / W3s [E][d/128][f/128], block (d-block of n, kt mod f/128)
+      const int fb = f / 128;
+      const float* s = kt < fb ? args.b_s : args.b_s2;
+      return s[(e * (d / 128) + nbw) * fb + (kt < fb ? kt : kt - fb)];
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  float sa[FM], sa_n[FM];
+  f32x4_t sb[FN], sb_n[FN];
+  if (KT > 0) {
+    load_sa(0, sa);
+    if constexpr (WGRAD) load_sb(0, sb);
+    issue_stage(0);
+  }
+  wait_vmcnt<0>();
+  block_barrier();
+
+  // B rows of fragment j within the B tile (fc1 forward: W1 rows then W3 rows)
+  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (OP == OP_FC1_FWD) return (j < FN / 2 ? 0 : 128) + wn * (WN / 2) + 16 * (j % (FN / 2)) + lm;
+    else return wn * WN + 16 * j + lm;
+  };
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
+    if (kt + 1 < KT) {
+      load_sa(kt + 1, sa_n);
+      if constexpr (WGRAD) load_sb(kt + 1, sb_n);
+      issue_stage(kt + 1);
+    }
+    float wsc0 = 0.f, wsc1 = 0.f;
+    if constexpr (RAGGED) {
+      wsc0 = weight_scale(kt, 0);
+      wsc1 = (OP == OP_FC1_FWD) ? weight_scale(kt, 1) : wsc0;
+    }
+    i32x8_t bf[FN];
+    static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+      const int r = b_row(J.value);
+      bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, 2 * lg, swz(r));
+    });
+    static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = I.value;
+      const int r = wm * WM + 16 * i + lm;
+      const i32x8_t af = lds_frag(cur + r * BK, 2 * lg, swz(r));
+      static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = J.value;
+        const f32x4_t p = mfma_fp8(bf[j], af);
+        if constexpr (RAGGED) {
+          const float s = sa[i] * (j < FN / 2 ? wsc0 : wsc1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], s, acc[i][j][q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], sa[i] * sb[j][q], acc[i][j][q]);
+        }
+      });
+    });
+    wait_vmcnt<0>();
+    block_barrier();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
+    if constexpr (WGRAD) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
+}
+
+template <int OP>
+int launch(const GemmArgs& a, hipStream_t s) {
+  int NT, MT = 0;
+  int64_t grid;
+  if (OP <= OP_FC1_DGRAD) {
+    const int N = (OP == OP_FC1_FWD) ? 2 * a.f : (OP == OP_FC2_DGRAD ? a.f : a.d);
+    NT = (N + BN - 1) / BN;
+    grid = ((int64_t)a.P / BM + a.E) * NT;
+  } else {
+    const int M = (OP == OP_FC2_WGRAD) ? a.f : a.d;
+    const int N = (OP == OP_FC2_WGRAD) ? a.d : 2 * a.f;
+    MT = (M + BM - 1) / BM;
+    NT = (N + BN - 1) / BN;
+    grid = (int64_t)a.E * MT * NT;
+  }
+  if (grid == 0) return MOE_OK;
+  gemm_fp8_kernel<OP><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace
+
+int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_FC1_FWD: return launch<OP_FC1_FWD>(a, s);
+    case OP_FC2_FWD: return launch<OP_FC2_FWD>(a, s);
+    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD>(a, s);
+    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD>(a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD>(a, s);
+  }
+  return MOE_ERR_INVALID;
+}
+
+}  // namespace tre

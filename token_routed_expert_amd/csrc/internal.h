@@ -52,11 +52,41 @@ struct GemmArgs {
   void* dW1;
   void* dW3;
   void* dW2;
+  // e4m3 products only (gemm_fp8.hip).  Every operand is K-contiguous codes:
+  //   ragged-M ops: A = a_q [P][K] with scales a_s [P][K/128]; B = weight
+  //     codes laid out [n][k] (b_q, and b_q2 for the W3 half of fc1 products)
+  //     with 128x128 block scales b_s, b_s2 as stored by the weight quantiser;
+  //   wgrad ops: A = a_q [M][ldt], B = b_q [N][ldt] (token blocks of the
+  //     expert start at column 128 * blk[e]) with scales a_s [NB][M], b_s [NB][N].
+  const uint8_t* a_q;
+  const float* a_s;
+  const uint8_t* b_q;
+  const uint8_t* b_q2;
+  const float* b_s;
+  const float* b_s2;
+  const int32_t* blk;  // [E+1] token-block table (wgrad)
+  int64_t ldt;         // row length in bytes of the token-block operands (wgrad)
 };
 
 // gemm_bf16.hip: MFMA kernels, bf16 in/out, fp32 accumulation
 int gemm_bf16_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // gemm_f32.hip: fp32 kernels
 int gemm_f32_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
+// gemm_fp8.hip: e4m3 x e4m3 MFMA with per-128-K scale promotion, bf16 outputs
+int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
+
+// quant.hip: e4m3 block quantisers
+int quant_rows_launch(const void* src, bool src_f32, int64_t rows, int64_t cols, uint8_t* codes,
+                      float* scales, hipStream_t s);
+int quant_tiles_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                       uint8_t* codes_t, float* scales, hipStream_t s);
+int64_t tokblk_max_blocks(int64_t P, int64_t E);  // bound on sum_e ceil(m_e / 128)
+int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t s);
+int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
+                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                        float* scales, hipStream_t s);
+// permute.hip: rows of e4m3 codes [T][d] and their scales [T][d/128]
+int permute_e4m3_launch(const uint8_t* codes, const float* scales, const int32_t* row_of, int T,
+                        int k, int d, uint8_t* dst_codes, float* dst_scales, hipStream_t s);
 
 }  // namespace tre

@@ -4,6 +4,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 using namespace tre;
 
 namespace {
@@ -22,7 +24,9 @@ int check_shape(const moe_shape* sh) {
   if (sh->T < 1 || sh->d < 1 || sh->E < 1 || sh->k < 1 || sh->f < 1 || sh->f_shared < 0)
     return MOE_ERR_INVALID;
   if (sh->k > sh->E || sh->reserved != 0) return MOE_ERR_INVALID;
-  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16 && sh->dtype != MOE_E4M3)
+    return MOE_ERR_UNSUPPORTED;
+  if (sh->dtype == MOE_E4M3 && sh->f_shared != 0) return MOE_ERR_UNSUPPORTED;
   if (sh->E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (sh->T * sh->k >= ((int64_t)1 << 31) || sh->d >= (1 << 30) || sh->f >= (1 << 30) ||
       sh->f_shared >= (1 << 30))
@@ -33,8 +37,76 @@ int check_shape(const moe_shape* sh) {
 }
 
 int check_gemm_dims(const moe_shape* sh, int64_t f) {
-  if (sh->dtype == MOE_BF16 && (sh->d % 128 != 0 || f % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (sh->dtype != MOE_F32 && (sh->d % 128 != 0 || f % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// ---- e4m3 workspaces: consecutive 256-byte aligned regions
+struct Carver {
+  char* p;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = (T*)(p ? p + used : nullptr);
+    used += align_up(bytes, 256);
+    return r;
+  }
+};
+
+struct Fwd8Ws {
+  uint8_t* hq;
+  float* hs;
+};
+Fwd8Ws carve_fwd8(const moe_shape* sh, void* ws, size_t* bytes) {
+  const size_t P = (size_t)(sh->T * sh->k), f = (size_t)sh->f;
+  Carver c{(char*)ws};
+  Fwd8Ws w;
+  w.hq = c.take<uint8_t>(P * f);
+  w.hs = c.take<float>(P * (f / 128) * 4);
+  *bytes = c.used;
+  return w;
+}
+
+struct Bwd8Ws {
+  uint8_t *dOq, *dabq, *AT, *BT;
+  float *dOs, *dabs, *sA, *sB;
+  int32_t* blk;
+  int64_t cap;
+};
+Bwd8Ws carve_bwd8(const moe_shape* sh, void* ws, size_t* bytes) {
+  const size_t P = (size_t)(sh->T * sh->k), d = (size_t)sh->d, f = (size_t)sh->f;
+  const int64_t cap = tokblk_max_blocks((int64_t)P, sh->E);
+  const size_t Lt = 128 * (size_t)cap;
+  const size_t ma = f > d ? f : d, mb = d > 2 * f ? d : 2 * f;
+  Carver c{(char*)ws};
+  Bwd8Ws w;
+  w.cap = cap;
+  w.dOq = c.take<uint8_t>(P * d);
+  w.dOs = c.take<float>(P * (d / 128) * 4);
+  w.dabq = c.take<uint8_t>(P * 2 * f);
+  w.dabs = c.take<float>(P * (2 * f / 128) * 4);
+  w.blk = c.take<int32_t>((size_t)(sh->E + 1) * 4);
+  w.AT = c.take<uint8_t>(ma * Lt);
+  w.BT = c.take<uint8_t>(mb * Lt);
+  w.sA = c.take<float>((size_t)cap * ma * 4);
+  w.sB = c.take<float>((size_t)cap * mb * 4);
+  *bytes = c.used;
+  return w;
+}
+
+size_t fwd8_ws_bytes(const moe_shape* sh) {
+  size_t b;
+  carve_fwd8(sh, nullptr, &b);
+  return b;
+}
+size_t bwd8_ws_bytes(const moe_shape* sh) {
+  size_t b;
+  carve_bwd8(sh, nullptr, &b);
+  return b;
+}
+
+bool weights_ok(const moe_e4m3_weights* w) {
+  return w && w->W1 && w->W3 && w->W2 && w->W1t && w->W3t && w->W2t && w->W1s && w->W3s && w->W2s;
 }
 
 int run_gemm(const moe_shape* sh, GemmOp op, const GemmArgs& a, hipStream_t s) {
@@ -77,6 +149,11 @@ int bwd_sequence(const moe_shape* sh, GemmArgs a, hipStream_t s) {
   return run_gemm(sh, OP_FC1_WGRAD, a, s);
 }
 
+int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream);
+int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -94,6 +171,16 @@ const char* moe_status_str(int status) {
 
 size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
   if (check_shape(sh) != MOE_OK) return 0;
+  if (sh->dtype == MOE_E4M3) {
+    switch (kind) {
+      case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
+      case MOE_WS_GEMM_FWD: return fwd8_ws_bytes(sh);
+      case MOE_WS_GEMM_BWD: return bwd8_ws_bytes(sh);
+      case MOE_WS_LAYER_FWD: return permute_ws_bytes(sh->T, sh->E) + fwd8_ws_bytes(sh);
+      case MOE_WS_LAYER_BWD: return bwd8_ws_bytes(sh);
+    }
+    return 0;
+  }
   switch (kind) {
     case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
     case MOE_WS_GEMM_FWD:
@@ -149,6 +236,7 @@ int moe_grouped_gemm_fwd(const moe_shape* sh, const int32_t* offsets, const void
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->dtype == MOE_E4M3) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_fwd_e4m3
   if (!offsets || !xp || !W1 || !W3 || !W2 || !ab || !h || !o) return MOE_ERR_INVALID;
   GemmArgs a = expert_args(sh, offsets);
   a.xp = xp; a.W1 = W1; a.W3 = W3; a.W2 = W2;
@@ -165,6 +253,7 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->dtype == MOE_E4M3) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_bwd_e4m3
   if (!offsets || !xp || !ab || !h || !dO || !W1 || !W3 || !W2 || !dab || !dXp || !dW1 || !dW3 ||
       !dW2)
     return MOE_ERR_INVALID;
@@ -174,10 +263,139 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   return bwd_sequence(sh, a, (hipStream_t)stream);
 }
 
+int moe_quantize_rows(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                      uint8_t* codes, float* scales, void* stream) {
+  if (!src || !codes || !scales || rows < 0 || cols < 0) return MOE_ERR_INVALID;
+  if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (cols % 128 != 0 || rows * (cols / 128) >= ((int64_t)1 << 35)) return MOE_ERR_UNSUPPORTED;
+  return quant_rows_launch(src, src_dtype == MOE_F32, rows, cols, codes, scales,
+                           (hipStream_t)stream);
+}
+
+int moe_quantize_weights(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                         uint8_t* codes_t, float* scales, void* stream) {
+  if (!W || !codes || !scales || E < 0 || R < 0 || C < 0) return MOE_ERR_INVALID;
+  if (R % 128 != 0 || C % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (R >= (1 << 30) || C >= (1 << 30) || E > 65535 || C / 128 > 65535 || R / 128 > 65535)
+    return MOE_ERR_UNSUPPORTED;
+  return quant_tiles_launch(W, E, R, C, codes, codes_t, scales, (hipStream_t)stream);
+}
+
+int64_t moe_token_block_capacity(int64_t P, int64_t E) {
+  if (P < 0 || E < 0) return 0;
+  return tokblk_max_blocks(P, E);
+}
+
+int moe_quantize_token_blocks(const int32_t* offsets, int64_t E, int64_t P, const void* src,
+                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes_t,
+                              float* scales, void* stream) {
+  if (!offsets || !src || !blk || !codes_t || !scales) return MOE_ERR_INVALID;
+  if (E < 1 || P < 0 || C < 0) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (C % 128 != 0 || C >= (1 << 30) || P >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  // transposed rows are addressed with 32-bit offsets by the GEMMs
+  if ((C + 256) * 128 * tokblk_max_blocks(P, E) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  int st = tokblk_table_launch(offsets, (int)E, blk, s);
+  if (st) return st;
+  return quant_tokblk_launch(src, src_row, offsets, blk, (int)E, P, C, codes_t, scales, s);
+}
+
+int moe_permute_e4m3(const moe_shape* sh, const uint8_t* codes, const float* scales,
+                     const int32_t* topk_idx, int build_map, int32_t* counts, int32_t* offsets,
+                     int32_t* row_of, int32_t* token_of, uint8_t* dst_codes, float* dst_scales,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (sh->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!codes || !scales || !dst_codes || !dst_scales || !row_of) return MOE_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  if (build_map) {
+    if (!topk_idx || !counts || !offsets || !token_of) return MOE_ERR_INVALID;
+    if (!ws || ws_bytes < permute_ws_bytes(sh->T, sh->E)) return MOE_ERR_WORKSPACE;
+    st = permute_map_launch(topk_idx, (int)sh->T, (int)sh->E, (int)sh->k, counts, offsets, row_of,
+                            token_of, ws, s);
+    if (st) return st;
+  }
+  return permute_e4m3_launch(codes, scales, row_of, (int)sh->T, (int)sh->k, (int)sh->d, dst_codes,
+                             dst_scales, s);
+}
+
+int moe_grouped_gemm_fwd_e4m3(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq,
+                              const float* xps, const moe_e4m3_weights* w, void* ab, void* h,
+                              void* o, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (sh->dtype != MOE_E4M3) return MOE_ERR_INVALID;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!offsets || !xpq || !xps || !weights_ok(w) || !ab || !h || !o) return MOE_ERR_INVALID;
+  size_t need;
+  Fwd8Ws W = carve_fwd8(sh, ws, &need);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t P = sh->T * sh->k;
+  GemmArgs a = expert_args(sh, offsets);
+  a.a_q = xpq; a.a_s = xps;
+  a.b_q = w->W1t; a.b_q2 = w->W3t; a.b_s = w->W1s; a.b_s2 = w->W3s;
+  a.ab_out = ab; a.h_out = h;
+  if ((st = gemm_fp8_launch(OP_FC1_FWD, a, s))) return st;
+  if ((st = quant_rows_launch(h, false, P, sh->f, W.hq, W.hs, s))) return st;
+  a.a_q = W.hq; a.a_s = W.hs;
+  a.b_q = w->W2t; a.b_q2 = nullptr; a.b_s = w->W2s; a.b_s2 = nullptr;
+  a.o_out = o;
+  return gemm_fp8_launch(OP_FC2_FWD, a, s);
+}
+
+int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
+                              const int32_t* token_of, const void* x, const void* ab,
+                              const void* h, const void* dO, const moe_e4m3_weights* w, void* dab,
+                              void* dXp, void* dW1, void* dW3, void* dW2, void* ws,
+                              size_t ws_bytes, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (sh->dtype != MOE_E4M3) return MOE_ERR_INVALID;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!offsets || !token_of || !x || !ab || !h || !dO || !weights_ok(w) || !dab || !dXp || !dW1 ||
+      !dW3 || !dW2)
+    return MOE_ERR_INVALID;
+  size_t need;
+  Bwd8Ws W = carve_bwd8(sh, ws, &need);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int64_t P = sh->T * sh->k, d = sh->d, f = sh->f, E = sh->E;
+  if ((std::max(d, 2 * f) + 256) * 128 * W.cap >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs a = expert_args(sh, offsets);
+  // data gradients: dH = dO W2^T (+ SwiGLU backward -> dab), dXp = dab [W1|W3]^T
+  if ((st = quant_rows_launch(dO, false, P, d, W.dOq, W.dOs, s))) return st;
+  a.a_q = W.dOq; a.a_s = W.dOs; a.b_q = w->W2; a.b_s = w->W2s;
+  a.ab = ab; a.dab_out = dab;
+  if ((st = gemm_fp8_launch(OP_FC2_DGRAD, a, s))) return st;
+  if ((st = quant_rows_launch(dab, false, P, 2 * f, W.dabq, W.dabs, s))) return st;
+  a.a_q = W.dabq; a.a_s = W.dabs;
+  a.b_q = w->W1; a.b_q2 = w->W3; a.b_s = w->W1s; a.b_s2 = w->W3s;
+  a.dXp_out = dXp;
+  if ((st = gemm_fp8_launch(OP_FC1_DGRAD, a, s))) return st;
+  // weight gradients on 128-row token blocks: dW2 = h^T dO, [dW1|dW3] = xp^T dab
+  if ((st = tokblk_table_launch(offsets, (int)E, W.blk, s))) return st;
+  a.blk = W.blk;
+  a.ldt = 128 * W.cap;
+  if ((st = quant_tokblk_launch(h, nullptr, offsets, W.blk, (int)E, P, f, W.AT, W.sA, s))) return st;
+  if ((st = quant_tokblk_launch(dO, nullptr, offsets, W.blk, (int)E, P, d, W.BT, W.sB, s))) return st;
+  a.a_q = W.AT; a.a_s = W.sA; a.b_q = W.BT; a.b_q2 = nullptr; a.b_s = W.sB; a.b_s2 = nullptr;
+  a.dW2 = dW2;
+  if ((st = gemm_fp8_launch(OP_FC2_WGRAD, a, s))) return st;
+  if ((st = quant_tokblk_launch(x, token_of, offsets, W.blk, (int)E, P, d, W.AT, W.sA, s))) return st;
+  if ((st = quant_tokblk_launch(dab, nullptr, offsets, W.blk, (int)E, P, 2 * f, W.BT, W.sB, s)))
+    return st;
+  a.dW1 = dW1; a.dW3 = dW3;
+  return gemm_fp8_launch(OP_FC1_WGRAD, a, s);
+}
+
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
+  if (sh->dtype == MOE_E4M3) return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
   if (!io || !io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
@@ -217,6 +435,7 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
+  if (sh->dtype == MOE_E4M3) return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
   if (!io || !io->dY || !io->W1 || !io->W3 || !io->W2 || !io->topk_prob || !io->offsets ||
@@ -254,3 +473,49 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
 }
 
 }  // extern "C"
+
+namespace {
+
+int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!io || !io->logits || !io->x || !weights_ok(io->wq) || !io->topk_idx || !io->topk_prob ||
+      !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xq || !io->xs ||
+      !io->xpq || !io->xps || !io->ab || !io->h || !io->o || !io->y)
+    return MOE_ERR_INVALID;
+  const size_t pws = permute_ws_bytes(sh->T, sh->E);
+  const size_t gws = fwd8_ws_bytes(sh);
+  if (!ws || ws_bytes < pws + gws) return MOE_ERR_WORKSPACE;
+  if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
+    return st;
+  if ((st = moe_quantize_rows(io->x, MOE_BF16, sh->T, sh->d, io->xq, io->xs, stream))) return st;
+  if ((st = moe_permute_e4m3(sh, io->xq, io->xs, io->topk_idx, 1, io->counts, io->offsets,
+                             io->row_of, io->token_of, io->xpq, io->xps, ws, pws, stream)))
+    return st;
+  if ((st = moe_grouped_gemm_fwd_e4m3(sh, io->offsets, io->xpq, io->xps, io->wq, io->ab, io->h,
+                                      io->o, (char*)ws + pws, gws, stream)))
+    return st;
+  return moe_unpermute(sh, io->o, io->row_of, io->topk_prob, nullptr, io->y, stream);
+}
+
+int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!io || !io->dY || !io->x || !weights_ok(io->wq) || !io->topk_prob || !io->offsets ||
+      !io->row_of || !io->token_of || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp ||
+      !io->dX || !io->dW1 || !io->dW3 || !io->dW2)
+    return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < bwd8_ws_bytes(sh)) return MOE_ERR_WORKSPACE;
+  if ((st = moe_permute(sh, io->dY, nullptr, io->topk_prob, 0, nullptr, nullptr, io->row_of,
+                        nullptr, io->dO, nullptr, 0, stream)))
+    return st;
+  if ((st = moe_grouped_gemm_bwd_e4m3(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
+                                      io->wq, io->dab, io->dXp, io->dW1, io->dW3, io->dW2, ws,
+                                      ws_bytes, stream)))
+    return st;
+  return moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream);
+}
+
+}  // namespace

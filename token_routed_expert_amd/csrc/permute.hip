@@ -210,6 +210,26 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restr
   }
 }
 
+// e4m3 dispatch: one block per token; C = 16-byte chunks of codes per row,
+// KB = scales per row (one per 128 codes).  Codes and scales are bit copies.
+__global__ __launch_bounds__(256) void scatter_e4m3_kernel(const u32x4_t* __restrict__ codes,
+                                                           const float* __restrict__ scales,
+                                                           const int32_t* __restrict__ row_of,
+                                                           int k, int C, int KB,
+                                                           u32x4_t* __restrict__ dst_codes,
+                                                           float* __restrict__ dst_scales) {
+  const int t = blockIdx.x;
+  const int32_t* rows = row_of + (size_t)t * k;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    const u32x4_t v = __builtin_nontemporal_load(&codes[(size_t)t * C + c]);
+    for (int j = 0; j < k; ++j) __builtin_nontemporal_store(v, &dst_codes[(size_t)rows[j] * C + c]);
+  }
+  for (int c = threadIdx.x; c < KB; c += blockDim.x) {
+    const float v = scales[(size_t)t * KB + c];
+    for (int j = 0; j < k; ++j) dst_scales[(size_t)rows[j] * KB + c] = v;
+  }
+}
+
 int block_for_chunks(int C) {
   int b = ((C + 63) / 64) * 64;
   return b > 256 ? 256 : b;
@@ -280,6 +300,15 @@ int unpermute_launch(const void* src, const int32_t* row_of, const float* prob, 
                      int T, int k, int d, int elem_bytes, void* dst, hipStream_t s) {
   if (elem_bytes == 4) return gather_typed<float>(src, row_of, prob, add, T, k, d, dst, s);
   return gather_typed<bf16_t>(src, row_of, prob, add, T, k, d, dst, s);
+}
+
+int permute_e4m3_launch(const uint8_t* codes, const float* scales, const int32_t* row_of, int T,
+                        int k, int d, uint8_t* dst_codes, float* dst_scales, hipStream_t s) {
+  const int C = d / 16, KB = d / 128;
+  scatter_e4m3_kernel<<<T, block_for_chunks(C), 0, s>>>((const u32x4_t*)codes, scales, row_of, k,
+                                                         C, KB, (u32x4_t*)dst_codes, dst_scales);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 }  // namespace tre

@@ -1,0 +1,311 @@
+// e4m3 block quantisers: OCP E4M3FN codes with one fp32 scale per block.
+//
+// The pages run the expert GEMMs in FP8 with a blockwise recipe while the
+// router stays in high precision, and quantise weights straight from the
+// fp32 masters (German technical summary of "Scalable Training of
+// Mixture-of-Experts Models with Megatron Core", section 2 E; French summary,
+// section 2 E).  They give no formula; the one used here, for a block B of
+// values v:
+//   amax = max |v| over B;  scale = 1 if amax == 0, else fp32(amax / 448);
+//   code(v) = E4M3FN(fp32(v / scale)), round to nearest even, |x| >= 448
+//   saturates to 448, subnormals kept, sign kept (-0 -> 0x80); an all-zero
+//   block gets code +0 everywhere.
+// Both divisions are IEEE fp32 divisions, so codes and scales are one
+// well-defined function of the stored input values.
+//
+// Three block shapes, one kernel each:
+//  * rows (1 x 128 along a row): activation operands of the forward and
+//    data-gradient GEMMs, whose contraction runs along the row;
+//  * tiles (128 x 128): expert weights, from fp32 masters; the kernel also
+//    writes the transposed codes, so that every GEMM can read its weight
+//    operand with the contraction axis contiguous;
+//  * token blocks (128 consecutive rows of one expert, per column): operands
+//    of the weight-gradient GEMMs, whose contraction runs over the expert's
+//    rows; written transposed (column-major over a padded row axis in which
+//    every expert starts at a multiple of 128 and padding codes are 0).
+#include "common.h"
+#include "internal.h"
+
+namespace tre {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+// E4M3FN code of a finite fp32 value, from the format: sign bit, 4 exponent
+// bits with bias 7, 3 mantissa bits; normals from 2^-6 to 448, subnormals
+// m * 2^-9.  Round to nearest, ties to even; |v| >= 448 gives 448 (0x7e).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t mag;
+  if (a >= 0x43e00000u) {          // |v| >= 448
+    mag = 0x7eu;
+  } else if (a >= 0x3c800000u) {  // 2^-6 <= |v| < 448: keep 3 mantissa bits
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // ties to even at bit 20
+    mag = (r >> 20) - (120u << 3);                       // exponent bias 127 -> 7
+  } else {                         // below the normal range: multiples of 2^-9
+    mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);  // exact scaling, then RNE
+  }
+  return sign | mag;
+}
+
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+}
+
+// Code of v in a block with scale `scale` (zero_block: the block's amax is 0).
+__device__ __forceinline__ uint32_t quant1(float v, float scale, bool zero_block) {
+  return zero_block ? 0u : e4m3_code(v / scale);
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  const u32x4_t w = *(const u32x4_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const f32x4_t a = *(const f32x4_t*)p, b = *(const f32x4_t*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+// ---------------------------------------------------------------- rows
+// 16 lanes per 128-value block (8 values each); 16 blocks per 256 threads.
+// nblk = rows * cols / 128; block g covers values [128 g, 128 g + 128) of the
+// row-major matrix, and its scale is scales[g] (= [row][col / 128]).
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ src, int64_t nblk,
+                                                         uint8_t* __restrict__ codes,
+                                                         float* __restrict__ scales) {
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (g >= nblk) return;  // whole 16-lane groups leave together
+  float v[8];
+  load8<T>(src + g * 128 + sub * 8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+  const float sc = block_scale(m);
+  const bool z = m == 0.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= quant1(v[i], sc, z) << (8 * i);
+    hi |= quant1(v[4 + i], sc, z) << (8 * i);
+  }
+  *(uint2*)(codes + g * 128 + sub * 8) = make_uint2(lo, hi);
+  if (sub == 0) scales[g] = sc;
+}
+
+// ---------------------------------------------------------------- tiles
+// One block per 128 x 128 tile of matrix e (grid: C/128, R/128, E).
+// codes [E][R][C], codes_t [E][C][R] (may be NULL), scales [E][R/128][C/128].
+__global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restrict__ W, int R, int C,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ codes_t,
+                                                          float* __restrict__ scales) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row], padded rows
+  const int cb = blockIdx.x, rb = blockIdx.y, e = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const size_t mat = (size_t)e * R * C;
+  const float* Wt = W + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
+  const int col = (tid & 31) * 4;
+  f32x4_t v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (tid >> 5);
+    v[it] = *(const f32x4_t*)(Wt + (size_t)row * C + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = fmaxf(m, fabsf(v[it][q]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = block_scale(m);
+  const bool z = m == 0.0f;
+  uint8_t* Ct = codes + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (tid >> 5);
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c = quant1(v[it][q], sc, z);
+      w |= c << (8 * q);
+      tt[col + q][row] = (uint8_t)c;
+    }
+    *(uint32_t*)(Ct + (size_t)row * C + col) = w;
+  }
+  if (tid == 0) scales[((size_t)e * (R / 128) + rb) * (C / 128) + cb] = sc;
+  if (codes_t == nullptr) return;
+  __syncthreads();
+  // transposed tile: row c of codes_t holds column c of the tile (128 bytes)
+  uint8_t* Tt = codes_t + mat + (size_t)cb * 128 * R + (size_t)rb * 128;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int id = pass * 256 + tid;
+    const int c = id >> 3, r16 = (id & 7) * 16;
+    *(u32x4_t*)(Tt + (size_t)c * R + r16) = *(const u32x4_t*)&tt[c][r16];
+  }
+}
+
+// ---------------------------------------------------------------- token blocks
+// blk[e] = sum_{e' < e} ceil(m_e' / 128), blk[E] = number of blocks.
+__global__ __launch_bounds__(256) void tokblk_table_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int32_t* __restrict__ blk) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int c = 0;
+  if (tid < E) c = (offsets[tid + 1] - offsets[tid] + 127) / 128;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  if (tid < E) blk[tid] = before + incl - c;
+  if (tid == E - 1) blk[E] = before + incl;
+}
+
+// One block per (token block b, 128 columns cb): rows r0 .. r0 + nr - 1 of the
+// expert that owns block b (source row src_row[r] if src_row is given, else
+// r), columns cb*128 .. +127 of a bf16 [.][C] matrix.  Writes
+//   codes_t[c][128 b + i] for i < 128 (0 past the expert's rows), row length ldt;
+//   scales[b][c].
+// Blocks with b >= blk[E] leave at once.
+__global__ __launch_bounds__(256) void quant_tokblk_kernel(
+    const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
+    int64_t ldt, uint8_t* __restrict__ codes_t, float* __restrict__ scales) {
+  __shared__ float red[16][128];
+  __shared__ float sc[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row]
+  const int b = blockIdx.x, cb = blockIdx.y, tid = threadIdx.x;
+  if (b >= blk[E]) return;
+  // owner expert: the last e with blk[e] <= b (binary search, same in every lane)
+  int lo = 0, hi = E;  // invariant blk[lo] <= b < blk[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (blk[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (b - blk[e]) * 128;
+  const int nr = min(128, offsets[e + 1] - r0);
+  const int cg = (tid & 15) * 8;  // 8 columns of this thread
+  const int rg = tid >> 4;        // rows rg, rg + 16, ..., rg + 112
+  float v[8][8];
+  float m[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m[q] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rg + 16 * i;
+    if (r < nr) {
+      const int s = src_row ? src_row[r0 + r] : r0 + r;
+      load8<bf16_t>(src + (size_t)s * C + (size_t)cb * 128 + cg, v[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[i][q] = 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], fabsf(v[i][q]));
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[rg][cg + q] = m[q];
+  __syncthreads();
+  if (tid < 128) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, red[i][tid]);
+    sc[tid] = a;  // amax for now
+    scales[(size_t)b * C + (size_t)cb * 128 + tid] = block_scale(a);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float a = sc[cg + q];
+    const float s = block_scale(a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = rg + 16 * i;
+      tt[cg + q][r] = (uint8_t)quant1(v[i][q], s, a == 0.0f || r >= nr);
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = codes_t + (size_t)cb * 128 * ldt + (size_t)b * 128;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int id = pass * 256 + tid;
+    const int c = id >> 3, r16 = (id & 7) * 16;
+    *(u32x4_t*)(dst + (size_t)c * ldt + r16) = *(const u32x4_t*)&tt[c][r16];
+  }
+}
+
+}  // namespace
+
+int quant_rows_launch(const void* src, bool src_f32, int64_t rows, int64_t cols, uint8_t* codes,
+                      float* scales, hipStream_t s) {
+  const int64_t nblk = rows * (cols / 128);
+  if (nblk == 0) return MOE_OK;
+  const int64_t grid = (nblk + 15) / 16;
+  if (src_f32)
+    quant_rows_kernel<float><<<dim3((unsigned)grid), 256, 0, s>>>((const float*)src, nblk, codes,
+                                                                   scales);
+  else
+    quant_rows_kernel<bf16_t><<<dim3((unsigned)grid), 256, 0, s>>>((const bf16_t*)src, nblk,
+                                                                    codes, scales);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int quant_tiles_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                       uint8_t* codes_t, float* scales, hipStream_t s) {
+  if (E == 0) return MOE_OK;
+  quant_tiles_kernel<<<dim3((unsigned)(C / 128), (unsigned)(R / 128), (unsigned)E), 256, 0, s>>>(
+      W, (int)R, (int)C, codes, codes_t, scales);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int64_t tokblk_max_blocks(int64_t P, int64_t E) { return P / 128 + E; }
+
+int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t s) {
+  tokblk_table_kernel<<<1, 256, 0, s>>>(offsets, E, blk);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
+                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                        float* scales, hipStream_t s) {
+  const int64_t nb = tokblk_max_blocks(P, E);
+  if (nb == 0) return MOE_OK;
+  quant_tokblk_kernel<<<dim3((unsigned)nb, (unsigned)(C / 128)), 256, 0, s>>>(
+      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, nb * 128, codes_t, scales);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace tre

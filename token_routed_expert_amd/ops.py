@@ -43,7 +43,7 @@ def _check(status, call):
 
 
 def make_shape(T, d, E, k, f, f_shared=0, dtype="bf16") -> N.moe_shape:
-    code = {"f32": N.MOE_F32, "bf16": N.MOE_BF16}[dtype]
+    code = {"f32": N.MOE_F32, "bf16": N.MOE_BF16, "e4m3": N.MOE_E4M3}[dtype]
     return N.moe_shape(int(T), int(d), int(E), int(k), int(f), int(f_shared), code, 0)
 
 
@@ -89,11 +89,83 @@ def moe_grouped_gemm_bwd(sh, offsets, xp, ab, h, dO, W1, W3, W2, dab, dXp, dW1, 
                                         _stream(stream)), "moe_grouped_gemm_bwd")
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_quantize_rows(src, codes, scales, stream=None):
+    """1 x 128 e4m3 blocks along the rows of a bf16 or fp32 matrix."""
+    rows, cols = src.shape
+    code = {torch.bfloat16: N.MOE_BF16, torch.float32: N.MOE_F32}[src.dtype]
+    _check(N.lib().moe_quantize_rows(_ptr(src), code, rows, cols, _ptr(codes), _ptr(scales),
+                                     _stream(stream)), "moe_quantize_rows")
+
+
+def moe_quantize_weights(W, codes, codes_t, scales, stream=None):
+    """128 x 128 e4m3 tiles of fp32 matrices W [E][R][C]."""
+    E, R, Cc = W.shape
+    _check(N.lib().moe_quantize_weights(_ptr(W), E, R, Cc, _ptr(codes), _ptr(codes_t), _ptr(scales),
+                                        _stream(stream)), "moe_quantize_weights")
+
+
+def moe_token_block_capacity(P, E) -> int:
+    return int(N.lib().moe_token_block_capacity(int(P), int(E)))
+
+
+def moe_quantize_token_blocks(offsets, E, P, src, src_row, blk, codes_t, scales, stream=None):
+    """Per-expert 128-row e4m3 blocks of a bf16 [.][C] matrix, written transposed."""
+    Cc = src.shape[1]
+    _check(N.lib().moe_quantize_token_blocks(_ptr(offsets), int(E), int(P), _ptr(src),
+                                             _ptr(src_row), Cc, _ptr(blk), _ptr(codes_t),
+                                             _ptr(scales), _stream(stream)),
+           "moe_quantize_token_blocks")
+
+
+def moe_permute_e4m3(sh, codes, scales, topk_idx, build_map, counts, offsets, row_of, token_of,
+                     dst_codes, dst_scales, ws, stream=None):
+    _check(N.lib().moe_permute_e4m3(C.byref(sh), _ptr(codes), _ptr(scales), _ptr(topk_idx),
+                                    int(build_map), _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                    _ptr(token_of), _ptr(dst_codes), _ptr(dst_scales), _ptr(ws),
+                                    _nbytes(ws), _stream(stream)), "moe_permute_e4m3")
+
+
+class E4M3Weights:
+    """The moe_e4m3_weights struct over torch tensors (kept alive here)."""
+
+    NAMES = ("W1", "W3", "W2", "W1t", "W3t", "W2t", "W1s", "W3s", "W2s")
+
+    def __init__(self, tensors: dict):
+        self.tensors = {n: tensors[n] for n in self.NAMES}
+        self.struct = N.moe_e4m3_weights(*[_ptr(self.tensors[n]).value for n in self.NAMES])
+
+    def __getitem__(self, name):
+        return self.tensors[name]
+
+
+def moe_grouped_gemm_fwd_e4m3(sh, offsets, xpq, xps, wq: E4M3Weights, ab, h, o, ws, stream=None):
+    _check(N.lib().moe_grouped_gemm_fwd_e4m3(C.byref(sh), _ptr(offsets), _ptr(xpq), _ptr(xps),
+                                             C.byref(wq.struct), _ptr(ab), _ptr(h), _ptr(o),
+                                             _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_grouped_gemm_fwd_e4m3")
+
+
+def moe_grouped_gemm_bwd_e4m3(sh, offsets, token_of, x, ab, h, dO, wq: E4M3Weights, dab, dXp, dW1,
+                              dW3, dW2, ws, stream=None):
+    _check(N.lib().moe_grouped_gemm_bwd_e4m3(C.byref(sh), _ptr(offsets), _ptr(token_of), _ptr(x),
+                                             _ptr(ab), _ptr(h), _ptr(dO), C.byref(wq.struct),
+                                             _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3), _ptr(dW2),
+                                             _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_grouped_gemm_bwd_e4m3")
+
+
 def _io(buffers: dict) -> N.moe_layer_io:
     io = N.moe_layer_io()
     for name in N.IO_FIELDS:
         t = buffers.get(name)
         setattr(io, name, None if t is None else _ptr(t).value)
+    wq = buffers.get("wq")
+    if wq is not None:
+        io.wq = C.cast(C.pointer(wq.struct), C.c_void_p).value
     return io
 
 
