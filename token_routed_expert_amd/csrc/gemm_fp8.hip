@@ -65,9 +65,6 @@ __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& b, const i32x8_t& a) 
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-__device__ __forceinline__ f32x4_t buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 template <int OP>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
@@ -78,6 +75,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   constexpr bool WGRAD = !RAGGED;
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
+  // weight-gradient products: per stage the 256 A-row and 256 B-column scales
+  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][256];
   __shared__ int sched[NW + 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
@@ -167,9 +166,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     b_off[t] = (uint32_t)brow * b_ld + ch;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const uint32_t sc_base = (uint32_t)(uintptr_t)&sc_lds[0][0][0];
+  // weight gradients: the stage's scale rows ([NB][M] and [NB][N], 256
+  // consecutive floats each) go to LDS with one DMA instruction each
+  // (wavefronts 0 and 1); rows past the matrix read as zero.
+  rsrc_t sca_src, scb_src;
+  if constexpr (WGRAD) {
+    const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
+    sca_src = make_rsrc(args.a_s + (size_t)kb0 * Mt + ti.m0, (uint32_t)((K / BK) * Mt - ti.m0) * 4u);
+    scb_src = make_rsrc(args.b_s + (size_t)kb0 * N + ti.n0, (uint32_t)((K / BK) * N - ti.n0) * 4u);
+  }
   auto issue_stage = [&](int kt) __attribute__((always_inline)) {
     const uint32_t st = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
     const uint32_t ka = (uint32_t)kt * BK;
+    if constexpr (WGRAD) {
+      const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
+      const uint32_t sc = sc_base + (uint32_t)((kt & (NSTAGE - 1)) * 2048);
+      if (wid == 0) dma16(sca_src, (uint32_t)kt * (uint32_t)Mt * 4u + (uint32_t)lane * 16u, sc);
+      if (wid == 1) dma16(scb_src, (uint32_t)kt * (uint32_t)N * 4u + (uint32_t)lane * 16u, sc + 1024);
+    }
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int tt = wid * DMA_PER_WAVE + t;
@@ -195,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // ragged ops: a_s[(row0 + m) * K/128 + kt] (0 past the expert's rows);
   // wgrad: a_s[(kb0 + kt) * M_total + m0 + m].
   const int lm = lane & 15, lg = lane >> 4;
-  __amdgpu_buffer_rsrc_t sa_src, sb_src;
+  __amdgpu_buffer_rsrc_t sa_src;
   uint32_t sa_stride;  // bytes between the scales of consecutive stages
   uint32_t sa_off0;
   if constexpr (RAGGED) {
@@ -203,26 +218,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
                                                ti.rows * (K / BK) * 4, 0x00020000);
     sa_stride = 4;
     sa_off0 = (uint32_t)(wm * WM + lm) * (uint32_t)(K / BK) * 4u;
-  } else {
-    const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
-    sa_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_s + (size_t)kb0 * Mt), 0,
-                                               (K / BK) * Mt * 4, 0x00020000);
-    sa_stride = (uint32_t)Mt * 4u;
-    sa_off0 = (uint32_t)(ti.m0 + wm * WM + lm) * 4u;
-    sb_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_s + (size_t)kb0 * N), 0,
-                                               (K / BK) * N * 4, 0x00020000);
+  } else {  // from LDS (sc_lds), see issue_stage
+    sa_src = __builtin_amdgcn_make_buffer_rsrc((void*)args.a_s, 0, 0, 0x00020000);
+    sa_stride = 0;
+    sa_off0 = 0;
   }
-  const uint32_t sa_istep = RAGGED ? 16u * (uint32_t)(K / BK) * 4u : 64u;  // 16 rows
+  const uint32_t sa_istep = 16u * (uint32_t)(K / BK) * 4u;  // 16 rows
   auto load_sa = [&](int kt, float (&sa)[FM]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       sa[i] = buf_f32(sa_src, sa_off0 + (uint32_t)i * sa_istep + (uint32_t)kt * sa_stride);
-  };
-  // wgrad: sb[j] = scales of columns n0 + wn*WN + 16 j + 4 (lane >> 4) + 0..3
-  auto load_sb = [&](int kt, f32x4_t (&sb)[FN]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      sb[j] = buf_f32x4(sb_src, ((uint32_t)kt * N + ti.n0 + wn * WN + 16 * j + 4 * lg) * 4u);
   };
   // ragged ops: the weight block scale is one value per wavefront and stage
   // (fc1 forward: one for the W1 half, one for the W3 half).  nbw: the
@@ -251,11 +256,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  float sa[FM], sa_n[FM];
-  f32x4_t sb[FN], sb_n[FN];
+  float sa[FM], sa_n[FM];  // ragged ops: this stage's and the next stage's A scales
+  f32x4_t sb[FN];           // weight gradients: this stage's B scales (4 columns per fragment)
   if (KT > 0) {
-    load_sa(0, sa);
-    if constexpr (WGRAD) load_sb(0, sb);
+    if constexpr (RAGGED) load_sa(0, sa);
     issue_stage(0);
   }
   wait_vmcnt<0>();
@@ -270,9 +274,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
     if (kt + 1 < KT) {
-      load_sa(kt + 1, sa_n);
-      if constexpr (WGRAD) load_sb(kt + 1, sb_n);
+      if constexpr (RAGGED) load_sa(kt + 1, sa_n);
       issue_stage(kt + 1);
+    }
+    if constexpr (WGRAD) {
+      const float* sct = &sc_lds[kt & (NSTAGE - 1)][0][0];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = sct[wm * WM + 16 * i + lm];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = *(const f32x4_t*)&sct[256 + wn * WN + 16 * j + 4 * lg];
     }
     float wsc0 = 0.f, wsc1 = 0.f;
     if constexpr (RAGGED) {
@@ -284,30 +294,47 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       const int r = b_row(J.value);
       bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, 2 * lg, swz(r));
     });
-    static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = I.value;
-      const int r = wm * WM + 16 * i + lm;
-      const i32x8_t af = lds_frag(cur + r * BK, 2 * lg, swz(r));
+    // Software pipeline over the FM fragment rows: the FN MFMAs of row i go
+    // to their own product registers while the scale FMAs of row i-1 (whose
+    // MFMAs have completed meanwhile) and the read of row i+1's A fragment
+    // are issued; the sched barriers keep the compiler from pulling each
+    // product's FMAs up against its MFMA.
+    auto scale_row = [&](int i, const f32x4_t (&p)[FN]) __attribute__((always_inline)) {
       static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
         constexpr int j = J.value;
-        const f32x4_t p = mfma_fp8(bf[j], af);
         if constexpr (RAGGED) {
           const float s = sa[i] * (j < FN / 2 ? wsc0 : wsc1);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], s, acc[i][j][q]);
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], s, acc[i][j][q]);
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], sa[i] * sb[j][q], acc[i][j][q]);
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], sa[i] * sb[j][q], acc[i][j][q]);
         }
       });
+    };
+    f32x4_t pc[FN], pp[FN];
+    i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, 2 * lg, swz(wm * WM + lm));
+    static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = I.value;
+      i32x8_t af_next;
+      if constexpr (i + 1 < FM) {
+        const int r = wm * WM + 16 * (i + 1) + lm;
+        af_next = lds_frag(cur + r * BK, 2 * lg, swz(r));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, FN>([&](auto J) __attribute__((always_inline)) { pc[J.value] = mfma_fp8(bf[J.value], af); });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i > 0) scale_row(i - 1, pp);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, FN>([&](auto J) __attribute__((always_inline)) { pp[J.value] = pc[J.value]; });
+      if constexpr (i + 1 < FM) af = af_next;
     });
+    scale_row(FM - 1, pp);
     wait_vmcnt<0>();
     block_barrier();
+    if constexpr (RAGGED) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
-    if constexpr (WGRAD) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
+      for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
     }
   }
 
