@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
 }
 
 template <typename T, bool WEIGHTED, bool ADD>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ src,
+__global__ __launch_bounds__(512) void gather_rows_kernel(const u32x4_t* __restrict__ src,
                                                           const int32_t* __restrict__ row_of,
                                                           const float* __restrict__ prob,
                                                           const u32x4_t* __restrict__ add, int k,
@@ -230,16 +230,19 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(const u32x4_t* __rest
   }
 }
 
-int block_for_chunks(int C) {
+// Threads per block for a row of C 16-byte chunks: one wavefront per 64
+// chunks, at most `cap` (measured on the Qwen3-shaped rows: 512 for the
+// gathers of the combine, 256 for the scatter).
+int block_for_chunks(int C, int cap) {
   int b = ((C + 63) / 64) * 64;
-  return b > 256 ? 256 : b;
+  return b > cap ? cap : b;
 }
 
 template <typename T>
 int scatter_typed(const void* src, const int32_t* row_of, const float* scale, int T_, int k, int d,
                   void* dst, hipStream_t s) {
   const int C = d * (int)sizeof(T) / 16;
-  const int bs = block_for_chunks(C);
+  const int bs = block_for_chunks(C, 256);
   if (scale)
     scatter_rows_kernel<T, true><<<T_, bs, 0, s>>>((const u32x4_t*)src, row_of, scale, k, C,
                                                    (u32x4_t*)dst);
@@ -254,7 +257,7 @@ template <typename T>
 int gather_typed(const void* src, const int32_t* row_of, const float* prob, const void* add,
                  int T_, int k, int d, void* dst, hipStream_t s) {
   const int C = d * (int)sizeof(T) / 16;
-  const int bs = block_for_chunks(C);
+  const int bs = block_for_chunks(C, 512);
   const u32x4_t* S = (const u32x4_t*)src;
   const u32x4_t* A = (const u32x4_t*)add;
   u32x4_t* D = (u32x4_t*)dst;
@@ -305,7 +308,7 @@ int unpermute_launch(const void* src, const int32_t* row_of, const float* prob, 
 int permute_e4m3_launch(const uint8_t* codes, const float* scales, const int32_t* row_of, int T,
                         int k, int d, uint8_t* dst_codes, float* dst_scales, hipStream_t s) {
   const int C = d / 16, KB = d / 128;
-  scatter_e4m3_kernel<<<T, block_for_chunks(C), 0, s>>>((const u32x4_t*)codes, scales, row_of, k,
+  scatter_e4m3_kernel<<<T, block_for_chunks(C, 256), 0, s>>>((const u32x4_t*)codes, scales, row_of, k,
                                                          C, KB, (u32x4_t*)dst_codes, dst_scales);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
