@@ -299,12 +299,13 @@ def main():
     gemm_ms = t_gf + t_gb
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    move_bytes = (wl.T * wl.d + wl.P * wl.d) * s
+    move_bytes = (wl.T * wl.d + wl.P * wl.d) * s          # bf16 / fp32 rows in and out
+    perm_bytes = move_bytes
     if wl.dtype == "e4m3":
         # quantise x (read bf16, write codes + scales), then move codes + scales
         qx = wl.T * wl.d * (2 + 1) + wl.T * (wl.d // 128) * 4
-        move_bytes = qx + (wl.T + wl.P) * (wl.d + (wl.d // 128) * 4)
-    perm_gbs = (move_bytes + 16 * wl.P) / (t_perm * 1e-3) / 1e9
+        perm_bytes = qx + (wl.T + wl.P) * (wl.d + (wl.d // 128) * 4)
+    perm_gbs = (perm_bytes + 16 * wl.P) / (t_perm * 1e-3) / 1e9
     comb_gbs = (move_bytes + 8 * wl.P + (wl.T * wl.d * s if wl.f_shared else 0)) / (t_comb * 1e-3) / 1e9
     out = {
         "metric": METRIC,
