@@ -114,6 +114,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ s
 // ---------------------------------------------------------------- tiles
 // One block per 128 x 128 tile of matrix e (grid: C/128, R/128, E).
 // codes [E][R][C], codes_t [E][C][R] (may be NULL), scales [E][R/128][C/128].
+// Thread (rg, cl) = (tid / 32, tid % 32) holds rows 16 rg .. 16 rg + 15 and
+// columns 4 cl .. 4 cl + 3: float4 loads (a wavefront reads 2 rows of 512
+// bytes), 4-byte row-major code stores, and per column 16 consecutive row
+// codes -- one 16-byte LDS write into the transposed tile, which is then
+// stored row by row.
 __global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restrict__ W, int R, int C,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ codes_t,
@@ -122,17 +127,16 @@ __global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restric
   __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row], padded rows
   const int cb = blockIdx.x, rb = blockIdx.y, e = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int rg = tid >> 5, col = (tid & 31) * 4;
   const size_t mat = (size_t)e * R * C;
   const float* Wt = W + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
-  const int col = (tid & 31) * 4;
   f32x4_t v[16];
   float m = 0.0f;
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 8 + (tid >> 5);
-    v[it] = *(const f32x4_t*)(Wt + (size_t)row * C + col);
+  for (int i = 0; i < 16; ++i) {
+    v[i] = *(const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m = fmaxf(m, fabsf(v[it][q]));
+    for (int q = 0; q < 4; ++q) m = fmaxf(m, fabsf(v[i][q]));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -142,20 +146,23 @@ __global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restric
   const float sc = block_scale(m);
   const bool z = m == 0.0f;
   uint8_t* Ct = codes + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
+  uint32_t colw[4][4] = {};  // [column q][word w]: rows 16 rg + 4 w .. + 3 of column col + q
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 8 + (tid >> 5);
+  for (int i = 0; i < 16; ++i) {
     uint32_t w = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t c = quant1(v[it][q], sc, z);
+      const uint32_t c = quant1(v[i][q], sc, z);
       w |= c << (8 * q);
-      tt[col + q][row] = (uint8_t)c;
+      colw[q][i >> 2] |= c << (8 * (i & 3));
     }
-    *(uint32_t*)(Ct + (size_t)row * C + col) = w;
+    *(uint32_t*)(Ct + (size_t)(16 * rg + i) * C + col) = w;
   }
   if (tid == 0) scales[((size_t)e * (R / 128) + rb) * (C / 128) + cb] = sc;
   if (codes_t == nullptr) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(u32x4_t*)&tt[col + q][16 * rg] = u32x4_t{colw[q][0], colw[q][1], colw[q][2], colw[q][3]};
   __syncthreads();
   // transposed tile: row c of codes_t holds column c of the tile (128 bytes)
   uint8_t* Tt = codes_t + mat + (size_t)cb * 128 * R + (size_t)rb * 128;
