@@ -19,3 +19,4 @@ invariants, finite differences or an independent library derivation; none is
 from .moe import *  # noqa: F401,F403
 from .e4m3 import *  # noqa: F401,F403
 from .moe_e4m3 import *  # noqa: F401,F403
+from .router import *  # noqa: F401,F403
