@@ -74,7 +74,8 @@ typedef enum {
   MOE_WS_GEMM_FWD = 1,
   MOE_WS_GEMM_BWD = 2,
   MOE_WS_LAYER_FWD = 3,
-  MOE_WS_LAYER_BWD = 4
+  MOE_WS_LAYER_BWD = 4,
+  MOE_WS_AUX_LOSS = 5
 } moe_ws_kind;
 
 /*
@@ -194,6 +195,13 @@ typedef struct {
   float* xs;                              /* [T][d/128] scales of x */
   uint8_t* xpq;                           /* [P][d] permuted codes */
   float* xps;                             /* [P][d/128] permuted scales */
+  /* router gradient (optional; NULL = not computed): the forward writes the
+     load-balancing loss when aux_loss is set, the backward writes dprob and
+     dlogits when dlogits is set (dprob is then required) */
+  float* aux_loss;                        /* device scalar */
+  float* dprob;                           /* [T][k] */
+  float* dlogits;                         /* [T][E] */
+  float aux_alpha;                        /* coefficient alpha of the loss; 0 = none */
 } moe_layer_io;
 
 /*
@@ -202,7 +210,9 @@ typedef struct {
  * moe_route, moe_permute(build_map=1), moe_grouped_gemm_fwd and
  * moe_unpermute in sequence on one stream.  For MOE_E4M3: moe_route,
  * moe_quantize_rows of x into xq/xs, moe_permute_e4m3 into xpq/xps,
- * moe_grouped_gemm_fwd_e4m3, moe_unpermute.
+ * moe_grouped_gemm_fwd_e4m3, moe_unpermute.  With io->aux_loss set, also
+ * moe_aux_loss (alpha = io->aux_alpha) after the permutation; ws_bytes then
+ * needs MOE_WS_AUX_LOSS more bytes.
  */
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -211,8 +221,10 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
  * moe_layer_bwd -- backward of moe_layer_fwd for upstream gradient dY:
  * dO = p * dY permuted, expert backward, dX = un-permuted sum of dXp (+ the
  * shared expert's dXs), and all weight gradients.  No gradient flows to the
- * logits, which are an input of the layer.  For MOE_E4M3 the expert backward
- * is moe_grouped_gemm_bwd_e4m3.
+ * logits unless io->dlogits is set: then dO comes from moe_combine_bwd
+ * (writing io->dprob) and moe_route_bwd adds the router gradient, with the
+ * load-balancing term (coefficient io->aux_alpha, upstream gradient 1).  For
+ * MOE_E4M3 the expert backward is moe_grouped_gemm_bwd_e4m3.
  */
 int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -320,6 +332,51 @@ int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
                               const void* h, const void* dO, const moe_e4m3_weights* w, void* dab,
                               void* dXp, void* dW1, void* dW3, void* dW2, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * Router gradient and load-balancing loss
+ * ----------------------------------------
+ * The pages fuse routing, permutation and auxiliary-loss computations into
+ * few kernels (German technical summary, section 2 D "Kernel Fusion";
+ * Spanish summary, section 2.3 C) without stating a formula.  Readings:
+ *  - y[t] = sum_j p[t][j] o[row_of[t][j]] with p the softmax over the k
+ *    selected logits, so dp[t][j] = <dY[t], o[row_of[t][j]]> and
+ *    dlogits[t][topk_idx[t][j]] = p_j (dp_j - sum_i p_i dp_i), 0 for the
+ *    experts not selected;
+ *  - L = alpha E sum_e f_e P_e, f_e = counts[e] / (T k), P_e = mean over
+ *    tokens of the softmax over all E logits; counts are held constant:
+ *    dL/dlogits[t] = s[t] (g - <g, s[t]>), g_e = alpha E f_e / T.
+ */
+
+/*
+ * moe_aux_loss -- *loss (device fp32 scalar) = L above, from the router
+ * logits [T][E] and counts [E] (from moe_permute).  ws_bytes >=
+ * moe_workspace_bytes(sh with this T and E, MOE_WS_AUX_LOSS).  Deterministic.
+ */
+int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* counts,
+                 float alpha, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine_bwd -- the backward of the weighted combine with the
+ * probability gradient: dO[row_of[t][j]] = round(p[t][j] dY[t]) (exactly
+ * moe_permute's scaled form) and dprob [T][k] fp32 = <dY[t], o[row_of[t][j]]>
+ * with o [P][d] the expert outputs of the forward (sh->dtype; bf16 for
+ * e4m3 layers).  d * element bytes must be at most 32768.
+ */
+int moe_combine_bwd(const moe_shape* sh, const void* dY, const void* o, const int32_t* row_of,
+                    const float* topk_prob, void* dO, float* dprob, void* stream);
+
+/*
+ * moe_route_bwd -- dlogits [T][E] fp32: the top-k softmax Jacobian applied to
+ * dprob, plus aux_scale * dL/dlogits of the load-balancing loss (skipped when
+ * counts is NULL or alpha or aux_scale is 0).  logits, topk_idx, topk_prob
+ * as in moe_route.  The Jacobian term is evaluated as
+ * p_j sum_i p_i (dp_j - dp_i), which keeps its relative accuracy when one
+ * probability is close to 1.
+ */
+int moe_route_bwd(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* topk_idx,
+                  const float* topk_prob, const float* dprob, const int32_t* counts, float alpha,
+                  float aux_scale, float* dlogits, void* stream);
 
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);

@@ -30,11 +30,13 @@ def gpu_inputs(wl: Workload, seed: int = 0, **logit_overrides):
     return inp
 
 
-def run_layer(wl: Workload, inp: dict):
-    """moe_layer_fwd + moe_layer_bwd through the C ABI; returns every buffer."""
+def run_layer(wl: Workload, inp: dict, **kw):
+    """moe_layer_fwd + moe_layer_bwd through the C ABI; returns every buffer.
+    kw goes to layer_buffers (router_grad, aux_alpha)."""
     import token_routed_expert_amd as tre
     from token_routed_expert_amd.buffers import layer_buffers
-    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp)
+    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp,
+                                    **kw)
     tre.moe_layer_fwd(sh, b, wsf)
     tre.moe_layer_bwd(sh, b, wsb)
     torch.cuda.synchronize()

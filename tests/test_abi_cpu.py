@@ -122,3 +122,44 @@ def test_product_path_does_not_use_the_oracle():
             assert "oracle" not in open(path).read().replace("oracles", ""), path
     for path in glob.glob(os.path.join(ROOT, "oracle", "*.py")):
         assert "token_routed_expert_amd" not in open(path).read(), path
+
+
+def test_router_grad_validation():
+    lib = N.lib()
+    f = C.c_float
+    assert lib.moe_aux_loss(P, 4, 8, 2, P, f(0.01), P, P, 0, None) == N.MOE_ERR_WORKSPACE
+    assert lib.moe_aux_loss(P, 0, 8, 2, P, f(0.01), P, P, 1 << 20, None) == N.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(P, 4, 8, 9, P, f(0.01), P, P, 1 << 20, None) == N.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(None, 4, 8, 2, P, f(0.01), P, P, 1 << 20, None) == N.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(P, 4, 300, 2, P, f(0.01), P, P, 1 << 20, None) == \
+        N.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_bwd(P, 4, 8, 2, P, P, None, P, f(0.0), f(1.0), P, None) == \
+        N.MOE_ERR_INVALID
+    assert lib.moe_route_bwd(P, 4, 257, 2, P, P, P, P, f(0.0), f(1.0), P, None) == \
+        N.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_bwd(P, 4, 8, 9, P, P, P, P, f(0.0), f(1.0), P, None) == N.MOE_ERR_INVALID
+    sh = make_shape(4, 16392, 8, 2, 128, 0, "bf16")          # 32784-byte rows
+    assert lib.moe_combine_bwd(C.byref(sh), P, P, P, P, P, P, None) == N.MOE_ERR_UNSUPPORTED
+    sh = make_shape(4, 256, 8, 2, 128, 0, "bf16")
+    assert lib.moe_combine_bwd(C.byref(sh), P, P, P, P, P, None, None) == N.MOE_ERR_INVALID
+    assert moe_workspace_bytes(make_shape(8200, 4096, 128, 8, 1536), N.MOE_WS_AUX_LOSS) == \
+        -(-129 * 128 * 4 // 256) * 256
+
+
+def test_layer_router_grad_validation():
+    """The aux loss needs its workspace after the forward's, and dlogits needs
+    dprob: both are rejected before any launch."""
+    lib = N.lib()
+    for dtype in ("bf16", "e4m3"):
+        sh = make_shape(64, 256, 8, 2, 256, 0, dtype)
+        io = N.moe_layer_io()
+        for name in N.IO_FIELDS:
+            setattr(io, name, 16)
+        if dtype == "e4m3":
+            w = N.moe_e4m3_weights(*([16] * 9))         # dummy non-null pointers, never read
+            io.wq = C.cast(C.pointer(w), C.c_void_p).value
+        base = moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
+        assert base > 0
+        assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, base, None) == N.MOE_ERR_WORKSPACE
+        io.dprob = None
+        assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_INVALID

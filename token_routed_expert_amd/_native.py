@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtre_moe.
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 (MOE_WS_PERMUTE, MOE_WS_GEMM_FWD, MOE_WS_GEMM_BWD, MOE_WS_LAYER_FWD,
- MOE_WS_LAYER_BWD) = range(5)
+ MOE_WS_LAYER_BWD, MOE_WS_AUX_LOSS) = range(6)
 
 
 class moe_shape(C.Structure):
@@ -32,13 +32,16 @@ _IO_FIELDS = [
 
 # e4m3 layers: `wq` points to a moe_e4m3_weights struct; the rest are tensors
 _IO_FIELDS_E4M3 = ["wq", "xq", "xs", "xpq", "xps"]
+# router gradient (optional)
+_IO_FIELDS_ROUTER = ["aux_loss", "dprob", "dlogits"]
 
 
 class moe_layer_io(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3]
+    _fields_ = ([(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3 + _IO_FIELDS_ROUTER]
+                + [("aux_alpha", C.c_float)])
 
 
-IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:])
+IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:] + _IO_FIELDS_ROUTER)
 
 
 class moe_e4m3_weights(C.Structure):
@@ -68,6 +71,10 @@ _PROTOS = {
     "moe_grouped_gemm_bwd_e4m3": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P,
                                             C.POINTER(moe_e4m3_weights), _P, _P, _P, _P, _P, _P,
                                             C.c_size_t, _P]),
+    "moe_aux_loss": (C.c_int, [_P, _I64, _I64, _I64, _P, C.c_float, _P, _P, C.c_size_t, _P]),
+    "moe_combine_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_bwd": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, C.c_float, C.c_float, _P,
+                                _P]),
     "moe_workspace_bytes": (C.c_size_t, [_SH, C.c_int]),
     "moe_status_str": (C.c_char_p, [C.c_int]),
 }

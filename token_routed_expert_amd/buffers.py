@@ -7,10 +7,13 @@ from . import _native as N
 from .ops import E4M3Weights, make_shape, moe_quantize_weights, moe_workspace_bytes
 
 
-def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None):
+def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None,
+                  router_grad=False, aux_alpha=0.01):
     """Every buffer moe_layer_fwd/bwd touch, as a dict keyed like moe_layer_io.
 
     `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
+    router_grad: also the load-balancing loss (coefficient aux_alpha) and the
+    router gradient (aux_loss, dprob, dlogits).
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """
     sh = make_shape(T, d, E, k, f, f_shared, dtype)
@@ -37,8 +40,12 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     if f_shared:
         b.update(s_ab=z(T, 2 * f_shared), s_h=z(T, f_shared), ys=z(T, d), s_dab=z(T, 2 * f_shared),
                  dXs=z(T, d), dWs1=z(d, f_shared), dWs3=z(d, f_shared), dWs2=z(f_shared, d))
-    ws_f = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)), dtype=torch.uint8,
-                       device=device)
+    ws_f_bytes = moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
+    if router_grad:
+        b.update(aux_loss=z(1, dtype=torch.float32), dprob=z(T, k, dtype=torch.float32),
+                 dlogits=z(T, E, dtype=torch.float32), aux_alpha=float(aux_alpha))
+        ws_f_bytes += moe_workspace_bytes(sh, N.MOE_WS_AUX_LOSS)
+    ws_f = torch.empty(max(256, ws_f_bytes), dtype=torch.uint8, device=device)
     ws_b = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD)), dtype=torch.uint8,
                        device=device)
     return sh, b, ws_f, ws_b

@@ -23,6 +23,16 @@ int permute_rows_launch(const void* src, const int32_t* row_of, const float* row
 int unpermute_launch(const void* src, const int32_t* row_of, const float* prob, const void* add,
                      int T, int k, int d, int elem_bytes, void* dst, hipStream_t s);
 
+// router_grad.hip: router backward and load-balancing loss
+int combine_bwd_launch(const void* dY, const void* o, const int32_t* row_of, const float* prob,
+                       int T, int k, int d, int elem_bytes, void* dO, float* dprob, hipStream_t s);
+int route_bwd_launch(const float* logits, int T, int E, int k, const int32_t* idx,
+                     const float* prob, const float* dprob, const int32_t* counts, float alpha,
+                     float aux_scale, float* dlogits, hipStream_t s);
+size_t aux_ws_bytes(int64_t T, int64_t E);
+int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* counts, float alpha,
+                    float* loss, void* ws, hipStream_t s);
+
 // Grouped-GEMM problem: which of the six expert products to run.
 enum GemmOp {
   OP_FC1_FWD = 0,    // [a|b] = xp W{1,3}; saves ab, h = silu(a) b     (M ragged, K = d)

@@ -153,6 +153,10 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
                    void* stream);
 int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream);
+int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream);
+bool aux_ws_ok(const moe_shape* sh, const moe_layer_io* io, size_t ws_bytes);
+int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream);
 
 }  // namespace
 
@@ -173,6 +177,7 @@ size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
   if (check_shape(sh) != MOE_OK) return 0;
   if (sh->dtype == MOE_E4M3) {
     switch (kind) {
+      case MOE_WS_AUX_LOSS: return aux_ws_bytes(sh->T, sh->E);
       case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
       case MOE_WS_GEMM_FWD: return fwd8_ws_bytes(sh);
       case MOE_WS_GEMM_BWD: return bwd8_ws_bytes(sh);
@@ -182,6 +187,7 @@ size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
     return 0;
   }
   switch (kind) {
+    case MOE_WS_AUX_LOSS: return aux_ws_bytes(sh->T, sh->E);
     case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
     case MOE_WS_GEMM_FWD:
     case MOE_WS_GEMM_BWD: return 0;
@@ -261,6 +267,38 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   a.xp = xp; a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
   a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
   return bwd_sequence(sh, a, (hipStream_t)stream);
+}
+
+int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* counts,
+                 float alpha, float* loss, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !counts || !loss) return MOE_ERR_INVALID;
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T >= (1 << 30)) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < aux_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return aux_loss_launch(logits, (int)T, (int)E, (int)k, counts, alpha, loss, ws,
+                         (hipStream_t)stream);
+}
+
+int moe_combine_bwd(const moe_shape* sh, const void* dY, const void* o, const int32_t* row_of,
+                    const float* topk_prob, void* dO, float* dprob, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (!dY || !o || !row_of || !topk_prob || !dO || !dprob) return MOE_ERR_INVALID;
+  if (sh->d * elem_bytes(sh) > 32768) return MOE_ERR_UNSUPPORTED;
+  return combine_bwd_launch(dY, o, row_of, topk_prob, (int)sh->T, (int)sh->k, (int)sh->d,
+                            elem_bytes(sh), dO, dprob, (hipStream_t)stream);
+}
+
+int moe_route_bwd(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* topk_idx,
+                  const float* topk_prob, const float* dprob, const int32_t* counts, float alpha,
+                  float aux_scale, float* dlogits, void* stream) {
+  if (!logits || !topk_idx || !topk_prob || !dprob || !dlogits) return MOE_ERR_INVALID;
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T * k >= ((int64_t)1 << 31) || T * E >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  return route_bwd_launch(logits, (int)T, (int)E, (int)k, topk_idx, topk_prob, dprob, counts,
+                          alpha, aux_scale, dlogits, (hipStream_t)stream);
 }
 
 int moe_quantize_rows(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
@@ -406,7 +444,7 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
       (!io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h || !io->ys))
     return MOE_ERR_INVALID;
   const size_t pws = permute_ws_bytes(sh->T, sh->E);
-  if (!ws || ws_bytes < pws + 256) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < pws + 256 || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
 
   if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
@@ -414,6 +452,7 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
                         io->token_of, io->xp, ws, pws, stream)))
     return st;
+  if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
   if ((st = moe_grouped_gemm_fwd(sh, io->offsets, io->xp, io->W1, io->W3, io->W2, io->ab, io->h,
                                  io->o, nullptr, 0, stream)))
     return st;
@@ -448,10 +487,8 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if (!ws || ws_bytes < 256) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
 
-  // dO[row_of[t][j]] = p[t][j] * dY[t]
-  if ((st = moe_permute(sh, io->dY, nullptr, io->topk_prob, 0, nullptr, nullptr, io->row_of,
-                        nullptr, io->dO, nullptr, 0, stream)))
-    return st;
+  // dO[row_of[t][j]] = p[t][j] * dY[t] (+ dprob and the router gradient when asked for)
+  if ((st = layer_combine_bwd(sh, io, stream))) return st;
   if ((st = moe_grouped_gemm_bwd(sh, io->offsets, io->xp, io->ab, io->h, io->dO, io->W1, io->W3,
                                  io->W2, io->dab, io->dXp, io->dW1, io->dW3, io->dW2, nullptr, 0,
                                  stream)))
@@ -486,13 +523,14 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
     return MOE_ERR_INVALID;
   const size_t pws = permute_ws_bytes(sh->T, sh->E);
   const size_t gws = fwd8_ws_bytes(sh);
-  if (!ws || ws_bytes < pws + gws) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < pws + gws || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
   if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
     return st;
   if ((st = moe_quantize_rows(io->x, MOE_BF16, sh->T, sh->d, io->xq, io->xs, stream))) return st;
   if ((st = moe_permute_e4m3(sh, io->xq, io->xs, io->topk_idx, 1, io->counts, io->offsets,
                              io->row_of, io->token_of, io->xpq, io->xps, ws, pws, stream)))
     return st;
+  if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
   if ((st = moe_grouped_gemm_fwd_e4m3(sh, io->offsets, io->xpq, io->xps, io->wq, io->ab, io->h,
                                       io->o, (char*)ws + pws, gws, stream)))
     return st;
@@ -508,14 +546,47 @@ int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
       !io->dX || !io->dW1 || !io->dW3 || !io->dW2)
     return MOE_ERR_INVALID;
   if (!ws || ws_bytes < bwd8_ws_bytes(sh)) return MOE_ERR_WORKSPACE;
-  if ((st = moe_permute(sh, io->dY, nullptr, io->topk_prob, 0, nullptr, nullptr, io->row_of,
-                        nullptr, io->dO, nullptr, 0, stream)))
-    return st;
+  if ((st = layer_combine_bwd(sh, io, stream))) return st;
   if ((st = moe_grouped_gemm_bwd_e4m3(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
                                       io->wq, io->dab, io->dXp, io->dW1, io->dW3, io->dW2, ws,
                                       ws_bytes, stream)))
     return st;
   return moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream);
+}
+
+}  // namespace
+
+namespace {
+
+// the aux loss's workspace follows the layer's forward workspace
+bool aux_ws_ok(const moe_shape* sh, const moe_layer_io* io, size_t ws_bytes) {
+  return !io->aux_loss ||
+         ws_bytes >= moe_workspace_bytes(sh, MOE_WS_LAYER_FWD) + aux_ws_bytes(sh->T, sh->E);
+}
+
+// aux loss after the permutation's counts, when io->aux_loss is set
+int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!io->aux_loss) return MOE_OK;
+  const size_t base = moe_workspace_bytes(sh, MOE_WS_LAYER_FWD);
+  const size_t need = aux_ws_bytes(sh->T, sh->E);
+  if (ws_bytes < base + need) return MOE_ERR_WORKSPACE;
+  return moe_aux_loss(io->logits, sh->T, sh->E, sh->k, io->counts, io->aux_alpha, io->aux_loss,
+                      (char*)ws + base, need, stream);
+}
+
+// dO for the expert backward, plus dprob and dlogits when io->dlogits is set
+int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream) {
+  int st;
+  if (!io->dlogits)
+    return moe_permute(sh, io->dY, nullptr, io->topk_prob, 0, nullptr, nullptr, io->row_of,
+                       nullptr, io->dO, nullptr, 0, stream);
+  if (!io->dprob || !io->o || !io->logits || !io->topk_idx || !io->counts) return MOE_ERR_INVALID;
+  if ((st = moe_combine_bwd(sh, io->dY, io->o, io->row_of, io->topk_prob, io->dO, io->dprob,
+                            stream)))
+    return st;
+  return moe_route_bwd(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, io->dprob,
+                       io->counts, io->aux_alpha, 1.0f, io->dlogits, stream);
 }
 
 }  // namespace

@@ -1,0 +1,293 @@
+// Router backward and the load-balancing auxiliary loss.
+//
+// The pages fuse routing, permutation and auxiliary-loss computations into
+// few kernels ("Scalable Training of Mixture-of-Experts Models with Megatron
+// Core", gist.science German technical summary, section 2 D; Spanish summary,
+// section 2.3 C) but state no formula.  Readings:
+//  * the combine y[t] = sum_j p[t][j] o[row_of[t][j]] gives the probability
+//    gradient dp[t][j] = <dY[t], o[row_of[t][j]]>; p is the softmax over the k
+//    selected logits, so dlogits[t][idx[t][j]] = p_j (dp_j - sum_i p_i dp_i)
+//    and 0 for the other experts;
+//  * switch-style load balancing: L = alpha E sum_e f_e P_e with
+//    f_e = counts[e] / (T k) and P_e the mean over tokens of the softmax over
+//    all E logits; counts are held constant, so
+//    dL/dlogits[t] = s[t] (g - <g, s[t]>), g_e = alpha E f_e / T.
+// Every reduction runs in a fixed order: results are deterministic.
+#include "common.h"
+#include "internal.h"
+
+namespace tre {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void vec8(const u32x4_t& v, float* out);
+template <>
+__device__ __forceinline__ void vec8<float>(const u32x4_t& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+}
+template <>
+__device__ __forceinline__ void vec8<bf16_t>(const u32x4_t& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(v[i] << 16);
+    out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+template <typename T>
+__device__ __forceinline__ u32x4_t pack8(const float* in);
+template <>
+__device__ __forceinline__ u32x4_t pack8<float>(const float* in) {
+  return u32x4_t{__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                 __float_as_uint(in[3])};
+}
+template <>
+__device__ __forceinline__ u32x4_t pack8<bf16_t>(const float* in) {
+  return u32x4_t{pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]), pack_bf16x2(in[4], in[5]),
+                 pack_bf16x2(in[6], in[7])};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- combine backward
+// One block (256 threads) per token t; C 16-byte chunks per row, CPT chunks
+// per thread at most.  dO[row_of[t][j]] = round(p[t][j] * dY[t]) as the scaled
+// permutation does, and dprob[t][j] = <dY[t], o[row_of[t][j]]> in fp32: per
+// thread over its chunks in order, then a fixed-order block reduction.
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restrict__ dY,
+                                                          const u32x4_t* __restrict__ o,
+                                                          const int32_t* __restrict__ row_of,
+                                                          const float* __restrict__ prob, int k,
+                                                          int C, u32x4_t* __restrict__ dO,
+                                                          float* __restrict__ dprob) {
+  constexpr int N = 16 / sizeof(T);
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float g[CPT][N];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int c = tid + q * 256;
+    if (c < C) vec8<T>(dY[(size_t)t * C + c], g[q]);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int row = row_of[(size_t)t * k + j];
+    const float p = prob[(size_t)t * k + j];
+    float dot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * 256;
+      if (c < C) {
+        float ov[N], y[N];
+        vec8<T>(o[(size_t)row * C + c], ov);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          dot = fmaf(g[q][i], ov[i], dot);
+          y[i] = p * g[q][i];
+        }
+        dO[(size_t)row * C + c] = pack8<T>(y);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) red[w] = dot;
+    __syncthreads();
+    if (tid == 0) dprob[(size_t)t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- router backward
+// One wavefront per token, 4 tokens per block; lane l owns experts l, l+64,
+// l+128, l+192 (E <= 256).  g_e = gscale * counts[e] (gscale = aux_scale *
+// alpha * E / (T * T * k)); the auxiliary term is skipped when gscale == 0.
+__global__ __launch_bounds__(256) void route_bwd_kernel(
+    const float* __restrict__ logits, int T, int E, int k, const int32_t* __restrict__ idx,
+    const float* __restrict__ prob, const float* __restrict__ dprob,
+    const int32_t* __restrict__ counts, float gscale, float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wavefronts leave together
+  const float* L = logits + (size_t)t * E;
+  float dl[4] = {0.f, 0.f, 0.f, 0.f};
+  if (gscale != 0.0f) {
+    float v[4], m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = e < E ? L[e] : -INFINITY;
+      m = fmaxf(m, v[q]);
+    }
+    m = wave_max(m);
+    float sum = 0.f, s[4], gs = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      s[q] = e < E ? __expf(v[q] - m) : 0.f;
+      sum += s[q];
+    }
+    sum = wave_sum(sum);
+    float gv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      s[q] = s[q] / sum;
+      gv[q] = e < E ? gscale * (float)counts[e] : 0.f;
+      gs = fmaf(gv[q], s[q], gs);
+    }
+    gs = wave_sum(gs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dl[q] = s[q] * (gv[q] - gs);
+  }
+  // top-k softmax Jacobian p_j (dp_j - sum_i p_i dp_i), evaluated as
+  // p_j sum_i p_i (dp_j - dp_i) (equal, as the p sum to one): the plain form
+  // cancels catastrophically when one p_j is close to 1 and the others tiny
+  const float* pt = prob + (size_t)t * k;
+  const float* dpt = dprob + (size_t)t * k;
+  const int32_t* it = idx + (size_t)t * k;
+  for (int j = 0; j < k; ++j) {
+    const int e = it[j];
+    if ((e & 63) == lane) {
+      const float dpj = dpt[j];
+      float acc = 0.f;
+      for (int i = 0; i < k; ++i) acc = fmaf(pt[i], dpj - dpt[i], acc);
+      const float gj = pt[j] * acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e == lane + 64 * q) dl[q] += gj;
+    }
+  }
+  float* D = dlogits + (size_t)t * E;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) D[e] = dl[q];
+  }
+}
+
+// ---------------------------------------------------------------- auxiliary loss
+// Block b (4 wavefronts) sums the softmax of tokens [64 b, 64 b + 64) per
+// expert: wavefront w takes tokens 64 b + 16 w .. + 15 in order, the four
+// wavefront sums are added in order; partial[b][e].
+constexpr int AUX_TOK = 64;
+__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
+                                                          int E, float* __restrict__ partial) {
+  __shared__ float red[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < AUX_TOK / 4; ++i) {
+    const int t = blockIdx.x * AUX_TOK + w * (AUX_TOK / 4) + i;
+    if (t >= T) break;
+    const float* L = logits + (size_t)t * E;
+    float v[4], m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = e < E ? L[e] : -INFINITY;
+      m = fmaxf(m, v[q]);
+    }
+    m = wave_max(m);
+    float s[4], sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      s[q] = e < E ? __expf(v[q] - m) : 0.f;
+      sum += s[q];
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += s[q] / sum;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[w][lane + 64 * q] = acc[q];
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e < E) partial[(size_t)blockIdx.x * E + e] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+}
+
+// One block: column sums over the NB partials in block order, then
+// loss = scale * sum_e counts[e] * colsum[e], scale = alpha E / (T T k).
+__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ partial, int NB,
+                                                        int E, const int32_t* __restrict__ counts,
+                                                        float scale, float* __restrict__ loss) {
+  __shared__ float red[4];
+  const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+  float v = 0.f;
+  if (e < E) {
+    float col = 0.f;
+    for (int b = 0; b < NB; ++b) col += partial[(size_t)b * E + e];
+    v = (float)counts[e] * col;
+  }
+  v = wave_sum(v);
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  if (e == 0) *loss = scale * ((red[0] + red[1]) + (red[2] + red[3]));
+}
+
+template <typename T, int CPT>
+void combine_bwd_typed(const void* dY, const void* o, const int32_t* row_of, const float* prob,
+                       int T_, int k, int C, void* dO, float* dprob, hipStream_t s) {
+  combine_bwd_kernel<T, CPT><<<T_, 256, 0, s>>>((const u32x4_t*)dY, (const u32x4_t*)o, row_of,
+                                                 prob, k, C, (u32x4_t*)dO, dprob);
+}
+
+}  // namespace
+
+int combine_bwd_launch(const void* dY, const void* o, const int32_t* row_of, const float* prob,
+                       int T, int k, int d, int elem_bytes, void* dO, float* dprob,
+                       hipStream_t s) {
+  const int C = d * elem_bytes / 16;
+  const int cpt = (C + 255) / 256;
+  if (cpt > 8) return MOE_ERR_UNSUPPORTED;
+  if (elem_bytes == 4) {
+    if (cpt <= 2) combine_bwd_typed<float, 2>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+    else if (cpt <= 4) combine_bwd_typed<float, 4>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+    else combine_bwd_typed<float, 8>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+  } else {
+    if (cpt <= 2) combine_bwd_typed<bf16_t, 2>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+    else if (cpt <= 4) combine_bwd_typed<bf16_t, 4>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+    else combine_bwd_typed<bf16_t, 8>(dY, o, row_of, prob, T, k, C, dO, dprob, s);
+  }
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int route_bwd_launch(const float* logits, int T, int E, int k, const int32_t* idx,
+                     const float* prob, const float* dprob, const int32_t* counts, float alpha,
+                     float aux_scale, float* dlogits, hipStream_t s) {
+  const float gscale =
+      (counts && alpha != 0.0f && aux_scale != 0.0f)
+          ? (float)((double)aux_scale * alpha * E / ((double)T * T * k))
+          : 0.0f;
+  route_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, idx, prob, dprob, counts, gscale,
+                                              dlogits);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+size_t aux_ws_bytes(int64_t T, int64_t E) {
+  return align_up((size_t)((T + AUX_TOK - 1) / AUX_TOK) * (size_t)E * sizeof(float), 256);
+}
+
+int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* counts, float alpha,
+                    float* loss, void* ws, hipStream_t s) {
+  const int NB = (T + AUX_TOK - 1) / AUX_TOK;
+  float* partial = (float*)ws;
+  aux_partial_kernel<<<NB, 256, 0, s>>>(logits, T, E, partial);
+  TRE_LAUNCH_CHECK();
+  const float scale = (float)((double)alpha * E / ((double)T * T * k));
+  aux_final_kernel<<<1, 256, 0, s>>>(partial, NB, E, counts, scale, loss);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace tre

@@ -13,6 +13,9 @@ import torch
 
 from . import _native as N
 
+F32 = torch.float32
+I32 = torch.int32
+
 
 class MoeError(RuntimeError):
     def __init__(self, status: int, call: str):
@@ -21,11 +24,13 @@ class MoeError(RuntimeError):
         super().__init__(f"{call} returned {name} ({status})")
 
 
-def _ptr(t):
+def _ptr(t, dtype=None):
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"expected a torch.Tensor, got {type(t)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected a {dtype} tensor, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the MoE library must be contiguous")
     return C.c_void_p(t.data_ptr())
@@ -57,36 +62,37 @@ def moe_status_str(status: int) -> str:
 
 def moe_route(logits, k, topk_idx, topk_prob, stream=None):
     T, E = logits.shape
-    _check(N.lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_prob),
+    _check(N.lib().moe_route(_ptr(logits, F32), T, E, k, _ptr(topk_idx, I32), _ptr(topk_prob, F32),
                              _stream(stream)), "moe_route")
 
 
 def moe_permute(sh, src, topk_idx, row_scale, build_map, counts, offsets, row_of, token_of, dst,
                 ws, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(N.lib().moe_permute(C.byref(sh), _ptr(src), _ptr(topk_idx), _ptr(row_scale),
-                               int(build_map), _ptr(counts), _ptr(offsets), _ptr(row_of),
-                               _ptr(token_of), _ptr(dst), _ptr(ws), ws_bytes, _stream(stream)),
+    _check(N.lib().moe_permute(C.byref(sh), _ptr(src), _ptr(topk_idx, I32), _ptr(row_scale, F32),
+                               int(build_map), _ptr(counts, I32), _ptr(offsets, I32),
+                               _ptr(row_of, I32), _ptr(token_of, I32), _ptr(dst), _ptr(ws),
+                               ws_bytes, _stream(stream)),
            "moe_permute")
 
 
 def moe_unpermute(sh, src, row_of, topk_prob, add, dst, stream=None):
-    _check(N.lib().moe_unpermute(C.byref(sh), _ptr(src), _ptr(row_of), _ptr(topk_prob), _ptr(add),
-                                 _ptr(dst), _stream(stream)), "moe_unpermute")
+    _check(N.lib().moe_unpermute(C.byref(sh), _ptr(src), _ptr(row_of, I32), _ptr(topk_prob, F32),
+                                 _ptr(add), _ptr(dst), _stream(stream)), "moe_unpermute")
 
 
 def moe_grouped_gemm_fwd(sh, offsets, xp, W1, W3, W2, ab, h, o, stream=None):
-    _check(N.lib().moe_grouped_gemm_fwd(C.byref(sh), _ptr(offsets), _ptr(xp), _ptr(W1), _ptr(W3),
-                                        _ptr(W2), _ptr(ab), _ptr(h), _ptr(o), None, 0,
+    _check(N.lib().moe_grouped_gemm_fwd(C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(W1),
+                                        _ptr(W3), _ptr(W2), _ptr(ab), _ptr(h), _ptr(o), None, 0,
                                         _stream(stream)), "moe_grouped_gemm_fwd")
 
 
 def moe_grouped_gemm_bwd(sh, offsets, xp, ab, h, dO, W1, W3, W2, dab, dXp, dW1, dW3, dW2,
                          stream=None):
-    _check(N.lib().moe_grouped_gemm_bwd(C.byref(sh), _ptr(offsets), _ptr(xp), _ptr(ab), _ptr(h),
-                                        _ptr(dO), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dab),
-                                        _ptr(dXp), _ptr(dW1), _ptr(dW3), _ptr(dW2), None, 0,
-                                        _stream(stream)), "moe_grouped_gemm_bwd")
+    _check(N.lib().moe_grouped_gemm_bwd(C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(ab),
+                                        _ptr(h), _ptr(dO), _ptr(W1), _ptr(W3), _ptr(W2),
+                                        _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3), _ptr(dW2),
+                                        None, 0, _stream(stream)), "moe_grouped_gemm_bwd")
 
 
 def _nbytes(t):
@@ -115,17 +121,18 @@ def moe_token_block_capacity(P, E) -> int:
 def moe_quantize_token_blocks(offsets, E, P, src, src_row, blk, codes_t, scales, stream=None):
     """Per-expert 128-row e4m3 blocks of a bf16 [.][C] matrix, written transposed."""
     Cc = src.shape[1]
-    _check(N.lib().moe_quantize_token_blocks(_ptr(offsets), int(E), int(P), _ptr(src),
-                                             _ptr(src_row), Cc, _ptr(blk), _ptr(codes_t),
-                                             _ptr(scales), _stream(stream)),
+    _check(N.lib().moe_quantize_token_blocks(_ptr(offsets, I32), int(E), int(P), _ptr(src),
+                                             _ptr(src_row, I32), Cc, _ptr(blk, I32),
+                                             _ptr(codes_t), _ptr(scales, F32), _stream(stream)),
            "moe_quantize_token_blocks")
 
 
 def moe_permute_e4m3(sh, codes, scales, topk_idx, build_map, counts, offsets, row_of, token_of,
                      dst_codes, dst_scales, ws, stream=None):
-    _check(N.lib().moe_permute_e4m3(C.byref(sh), _ptr(codes), _ptr(scales), _ptr(topk_idx),
-                                    int(build_map), _ptr(counts), _ptr(offsets), _ptr(row_of),
-                                    _ptr(token_of), _ptr(dst_codes), _ptr(dst_scales), _ptr(ws),
+    _check(N.lib().moe_permute_e4m3(C.byref(sh), _ptr(codes), _ptr(scales, F32),
+                                    _ptr(topk_idx, I32), int(build_map), _ptr(counts, I32),
+                                    _ptr(offsets, I32), _ptr(row_of, I32), _ptr(token_of, I32),
+                                    _ptr(dst_codes), _ptr(dst_scales, F32), _ptr(ws),
                                     _nbytes(ws), _stream(stream)), "moe_permute_e4m3")
 
 
@@ -143,16 +150,17 @@ class E4M3Weights:
 
 
 def moe_grouped_gemm_fwd_e4m3(sh, offsets, xpq, xps, wq: E4M3Weights, ab, h, o, ws, stream=None):
-    _check(N.lib().moe_grouped_gemm_fwd_e4m3(C.byref(sh), _ptr(offsets), _ptr(xpq), _ptr(xps),
-                                             C.byref(wq.struct), _ptr(ab), _ptr(h), _ptr(o),
-                                             _ptr(ws), _nbytes(ws), _stream(stream)),
+    _check(N.lib().moe_grouped_gemm_fwd_e4m3(C.byref(sh), _ptr(offsets, I32), _ptr(xpq),
+                                             _ptr(xps, F32), C.byref(wq.struct), _ptr(ab), _ptr(h),
+                                             _ptr(o), _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_grouped_gemm_fwd_e4m3")
 
 
 def moe_grouped_gemm_bwd_e4m3(sh, offsets, token_of, x, ab, h, dO, wq: E4M3Weights, dab, dXp, dW1,
                               dW3, dW2, ws, stream=None):
-    _check(N.lib().moe_grouped_gemm_bwd_e4m3(C.byref(sh), _ptr(offsets), _ptr(token_of), _ptr(x),
-                                             _ptr(ab), _ptr(h), _ptr(dO), C.byref(wq.struct),
+    _check(N.lib().moe_grouped_gemm_bwd_e4m3(C.byref(sh), _ptr(offsets, I32),
+                                             _ptr(token_of, I32), _ptr(x), _ptr(ab), _ptr(h),
+                                             _ptr(dO), C.byref(wq.struct),
                                              _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3), _ptr(dW2),
                                              _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_grouped_gemm_bwd_e4m3")
@@ -166,7 +174,33 @@ def _io(buffers: dict) -> N.moe_layer_io:
     wq = buffers.get("wq")
     if wq is not None:
         io.wq = C.cast(C.pointer(wq.struct), C.c_void_p).value
+    io.aux_alpha = float(buffers.get("aux_alpha", 0.0))
     return io
+
+
+def moe_aux_loss(logits, k, counts, alpha, loss, ws, stream=None):
+    """Load-balancing loss (device scalar `loss`) from logits [T][E] and counts [E]."""
+    T, E = logits.shape
+    _check(N.lib().moe_aux_loss(_ptr(logits, F32), T, E, int(k), _ptr(counts, I32), float(alpha),
+                                _ptr(loss, F32), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_aux_loss")
+
+
+def moe_combine_bwd(sh, dY, o, row_of, topk_prob, dO, dprob, stream=None):
+    """dO = p * dY permuted, and dprob[t][j] = <dY[t], o[row_of[t][j]]>."""
+    _check(N.lib().moe_combine_bwd(C.byref(sh), _ptr(dY), _ptr(o), _ptr(row_of, I32),
+                                   _ptr(topk_prob, F32), _ptr(dO), _ptr(dprob, F32),
+                                   _stream(stream)), "moe_combine_bwd")
+
+
+def moe_route_bwd(logits, k, topk_idx, topk_prob, dprob, counts, alpha, aux_scale, dlogits,
+                  stream=None):
+    """Router gradient dlogits [T][E]: top-k softmax Jacobian + aux_scale * load-balancing term."""
+    T, E = logits.shape
+    _check(N.lib().moe_route_bwd(_ptr(logits, F32), T, E, int(k), _ptr(topk_idx, I32),
+                                 _ptr(topk_prob, F32), _ptr(dprob, F32), _ptr(counts, I32),
+                                 float(alpha), float(aux_scale), _ptr(dlogits, F32),
+                                 _stream(stream)), "moe_route_bwd")
 
 
 def moe_layer_fwd(sh, buffers: dict, ws, stream=None):
