@@ -6,6 +6,9 @@ of C-ABI calls on one stream: route -> permute -> grouped GEMM forward (fc1 +
 SwiGLU, fc2) [+ shared expert] -> weighted combine -> combine backward
 (scaled permute of dY) -> grouped GEMM backward (dgrad fc2 + SwiGLU backward,
 dgrad fc1, wgrad fc2, wgrad fc1) [+ shared expert] -> un-permute of dXp.
+With --router-grad the step also computes the load-balancing loss after the
+permutation, and the combine backward also writes the probability gradient,
+followed by the router backward (dlogits).
 Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the layer's algorithmic GEMM TFLOP/s over
@@ -77,14 +80,43 @@ def copy_calibration():
     del src, dst
 
 
-def build_step(wl, inp):
+# Event marks of one step, in order; segment i runs from mark i to mark i + 1.
+MARKS = ("start", "route", "permute", "aux_loss", "gemm_fwd", "combine", "combine_bwd",
+         "route_bwd", "gemm_bwd", "unpermute", "quantize_weights")
+
+
+def router_grad_calls(wl, sh, b, ws_aux):
+    """(aux loss after the permutation, combine backward with dprob, router
+    backward) as three callables, or no-ops when router_grad is off."""
+    import token_routed_expert_amd as tre
+
+    def aux():
+        tre.moe_aux_loss(b["logits"], wl.k, b["counts"], b["aux_alpha"], b["aux_loss"], ws_aux)
+
+    def comb_bwd():
+        tre.moe_combine_bwd(sh, b["dY"], b["o"], b["row_of"], b["topk_prob"], b["dO"], b["dprob"])
+
+    def route_bwd():
+        tre.moe_route_bwd(b["logits"], wl.k, b["topk_idx"], b["topk_prob"], b["dprob"], b["counts"],
+                          b["aux_alpha"], 1.0, b["dlogits"])
+
+    return aux, comb_bwd, route_bwd
+
+
+def build_step(wl, inp, router_grad=False):
     import torch
     import token_routed_expert_amd as tre
-    from token_routed_expert_amd.buffers import layer_buffers, requantize_weights
+    from token_routed_expert_amd import _native as N
+    from token_routed_expert_amd.buffers import layer_buffers
 
-    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp)
+    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp,
+                                    router_grad=router_grad)
+    rg = None
+    if router_grad:
+        base = tre.moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
+        rg = router_grad_calls(wl, sh, b, wsf[base:])
     if wl.dtype == "e4m3":
-        return build_step_e4m3(wl, inp, sh, b, wsf, wsb)
+        return build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg)
     shared = None
     if wl.f_shared:
         fs = wl.f_shared
@@ -93,38 +125,47 @@ def build_step(wl, inp):
         shared = (sh_s, off_s)
 
     def step(ev):
-        ev[0].record()
+        ev["start"].record()
         tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
-        ev[1].record()
+        ev["route"].record()
         tre.moe_permute(sh, b["x"], b["topk_idx"], None, 1, b["counts"], b["offsets"], b["row_of"],
                         b["token_of"], b["xp"], wsf)
-        ev[2].record()
+        ev["permute"].record()
+        if rg:
+            rg[0]()
+        ev["aux_loss"].record()
         tre.moe_grouped_gemm_fwd(sh, b["offsets"], b["xp"], b["W1"], b["W3"], b["W2"], b["ab"],
                                  b["h"], b["o"])
         if shared:
             tre.moe_grouped_gemm_fwd(shared[0], shared[1], b["x"], b["Ws1"], b["Ws3"], b["Ws2"],
                                      b["s_ab"], b["s_h"], b["ys"])
-        ev[3].record()
+        ev["gemm_fwd"].record()
         tre.moe_unpermute(sh, b["o"], b["row_of"], b["topk_prob"], b.get("ys"), b["y"])
-        ev[4].record()
-        tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
-                        b["dO"], None)
-        ev[5].record()
+        ev["combine"].record()
+        if rg:
+            rg[1]()
+        else:
+            tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
+                            b["dO"], None)
+        ev["combine_bwd"].record()
+        if rg:
+            rg[2]()
+        ev["route_bwd"].record()
         tre.moe_grouped_gemm_bwd(sh, b["offsets"], b["xp"], b["ab"], b["h"], b["dO"], b["W1"],
                                  b["W3"], b["W2"], b["dab"], b["dXp"], b["dW1"], b["dW3"], b["dW2"])
         if shared:
             tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
                                      b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
                                      b["dWs3"], b["dWs2"])
-        ev[6].record()
+        ev["gemm_bwd"].record()
         tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
-        ev[7].record()
-        ev[8].record()
+        ev["unpermute"].record()
+        ev["quantize_weights"].record()
 
     return step
 
 
-def build_step_e4m3(wl, inp, sh, b, wsf, wsb):
+def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
     """The e4m3 step: the expert weights are re-quantised from their fp32
     masters (as after an optimizer step), x is quantised in 1 x 128 blocks
     and its codes permuted; the GEMM calls quantise h, dO, [da|db] and the
@@ -140,29 +181,38 @@ def build_step_e4m3(wl, inp, sh, b, wsf, wsb):
     W = (inp["W1"], inp["W3"], inp["W2"])
 
     def step(ev):
-        ev[0].record()
+        ev["start"].record()
         tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
-        ev[1].record()
+        ev["route"].record()
         tre.moe_quantize_rows(b["x"], b["xq"], b["xs"])
         tre.moe_permute_e4m3(sh, b["xq"], b["xs"], b["topk_idx"], 1, b["counts"], b["offsets"],
                              b["row_of"], b["token_of"], b["xpq"], b["xps"], ws_perm)
-        ev[2].record()
+        ev["permute"].record()
+        if rg:
+            rg[0]()
+        ev["aux_loss"].record()
         tre.moe_grouped_gemm_fwd_e4m3(sh, b["offsets"], b["xpq"], b["xps"], wq, b["ab"], b["h"],
                                       b["o"], ws_gf)
-        ev[3].record()
+        ev["gemm_fwd"].record()
         tre.moe_unpermute(sh, b["o"], b["row_of"], b["topk_prob"], None, b["y"])
-        ev[4].record()
-        tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
-                        b["dO"], None)
-        ev[5].record()
+        ev["combine"].record()
+        if rg:
+            rg[1]()
+        else:
+            tre.moe_permute(sh, b["dY"], None, b["topk_prob"], 0, None, None, b["row_of"], None,
+                            b["dO"], None)
+        ev["combine_bwd"].record()
+        if rg:
+            rg[2]()
+        ev["route_bwd"].record()
         tre.moe_grouped_gemm_bwd_e4m3(sh, b["offsets"], b["token_of"], b["x"], b["ab"], b["h"],
                                       b["dO"], wq, b["dab"], b["dXp"], b["dW1"], b["dW3"],
                                       b["dW2"], wsb)
-        ev[6].record()
+        ev["gemm_bwd"].record()
         tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, None, b["dX"])
-        ev[7].record()
+        ev["unpermute"].record()
         requantize_weights(wq, *W)
-        ev[8].record()
+        ev["quantize_weights"].record()
 
     return step
 
@@ -253,6 +303,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router-grad", action="store_true",
+                    help="also the load-balancing loss, dprob and the router backward (dlogits)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run two 1 GiB device copies first (for hardware-counter runs)")
     args = ap.parse_args()
@@ -273,9 +325,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     inp = make_inputs(wl, seed=0, device="cuda")
-    step = build_step(wl, inp)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+    step = build_step(wl, inp, args.router_grad)
+
+    def marks():
+        return {m: torch.cuda.Event(enable_timing=True) for m in MARKS}
+
+    ev = [marks() for _ in range(args.steps)]
+    warm = marks()
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
@@ -290,10 +346,11 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
     log(f"bench: timed {args.steps} steps, {ms_step:.3f} ms/step")
 
-    def seg(a, b_):
-        return sum(e[a].elapsed_time(e[b_]) for e in ev) / args.steps
+    def seg(i):
+        return sum(e[MARKS[i]].elapsed_time(e[MARKS[i + 1]]) for e in ev) / args.steps
 
-    t_route, t_perm, t_gf, t_comb, t_permb, t_gb, t_unp, t_wq = (seg(i, i + 1) for i in range(8))
+    (t_route, t_perm, t_aux, t_gf, t_comb, t_permb, t_rbwd, t_gb, t_unp,
+     t_wq) = (seg(i) for i in range(len(MARKS) - 1))
     s = 4 if wl.dtype == "f32" else 2
     flops = wl.flops_fwd_bwd()
     gemm_ms = t_gf + t_gb
@@ -337,6 +394,16 @@ def main():
                 "permute_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
                 "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},
     }
+    if args.router_grad:
+        # combine backward with dprob: read dY once and the k rows of o, write dO
+        cb_bytes = (wl.T * wl.d + 2 * wl.P * wl.d) * s + 12 * wl.P
+        cb_gbs = cb_bytes / (t_permb * 1e-3) / 1e9
+        del out["breakdown_ms"]["combine_bwd_permute"]
+        out["config"]["router_grad"] = True
+        out["breakdown_ms"].update(aux_loss=round(t_aux, 4), combine_bwd=round(t_permb, 4),
+                                   route_bwd=round(t_rbwd, 4))
+        out["hbm"].update(combine_bwd_GBps=round(cb_gbs, 1),
+                          combine_bwd_frac=round(cb_gbs / HBM_PEAK_GBS, 4))
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

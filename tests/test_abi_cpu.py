@@ -143,7 +143,7 @@ def test_router_grad_validation():
     sh = make_shape(4, 256, 8, 2, 128, 0, "bf16")
     assert lib.moe_combine_bwd(C.byref(sh), P, P, P, P, P, None, None) == N.MOE_ERR_INVALID
     assert moe_workspace_bytes(make_shape(8200, 4096, 128, 8, 1536), N.MOE_WS_AUX_LOSS) == \
-        -(-129 * 128 * 4 // 256) * 256
+        -(-257 * 128 * 4 // 256) * 256
 
 
 def test_layer_router_grad_validation():

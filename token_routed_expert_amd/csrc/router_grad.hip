@@ -63,7 +63,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // One block (256 threads) per token t; C 16-byte chunks per row, CPT chunks
 // per thread at most.  dO[row_of[t][j]] = round(p[t][j] * dY[t]) as the scaled
 // permutation does, and dprob[t][j] = <dY[t], o[row_of[t][j]]> in fp32: per
-// thread over its chunks in order, then a fixed-order block reduction.
+// thread over its chunks in order, then a fixed-order block reduction.  The k
+// rows go in groups of KG so that KG * CPT row loads are in flight per thread
+// and the group's KG dot products share one block reduction.
+constexpr int KG = 8;
 template <typename T, int CPT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restrict__ dY,
                                                           const u32x4_t* __restrict__ o,
@@ -72,61 +75,83 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restr
                                                           int C, u32x4_t* __restrict__ dO,
                                                           float* __restrict__ dprob) {
   constexpr int N = 16 / sizeof(T);
-  __shared__ float red[4];
+  __shared__ float red[4][KG];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float g[CPT][N];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
     const int c = tid + q * 256;
-    if (c < C) vec8<T>(dY[(size_t)t * C + c], g[q]);
+    if (c < C) vec8<T>(__builtin_nontemporal_load(&dY[(size_t)t * C + c]), g[q]);
   }
-  for (int j = 0; j < k; ++j) {
-    const int row = row_of[(size_t)t * k + j];
-    const float p = prob[(size_t)t * k + j];
-    float dot = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += KG) {
+    const int nj = min(KG, k - j0);
+    float dot[KG];
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = tid + q * 256;
-      if (c < C) {
-        float ov[N], y[N];
-        vec8<T>(o[(size_t)row * C + c], ov);
+    for (int jj = 0; jj < KG; ++jj) {
+      dot[jj] = 0.0f;
+      if (jj < nj) {
+        const int row = row_of[(size_t)t * k + j0 + jj];
+        const float p = prob[(size_t)t * k + j0 + jj];
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-          dot = fmaf(g[q][i], ov[i], dot);
-          y[i] = p * g[q][i];
+        for (int q = 0; q < CPT; ++q) {
+          const int c = tid + q * 256;
+          if (c < C) {
+            float ov[N], y[N];
+            vec8<T>(__builtin_nontemporal_load(&o[(size_t)row * C + c]), ov);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+              dot[jj] = fmaf(g[q][i], ov[i], dot[jj]);
+              y[i] = p * g[q][i];
+            }
+            __builtin_nontemporal_store(pack8<T>(y), &dO[(size_t)row * C + c]);
+          }
         }
-        dO[(size_t)row * C + c] = pack8<T>(y);
       }
     }
-    dot = wave_sum(dot);
-    if (lane == 0) red[w] = dot;
+#pragma unroll
+    for (int jj = 0; jj < KG; ++jj) {
+      const float v = wave_sum(dot[jj]);
+      if (lane == 0) red[w][jj] = v;
+    }
     __syncthreads();
-    if (tid == 0) dprob[(size_t)t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid < nj) dprob[(size_t)t * k + j0 + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- router backward
 // One wavefront per token, 4 tokens per block; lane l owns experts l, l+64,
-// l+128, l+192 (E <= 256).  g_e = gscale * counts[e] (gscale = aux_scale *
-// alpha * E / (T * T * k)); the auxiliary term is skipped when gscale == 0.
+// l+128, l+192 (E <= 256) and the selections l, l+64, ... (k <= E).
+// g_e = gscale * counts[e] (gscale = aux_scale * alpha * E / (T * T * k)); the
+// auxiliary term is skipped when gscale == 0.  The Jacobian term of selection
+// j is computed by the lane that holds j and added into an LDS copy of the
+// token's row at expert idx[t][j] (the k experts of a token are distinct).
 __global__ __launch_bounds__(256) void route_bwd_kernel(
     const float* __restrict__ logits, int T, int E, int k, const int32_t* __restrict__ idx,
     const float* __restrict__ prob, const float* __restrict__ dprob,
     const int32_t* __restrict__ counts, float gscale, float* __restrict__ dlogits) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wavefronts leave together
+  __shared__ float rowbuf[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < T;  // no early return: the block synchronises below
   const float* L = logits + (size_t)t * E;
+  const float* pt = prob + (size_t)t * k;
+  const float* dpt = dprob + (size_t)t * k;
+  const int32_t* it = idx + (size_t)t * k;
+  float v[4], pj[4], dpj[4];
+  int ej[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = live && e < E ? L[e] : -INFINITY;
+    const bool sel = live && e < k;
+    pj[q] = sel ? pt[e] : 0.0f;
+    dpj[q] = sel ? dpt[e] : 0.0f;
+    ej[q] = sel ? it[e] : -1;
+  }
   float dl[4] = {0.f, 0.f, 0.f, 0.f};
   if (gscale != 0.0f) {
-    float v[4], m = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? L[e] : -INFINITY;
-      m = fmaxf(m, v[q]);
-    }
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
     m = wave_max(m);
     float sum = 0.f, s[4], gs = 0.f;
 #pragma unroll
@@ -141,71 +166,82 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
       s[q] = s[q] / sum;
-      gv[q] = e < E ? gscale * (float)counts[e] : 0.f;
+      gv[q] = live && e < E ? gscale * (float)counts[e] : 0.f;
       gs = fmaf(gv[q], s[q], gs);
     }
     gs = wave_sum(gs);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dl[q] = s[q] * (gv[q] - gs);
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rowbuf[w][lane + 64 * q] = dl[q];
   // top-k softmax Jacobian p_j (dp_j - sum_i p_i dp_i), evaluated as
   // p_j sum_i p_i (dp_j - dp_i) (equal, as the p sum to one): the plain form
-  // cancels catastrophically when one p_j is close to 1 and the others tiny
-  const float* pt = prob + (size_t)t * k;
-  const float* dpt = dprob + (size_t)t * k;
-  const int32_t* it = idx + (size_t)t * k;
-  for (int j = 0; j < k; ++j) {
-    const int e = it[j];
-    if ((e & 63) == lane) {
-      const float dpj = dpt[j];
-      float acc = 0.f;
-      for (int i = 0; i < k; ++i) acc = fmaf(pt[i], dpj - dpt[i], acc);
-      const float gj = pt[j] * acc;
+  // cancels catastrophically when one p_j is close to 1 and the others tiny.
+  // Selection i's p and dp are read from the lane that holds it, in order.
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < k; ++i) {
+    const int src = i & 63, q = i >> 6;
+    const float p_i = __shfl(q == 0 ? pj[0] : q == 1 ? pj[1] : q == 2 ? pj[2] : pj[3], src, 64);
+    const float dp_i = __shfl(q == 0 ? dpj[0] : q == 1 ? dpj[1] : q == 2 ? dpj[2] : dpj[3], src, 64);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (e == lane + 64 * q) dl[q] += gj;
-    }
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(p_i, dpj[r] - dp_i, acc[r]);
   }
-  float* D = dlogits + (size_t)t * E;
+  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    if (e < E) D[e] = dl[q];
+  for (int r = 0; r < 4; ++r)
+    if (ej[r] >= 0) rowbuf[w][ej[r]] += pj[r] * acc[r];
+  __syncthreads();
+  if (live) {
+    float* D = dlogits + (size_t)t * E;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) D[e] = rowbuf[w][e];
+    }
   }
 }
 
 // ---------------------------------------------------------------- auxiliary loss
-// Block b (4 wavefronts) sums the softmax of tokens [64 b, 64 b + 64) per
-// expert: wavefront w takes tokens 64 b + 16 w .. + 15 in order, the four
-// wavefront sums are added in order; partial[b][e].
-constexpr int AUX_TOK = 64;
+// Block b (4 wavefronts) sums the softmax of tokens [AUX_TOK b, AUX_TOK b +
+// AUX_TOK) per expert: wavefront w takes AUX_TOK / 4 consecutive tokens, 4 at a
+// time with their loads issued together, accumulating in token order; the four
+// wavefront sums are added in order into partial[b][e].
+constexpr int AUX_TOK = 32;
+constexpr int AUX_U = 4;
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
                                                           int E, float* __restrict__ partial) {
   __shared__ float red[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < AUX_TOK / 4; ++i) {
-    const int t = blockIdx.x * AUX_TOK + w * (AUX_TOK / 4) + i;
-    if (t >= T) break;
-    const float* L = logits + (size_t)t * E;
-    float v[4], m = -INFINITY;
+  const int t0 = blockIdx.x * AUX_TOK + w * (AUX_TOK / 4);
+  for (int i0 = 0; i0 < AUX_TOK / 4; i0 += AUX_U) {
+    float v[AUX_U][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? L[e] : -INFINITY;
-      m = fmaxf(m, v[q]);
+    for (int u = 0; u < AUX_U; ++u) {
+      const int t = t0 + i0 + u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        v[u][q] = t < T && e < E ? logits[(size_t)t * E + e] : -INFINITY;
+      }
     }
-    m = wave_max(m);
-    float s[4], sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      s[q] = e < E ? __expf(v[q] - m) : 0.f;
-      sum += s[q];
+    for (int u = 0; u < AUX_U; ++u) {
+      if (t0 + i0 + u >= T) break;  // uniform across the wavefront
+      float m = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
+      m = wave_max(m);
+      float s[4], sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        s[q] = e < E ? __expf(v[u][q] - m) : 0.f;
+        sum += s[q];
+      }
+      sum = wave_sum(sum);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += s[q] / sum;
     }
-    sum = wave_sum(sum);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] += s[q] / sum;
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) red[w][lane + 64 * q] = acc[q];
@@ -214,23 +250,40 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   if (e < E) partial[(size_t)blockIdx.x * E + e] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
 }
 
-// One block: column sums over the NB partials in block order, then
-// loss = scale * sum_e counts[e] * colsum[e], scale = alpha E / (T T k).
-__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ partial, int NB,
-                                                        int E, const int32_t* __restrict__ counts,
-                                                        float scale, float* __restrict__ loss) {
+// One block of 1024 threads: thread (r, e) with r = tid / 256 sums the partials
+// b = r, r + 4, r + 8, ... of expert e in order (8 loads issued together), the
+// four sums are added in order, then loss = scale * sum_e counts[e] colsum[e]
+// (scale = alpha E / (T T k)) by a fixed-order block reduction.
+constexpr int AUX_FIN_U = 8;
+__global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict__ partial, int NB,
+                                                         int E, const int32_t* __restrict__ counts,
+                                                         float scale, float* __restrict__ loss) {
+  __shared__ float cols[4][256];
   __shared__ float red[4];
-  const int e = threadIdx.x, lane = e & 63, w = e >> 6;
-  float v = 0.f;
+  const int e = threadIdx.x & 255, r = threadIdx.x >> 8;
+  float col = 0.f;
   if (e < E) {
-    float col = 0.f;
-    for (int b = 0; b < NB; ++b) col += partial[(size_t)b * E + e];
-    v = (float)counts[e] * col;
+    for (int b0 = r; b0 < NB; b0 += 4 * AUX_FIN_U) {
+      float pv[AUX_FIN_U];
+#pragma unroll
+      for (int u = 0; u < AUX_FIN_U; ++u) {
+        const int b = b0 + 4 * u;
+        pv[u] = b < NB ? partial[(size_t)b * E + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < AUX_FIN_U; ++u) col += pv[u];
+    }
   }
-  v = wave_sum(v);
-  if (lane == 0) red[w] = v;
+  cols[r][e] = col;
   __syncthreads();
-  if (e == 0) *loss = scale * ((red[0] + red[1]) + (red[2] + red[3]));
+  if (r == 0) {
+    const int lane = e & 63, w = e >> 6;
+    float v = e < E ? (float)counts[e] * ((cols[0][e] + cols[1][e]) + (cols[2][e] + cols[3][e])) : 0.f;
+    v = wave_sum(v);
+    if (lane == 0) red[w] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *loss = scale * ((red[0] + red[1]) + (red[2] + red[3]));
 }
 
 template <typename T, int CPT>
@@ -285,7 +338,7 @@ int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* cou
   aux_partial_kernel<<<NB, 256, 0, s>>>(logits, T, E, partial);
   TRE_LAUNCH_CHECK();
   const float scale = (float)((double)alpha * E / ((double)T * T * k));
-  aux_final_kernel<<<1, 256, 0, s>>>(partial, NB, E, counts, scale, loss);
+  aux_final_kernel<<<1, 1024, 0, s>>>(partial, NB, E, counts, scale, loss);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
