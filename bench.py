@@ -103,14 +103,14 @@ def router_grad_calls(wl, sh, b, ws_aux):
     return aux, comb_bwd, route_bwd
 
 
-def build_step(wl, inp, router_grad=False):
+def build_step(wl, inp, router_grad=False, memory_efficient=False):
     import torch
     import token_routed_expert_amd as tre
     from token_routed_expert_amd import _native as N
     from token_routed_expert_amd.buffers import layer_buffers
 
     sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp,
-                                    router_grad=router_grad)
+                                    router_grad=router_grad, memory_efficient=memory_efficient)
     rg = None
     if router_grad:
         base = tre.moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
@@ -123,6 +123,9 @@ def build_step(wl, inp, router_grad=False):
         sh_s = tre.make_shape(wl.T, wl.d, 1, 1, fs, 0, wl.dtype)
         off_s = torch.tensor([0, wl.T], dtype=torch.int32, device="cuda")
         shared = (sh_s, off_s)
+
+    if memory_efficient:
+        return build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg)
 
     def step(ev):
         ev["start"].record()
@@ -157,6 +160,53 @@ def build_step(wl, inp, router_grad=False):
             tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
                                      b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
                                      b["dWs3"], b["dWs2"])
+        ev["gemm_bwd"].record()
+        tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
+        ev["unpermute"].record()
+        ev["quantize_weights"].record()
+
+    return step
+
+
+def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg):
+    """The memory-efficient step: probabilities applied to h before W2, an
+    unweighted combine, the unscaled permutation of dY, and the row-scaled
+    expert backward (which also yields dprob when the router gradient is on)."""
+    import token_routed_expert_amd as tre
+
+    def step(ev):
+        ev["start"].record()
+        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        ev["route"].record()
+        tre.moe_permute(sh, b["x"], b["topk_idx"], None, 1, b["counts"], b["offsets"], b["row_of"],
+                        b["token_of"], b["xp"], wsf)
+        tre.moe_row_probs(sh, b["row_of"], b["topk_prob"], b["row_prob"])
+        ev["permute"].record()
+        if rg:
+            rg[0]()
+        ev["aux_loss"].record()
+        tre.moe_grouped_gemm_fwd_rowscaled(sh, b["offsets"], b["xp"], b["W1"], b["W3"], b["W2"],
+                                           b["row_prob"], b["ab"], b["h"], b["o"])
+        if shared:
+            tre.moe_grouped_gemm_fwd(shared[0], shared[1], b["x"], b["Ws1"], b["Ws3"], b["Ws2"],
+                                     b["s_ab"], b["s_h"], b["ys"])
+        ev["gemm_fwd"].record()
+        tre.moe_unpermute(sh, b["o"], b["row_of"], None, b.get("ys"), b["y"])
+        ev["combine"].record()
+        tre.moe_permute(sh, b["dY"], None, None, 0, None, None, b["row_of"], None, b["dO"], None)
+        ev["combine_bwd"].record()
+        ev["route_bwd"].record()
+        tre.moe_grouped_gemm_bwd_rowscaled(sh, b["offsets"], b["xp"], b["ab"], b["h"], b["dO"],
+                                           b["W1"], b["W3"], b["W2"], b["row_prob"], b["dab"],
+                                           b["dXp"], b["dW1"], b["dW3"], b["dW2"],
+                                           b["row_of"] if rg else None,
+                                           b["dprob"] if rg else None, wsb)
+        if shared:
+            tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
+                                     b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
+                                     b["dWs3"], b["dWs2"])
+        if rg:
+            rg[2]()
         ev["gemm_bwd"].record()
         tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
         ev["unpermute"].record()
@@ -305,6 +355,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--router-grad", action="store_true",
                     help="also the load-balancing loss, dprob and the router backward (dlogits)")
+    ap.add_argument("--memory-efficient", action="store_true",
+                    help="probabilities applied before W2 (bf16 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run two 1 GiB device copies first (for hardware-counter runs)")
     args = ap.parse_args()
@@ -325,7 +377,10 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     inp = make_inputs(wl, seed=0, device="cuda")
-    step = build_step(wl, inp, args.router_grad)
+    if args.memory_efficient and wl.dtype != "bf16":
+        log("bench.py: --memory-efficient needs a bf16 workload")
+        sys.exit(2)
+    step = build_step(wl, inp, args.router_grad, args.memory_efficient)
 
     def marks():
         return {m: torch.cuda.Event(enable_timing=True) for m in MARKS}
@@ -394,7 +449,14 @@ def main():
                 "permute_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
                 "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},
     }
-    if args.router_grad:
+    if args.memory_efficient:
+        out["config"]["memory_efficient"] = True
+        out["breakdown_ms"]["combine_bwd_permute"] = round(t_permb, 4)
+    if args.router_grad and args.memory_efficient:
+        # dprob comes out of the expert backward; the router backward is timed with it
+        out["config"]["router_grad"] = True
+        out["breakdown_ms"].update(aux_loss=round(t_aux, 4))
+    elif args.router_grad:
         # combine backward with dprob: read dY once and the k rows of o, write dO
         cb_bytes = (wl.T * wl.d + 2 * wl.P * wl.d) * s + 12 * wl.P
         cb_gbs = cb_bytes / (t_permb * 1e-3) / 1e9

@@ -75,7 +75,9 @@ typedef enum {
   MOE_WS_GEMM_BWD = 2,
   MOE_WS_LAYER_FWD = 3,
   MOE_WS_LAYER_BWD = 4,
-  MOE_WS_AUX_LOSS = 5
+  MOE_WS_AUX_LOSS = 5,
+  MOE_WS_GEMM_BWD_ROWSCALED = 6,
+  MOE_WS_LAYER_BWD_ROWSCALED = 7
 } moe_ws_kind;
 
 /*
@@ -202,6 +204,13 @@ typedef struct {
   float* dprob;                           /* [T][k] */
   float* dlogits;                         /* [T][E] */
   float aux_alpha;                        /* coefficient alpha of the loss; 0 = none */
+  /* memory-efficient permutation (bf16 layers): when memory_efficient != 0
+     the probabilities are applied before W2 (h and o hold p-scaled values),
+     the backward reads neither o nor a scaled dO, and row_prob [P] (written
+     by the forward, read by the backward) holds each permuted row's
+     probability */
+  float* row_prob;
+  int32_t memory_efficient;
 } moe_layer_io;
 
 /*
@@ -212,7 +221,9 @@ typedef struct {
  * moe_quantize_rows of x into xq/xs, moe_permute_e4m3 into xpq/xps,
  * moe_grouped_gemm_fwd_e4m3, moe_unpermute.  With io->aux_loss set, also
  * moe_aux_loss (alpha = io->aux_alpha) after the permutation; ws_bytes then
- * needs MOE_WS_AUX_LOSS more bytes.
+ * needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient (bf16):
+ * moe_row_probs into io->row_prob, moe_grouped_gemm_fwd_rowscaled and an
+ * unweighted moe_unpermute.
  */
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -224,7 +235,10 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
  * logits unless io->dlogits is set: then dO comes from moe_combine_bwd
  * (writing io->dprob) and moe_route_bwd adds the router gradient, with the
  * load-balancing term (coefficient io->aux_alpha, upstream gradient 1).  For
- * MOE_E4M3 the expert backward is moe_grouped_gemm_bwd_e4m3.
+ * MOE_E4M3 the expert backward is moe_grouped_gemm_bwd_e4m3.  With
+ * io->memory_efficient: dO = dY permuted without scaling, then
+ * moe_grouped_gemm_bwd_rowscaled (io->o is not read; dprob comes from its
+ * partials); ws_bytes >= moe_workspace_bytes(sh, MOE_WS_LAYER_BWD_ROWSCALED).
  */
 int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -377,6 +391,54 @@ int moe_combine_bwd(const moe_shape* sh, const void* dY, const void* o, const in
 int moe_route_bwd(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* topk_idx,
                   const float* topk_prob, const float* dprob, const int32_t* counts, float alpha,
                   float aux_scale, float* dlogits, void* stream);
+
+/*
+ * Memory-efficient permutation
+ * -----------------------------
+ * The pages reorder the routing weights algebraically so that the
+ * permutation keeps no redundant intermediates ("Scalable Training of
+ * Mixture-of-Experts Models with Megatron Core", German technical summary,
+ * section 2 B, memory; Spanish summary, section 2.3 A).  Reading: W2 is
+ * linear, so p (h W2) = (p h) W2; the probability is applied to h in the fc1
+ * epilogue, the combine is an unweighted sum, and the backward needs neither
+ * the expert outputs o nor a scaled dO: with dh' = dY[t] W2^T (unscaled
+ * rows), dh = p dh' and dp = <h, dh'>, taken in the fc2 dgrad epilogue.
+ * Results equal the plain layer's up to rounding.  bf16 only.
+ */
+
+/*
+ * moe_row_probs -- row_prob[row_of[t][j]] = topk_prob[t][j]: each permuted
+ * row's routing probability ([P] fp32).
+ */
+int moe_row_probs(const moe_shape* sh, const int32_t* row_of, const float* topk_prob,
+                  float* row_prob, void* stream);
+
+/*
+ * moe_grouped_gemm_fwd_rowscaled -- as moe_grouped_gemm_fwd, but h =
+ * row_prob[r] * silu(a) * b, so o = h W2 is already weighted (combine with
+ * moe_unpermute and topk_prob = NULL).  bf16 only (MOE_ERR_UNSUPPORTED else).
+ */
+int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                                   const void* W1, const void* W3, const void* W2,
+                                   const float* row_prob, void* ab, void* h, void* o,
+                                   void* stream);
+
+/*
+ * moe_grouped_gemm_bwd_rowscaled -- backward of the row-scaled forward: dO
+ * [P][d] is the UNSCALED permuted upstream gradient (moe_permute without
+ * row_scale), h the p-scaled h of the forward.  Writes dab, dXp, dW1, dW3,
+ * dW2 as moe_grouped_gemm_bwd, and, when dprob is not NULL, the probability
+ * gradient <silu(a_r) b_r, dO_r W2^T> of each permuted row r: dprob [P] in
+ * row order when row_of is NULL, else dprob [T][k] with
+ * dprob[t][j] = that of row row_of[t][j].  ws_bytes >= moe_workspace_bytes(sh,
+ * MOE_WS_GEMM_BWD_ROWSCALED) (per-row partials of the dot product).
+ */
+int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                                   const void* ab, const void* h, const void* dO, const void* W1,
+                                   const void* W3, const void* W2, const float* row_prob,
+                                   void* dab, void* dXp, void* dW1, void* dW3, void* dW2,
+                                   const int32_t* row_of, float* dprob, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);

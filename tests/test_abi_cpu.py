@@ -163,3 +163,39 @@ def test_layer_router_grad_validation():
         assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, base, None) == N.MOE_ERR_WORKSPACE
         io.dprob = None
         assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_INVALID
+
+
+def test_rowscaled_validation():
+    lib = N.lib()
+    for dtype, expect in (("f32", N.MOE_ERR_UNSUPPORTED), ("e4m3", N.MOE_ERR_UNSUPPORTED)):
+        sh = make_shape(64, 256, 8, 2, 256, 0, dtype)
+        assert lib.moe_grouped_gemm_fwd_rowscaled(C.byref(sh), *([P] * 10)) == expect
+        assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 17), 1 << 20, None) == expect
+    sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    args = [P] * 10
+    args[6] = None                                           # row_prob
+    assert lib.moe_grouped_gemm_fwd_rowscaled(C.byref(sh), *args) == N.MOE_ERR_INVALID
+    need = moe_workspace_bytes(sh, N.MOE_WS_GEMM_BWD_ROWSCALED)
+    assert need == -(-128 * 1 * 4 // 256) * 256
+    assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 17), need - 1, None) == \
+        N.MOE_ERR_WORKSPACE
+    assert lib.moe_row_probs(C.byref(sh), None, P, P, None) == N.MOE_ERR_INVALID
+    assert moe_workspace_bytes(make_shape(64, 256, 8, 2, 256, 0, "f32"),
+                               N.MOE_WS_LAYER_BWD_ROWSCALED) == 0
+
+
+def test_layer_memory_efficient_validation():
+    lib = N.lib()
+    io = N.moe_layer_io()
+    for name in N.IO_FIELDS:
+        setattr(io, name, 16)
+    io.memory_efficient = 1
+    sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")
+    need = moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD_ROWSCALED)
+    assert need == 256 + moe_workspace_bytes(sh, N.MOE_WS_GEMM_BWD_ROWSCALED)
+    assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, need - 1, None) == N.MOE_ERR_WORKSPACE
+    io.row_prob = None
+    assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_INVALID
+    assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_INVALID
+    sh = make_shape(64, 256, 8, 2, 256, 0, "f32")
+    assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED

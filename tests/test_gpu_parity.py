@@ -211,10 +211,17 @@ FULL = [WORKLOADS["mixtral_bf16"], WORKLOADS["qwen3_bf16"], WORKLOADS["deepseek_
 
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
 def test_layer_full_size_sampled(wl):
+    full_size_sampled(wl)
+
+
+def full_size_sampled(wl, **kw):
+    """The layer at full size (kw: layer_buffers options) against the oracle:
+    routing and permutation in full, y and dX on sampled tokens, dW on
+    sampled experts."""
     announce(f"{wl.name}: inputs")
     inp = make_inputs(wl, seed=0, device="cuda")
-    announce(f"{wl.name}: layer fwd+bwd")
-    b = run_layer(wl, inp)
+    announce(f"{wl.name}: layer fwd+bwd {kw}")
+    b = run_layer(wl, inp, **kw)
     announce(f"{wl.name}: oracle routing/permutation")
     L = inp["logits"].cpu().numpy()
     idx, p = oracle.route(L, wl.k)

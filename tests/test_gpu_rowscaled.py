@@ -1,0 +1,161 @@
+"""Memory-efficient permutation (probabilities applied before W2) on the GPU
+against the oracle, through the C ABI.
+
+The layer's results are the plain layer's (the oracle is unchanged: p (h W2)
+= (p h) W2 by linearity), within the bf16 tolerance of the other layer tests;
+h and o now hold p-scaled rows.  The probability gradient comes from the fc2
+data-gradient epilogue as <silu(a) b, dO W2^T> with a, b the stored bf16
+pre-activations, so it carries bf16 rounding of h:
+|dprob - exact| <= 2e-2 * sum_f |h_f (dY W2^T)_f|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_workloads import WORKLOADS, Workload, make_inputs, to_f64
+
+from gpu_common import TOL, announce, assert_close, host_inputs, need_gpu, oracle_layer, run_layer
+from test_gpu_parity import SMALL, check_routing_and_map, full_size_sampled
+
+pytestmark = pytest.mark.gpu
+BF16 = [w for w in SMALL if w.dtype == "bf16"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu(request):
+    need_gpu()
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+def permuted_probs(st):
+    """p of every permuted row (the oracle's map)."""
+    return st["p"].reshape(-1)[np.argsort(st["row_of"].reshape(-1))]
+
+
+def check_dprob(wl, st, h, dp):
+    """|dp - exact| <= 2e-2 * sum_f |h_f (dY W2^T)_f| for every (t, j)."""
+    dp_ref = oracle.combine_dprob(h["dY"], st["o"], st["row_of"])
+    toks = np.repeat(np.arange(wl.T), wl.k)
+    idx = st["idx"].reshape(-1)
+    dhp = np.empty((wl.T * wl.k, wl.f))
+    for e in range(wl.E):
+        sel = idx == e
+        if sel.any():
+            dhp[sel] = h["dY"][toks[sel]] @ h["W2"][e].T
+    hh = st["h"][st["row_of"].reshape(-1)]
+    mag = np.abs(hh * dhp).sum(1).reshape(wl.T, wl.k)
+    err = np.abs(dp - dp_ref)
+    assert (err <= 2e-2 * mag).all(), f"dprob: worst |err|/sum|terms| {(err / mag).max():.3e}"
+
+
+@pytest.mark.parametrize("wl", BF16, ids=lambda w: w.name)
+def test_layer_memory_efficient(wl):
+    inp = make_inputs(wl, seed=0, device="cuda")
+    b = run_layer(wl, inp, memory_efficient=True)
+    h = host_inputs(inp)
+    st, g = oracle_layer(wl, h)
+    check_routing_and_map(wl, b, inp, st)
+    tol = TOL[wl.dtype]
+    pr = permuted_probs(st)
+    assert np.abs(b["row_prob"].cpu().numpy() - pr).max() <= 1e-4 * pr.max()
+    assert_close("ab", to_f64(b["ab"]), np.concatenate([st["a"], st["b"]], 1), tol)
+    assert_close("p h", to_f64(b["h"]), pr[:, None] * st["h"], tol)
+    assert_close("p o", to_f64(b["o"]), pr[:, None] * st["o"], tol)
+    assert_close("y", to_f64(b["y"]), st["y"], tol)
+    assert_close("dXp", to_f64(b["dXp"]), g["dXp"], tol)
+    assert_close("dX", to_f64(b["dX"]), g["dX"], tol)
+    for n in ("dW1", "dW3", "dW2") + (("dWs1", "dWs3", "dWs2") if wl.f_shared else ()):
+        assert_close(n, to_f64(b[n]), g[n], tol)
+    for e in np.nonzero(st["counts"] == 0)[0]:
+        assert not b["dW1"][e].any() and not b["dW3"][e].any() and not b["dW2"][e].any()
+
+
+@pytest.mark.parametrize("wl", [Workload("me_rg_bf16", T=777, d=256, E=16, k=4, f=384),
+                                Workload("me_rg_skew_bf16", T=500, d=384, E=16, k=4, f=256,
+                                         skew=True)],
+                         ids=lambda w: w.name)
+def test_memory_efficient_router_grad(wl):
+    """dprob from the fc2 dgrad epilogue, dlogits and the loss; the backward
+    does not read o (poisoned between forward and backward)."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd.buffers import layer_buffers
+    inp = make_inputs(wl, seed=4, device="cuda")
+    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, 0, "bf16", "cuda", inp,
+                                    router_grad=True, aux_alpha=0.01, memory_efficient=True)
+    tre.moe_layer_fwd(sh, b, wsf)
+    b["o"].fill_(float("nan"))
+    tre.moe_layer_bwd(sh, b, wsb)
+    torch.cuda.synchronize()
+    h = host_inputs(inp)
+    st, g = oracle_layer(wl, h)
+    tol = TOL["bf16"]
+    for n in ("dX", "dW1", "dW3", "dW2"):
+        assert torch.isfinite(b[n]).all(), n
+        assert_close(n, to_f64(b[n]), g[n], tol)
+    dp = b["dprob"].cpu().numpy().astype(np.float64)
+    check_dprob(wl, st, h, dp)
+    idx = st["idx"]
+    ref = oracle.router_bwd(dp, st["p"], idx, wl.E) + oracle.aux_loss(h["logits"], st["counts"],
+                                                                      wl.k, 0.01)[1]
+    assert_close("dlogits", b["dlogits"].cpu().numpy().astype(np.float64), ref, 1e-4)
+    ref_loss = oracle.aux_loss(h["logits"], st["counts"], wl.k, 0.01)[0]
+    assert abs(float(b["aux_loss"].item()) - ref_loss) <= 5e-5 * ref_loss
+
+
+def test_memory_efficient_is_deterministic():
+    wl = Workload("me_det_bf16", T=900, d=256, E=16, k=4, f=256)
+    inp = make_inputs(wl, seed=2, device="cuda")
+    b1 = run_layer(wl, inp, memory_efficient=True, router_grad=True)
+    b2 = run_layer(wl, inp, memory_efficient=True, router_grad=True)
+    for n in ("y", "dX", "dW1", "dW3", "dW2", "h", "o", "dprob", "dlogits"):
+        assert torch.equal(b1[n], b2[n]), n
+
+
+def test_rowscaled_entry_points():
+    """moe_row_probs, the row-scaled GEMM forward and backward (dprob_rows)
+    called directly, against the plain entry points' results scaled by p."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    wl = Workload("me_ep_bf16", T=600, d=256, E=8, k=2, f=256)
+    inp = make_inputs(wl, seed=5, device="cuda")
+    b = run_layer(wl, inp)                      # plain layer: routing, map, xp, ab, h, o
+    sh = tre.make_shape(wl.T, wl.d, wl.E, wl.k, wl.f, 0, "bf16")
+    P = wl.P
+    rp = torch.empty(P, device="cuda")
+    tre.moe_row_probs(sh, b["row_of"], b["topk_prob"], rp)
+    h = host_inputs(inp)
+    st, g = oracle_layer(wl, h)
+    pr = permuted_probs(st)
+    assert np.abs(rp.cpu().numpy() - pr).max() <= 1e-4 * pr.max()
+    ab = torch.empty_like(b["ab"]); hs = torch.empty_like(b["h"]); os_ = torch.empty_like(b["o"])
+    tre.moe_grouped_gemm_fwd_rowscaled(sh, b["offsets"], b["xp"], inp["W1"], inp["W3"], inp["W2"],
+                                       rp, ab, hs, os_)
+    assert torch.equal(ab, b["ab"])             # the pre-activations are not scaled
+    assert_close("p h", to_f64(hs), pr[:, None] * st["h"], TOL["bf16"])
+    assert_close("p o", to_f64(os_), pr[:, None] * st["o"], TOL["bf16"])
+    dO = torch.empty_like(b["dO"])
+    tre.moe_permute(sh, inp["dY"], None, None, 0, None, None, b["row_of"], None, dO, None)
+    out = {n: torch.empty_like(b[n]) for n in ("dab", "dXp", "dW1", "dW3", "dW2")}
+    dpr = torch.empty(P, device="cuda")
+    ws = torch.empty(tre.moe_workspace_bytes(sh, N.MOE_WS_GEMM_BWD_ROWSCALED), dtype=torch.uint8,
+                     device="cuda")
+    tre.moe_grouped_gemm_bwd_rowscaled(sh, b["offsets"], b["xp"], ab, hs, dO, inp["W1"], inp["W3"],
+                                       inp["W2"], rp, out["dab"], out["dXp"], out["dW1"],
+                                       out["dW3"], out["dW2"], None, dpr, ws)
+    for n in ("dXp", "dW1", "dW3", "dW2"):
+        assert_close(n, to_f64(out[n]), g[n], TOL["bf16"])
+    check_dprob(wl, st, h, dpr.cpu().numpy().astype(np.float64)[st["row_of"]])
+    dtk = torch.empty(wl.T, wl.k, device="cuda")     # the [T][k] form through row_of
+    tre.moe_grouped_gemm_bwd_rowscaled(sh, b["offsets"], b["xp"], ab, hs, dO, inp["W1"], inp["W3"],
+                                       inp["W2"], rp, out["dab"], out["dXp"], out["dW1"],
+                                       out["dW3"], out["dW2"], b["row_of"], dtk, ws)
+    assert torch.equal(dtk, dpr[b["row_of"].long()])
+
+
+@pytest.mark.parametrize("wl", [WORKLOADS["qwen3_bf16"], WORKLOADS["deepseek_v3_bf16"]],
+                         ids=lambda w: w.name)
+def test_memory_efficient_full_size_sampled(wl):
+    full_size_sampled(wl, memory_efficient=True)

@@ -5,6 +5,7 @@ this package only marshals torch tensors into its calls.
 """
 from . import _native
 from .ops import (E4M3Weights, MoeError, make_shape, moe_aux_loss, moe_combine_bwd,
+                  moe_row_probs, moe_grouped_gemm_fwd_rowscaled, moe_grouped_gemm_bwd_rowscaled,
                   moe_grouped_gemm_bwd, moe_route_bwd,
                   moe_grouped_gemm_bwd_e4m3, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_e4m3,
                   moe_layer_bwd, moe_layer_fwd, moe_permute, moe_permute_e4m3,
@@ -16,4 +17,5 @@ __all__ = ["MoeError", "make_shape", "moe_route", "moe_permute", "moe_unpermute"
            "moe_workspace_bytes", "moe_status_str", "moe_quantize_rows", "moe_quantize_weights",
            "moe_token_block_capacity", "moe_quantize_token_blocks", "moe_permute_e4m3",
            "moe_grouped_gemm_fwd_e4m3", "moe_grouped_gemm_bwd_e4m3", "E4M3Weights", "moe_aux_loss",
-           "moe_combine_bwd", "moe_route_bwd", "_native"]
+           "moe_combine_bwd", "moe_route_bwd", "moe_row_probs", "moe_grouped_gemm_fwd_rowscaled",
+           "moe_grouped_gemm_bwd_rowscaled", "_native"]

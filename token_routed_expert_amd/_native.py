@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtre_moe.
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 (MOE_WS_PERMUTE, MOE_WS_GEMM_FWD, MOE_WS_GEMM_BWD, MOE_WS_LAYER_FWD,
- MOE_WS_LAYER_BWD, MOE_WS_AUX_LOSS) = range(6)
+ MOE_WS_LAYER_BWD, MOE_WS_AUX_LOSS, MOE_WS_GEMM_BWD_ROWSCALED,
+ MOE_WS_LAYER_BWD_ROWSCALED) = range(8)
 
 
 class moe_shape(C.Structure):
@@ -38,10 +39,11 @@ _IO_FIELDS_ROUTER = ["aux_loss", "dprob", "dlogits"]
 
 class moe_layer_io(C.Structure):
     _fields_ = ([(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3 + _IO_FIELDS_ROUTER]
-                + [("aux_alpha", C.c_float)])
+                + [("aux_alpha", C.c_float), ("row_prob", C.c_void_p),
+                   ("memory_efficient", C.c_int32)])
 
 
-IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:] + _IO_FIELDS_ROUTER)
+IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:] + _IO_FIELDS_ROUTER + ["row_prob"])
 
 
 class moe_e4m3_weights(C.Structure):
@@ -75,6 +77,9 @@ _PROTOS = {
     "moe_combine_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, C.c_float, C.c_float, _P,
                                 _P]),
+    "moe_row_probs": (C.c_int, [_SH, _P, _P, _P, _P]),
+    "moe_grouped_gemm_fwd_rowscaled": (C.c_int, [_SH] + [_P] * 10),
+    "moe_grouped_gemm_bwd_rowscaled": (C.c_int, [_SH] + [_P] * 17 + [C.c_size_t, _P]),
     "moe_workspace_bytes": (C.c_size_t, [_SH, C.c_int]),
     "moe_status_str": (C.c_char_p, [C.c_int]),
 }

@@ -8,12 +8,13 @@ from .ops import E4M3Weights, make_shape, moe_quantize_weights, moe_workspace_by
 
 
 def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None,
-                  router_grad=False, aux_alpha=0.01):
+                  router_grad=False, aux_alpha=0.01, memory_efficient=False):
     """Every buffer moe_layer_fwd/bwd touch, as a dict keyed like moe_layer_io.
 
     `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
     router_grad: also the load-balancing loss (coefficient aux_alpha) and the
     router gradient (aux_loss, dprob, dlogits).
+    memory_efficient: probabilities applied before W2 (bf16; row_prob [P]).
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """
     sh = make_shape(T, d, E, k, f, f_shared, dtype)
@@ -46,7 +47,11 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
                  dlogits=z(T, E, dtype=torch.float32), aux_alpha=float(aux_alpha))
         ws_f_bytes += moe_workspace_bytes(sh, N.MOE_WS_AUX_LOSS)
     ws_f = torch.empty(max(256, ws_f_bytes), dtype=torch.uint8, device=device)
-    ws_b = torch.empty(max(256, moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD)), dtype=torch.uint8,
+    bwd_kind = N.MOE_WS_LAYER_BWD
+    if memory_efficient:
+        b.update(row_prob=z(P, dtype=torch.float32), memory_efficient=True)
+        bwd_kind = N.MOE_WS_LAYER_BWD_ROWSCALED
+    ws_b = torch.empty(max(256, moe_workspace_bytes(sh, bwd_kind)), dtype=torch.uint8,
                        device=device)
     return sh, b, ws_f, ws_b
 

@@ -90,7 +90,7 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // NW wavefronts per block in a 2 x (NW/2) grid: NW = 4 gives 128 x 128
 // wavefront tiles (one wavefront per SIMD), NW = 8 gives 128 x 64 (two per
 // SIMD, so one wavefront's stalls leave the matrix core to the other).
-template <int OP, int NW>
+template <int OP, int NW, bool RS>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // wavefront sub-tile
@@ -104,6 +104,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
   __shared__ int sched[NW + 4];
+  // row-scaled fc2 dgrad: the wavefronts' per-row <h, dh'> partials
+  __shared__ float dp_red[RS ? (NW / 2) * 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
 
   // ---------------------------------------------------------------- epilogue
-  store_tile<OP, FM, FN, WM, WN, TR::ragged_m>(args, acc, ti, M, N, wm, wn, lane);
+  store_tile<OP, FM, FN, WM, WN, TR::ragged_m, RS>(args, acc, ti, M, N, wm, wn, lane, dp_red);
 }
 
 template <int OP, int NW>
@@ -392,7 +394,14 @@ int launch(const GemmArgs& a, hipStream_t s) {
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  gemm_bf16_kernel<OP, NW><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
+  bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
+  if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
+    if (a.row_prob) {
+      gemm_bf16_kernel<OP, NW, true><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
+      scaled = true;
+    }
+  }
+  if (!scaled) gemm_bf16_kernel<OP, NW, false><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

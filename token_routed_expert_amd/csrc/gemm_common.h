@@ -111,10 +111,19 @@ __device__ __forceinline__ void pair_f32(f32x4_t& x, f32x4_t& y) {
 // the SwiGLU backward for fc2 dgrad (reads the saved a|b), plain stores
 // otherwise.  Rows past the tile's valid rows and column pairs past N are
 // skipped.
-template <int OP, int FM, int FN, int WM, int WN, bool RAGGED>
+//
+// RS (row-scaled products, routing probabilities applied before W2; only
+// fc1 forward and fc2 dgrad differ): fc1 forward stores h = p_r silu(a) b;
+// fc2 dgrad takes its accumulators as dh' = dO' W2^T for the unscaled dO',
+// applies the SwiGLU backward to dh = p_r dh', and adds <silu(a) b, dh'> over
+// the tile's columns into args.dp_part[r][n-tile] (per lane over its columns
+// in order, then xor shuffles over the 4 lanes of a row, then the WAVES_N
+// wavefronts of a row in order through `red`, [WAVES_N][256] floats of LDS;
+// every wavefront of the block must call store_tile).
+template <int OP, int FM, int FN, int WM, int WN, bool RAGGED, bool RS = false>
 __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (&acc)[FM][FN],
                                            const TileInfo& ti, int M, int N, int wm, int wn,
-                                           int lane) {
+                                           int lane, float* red = nullptr) {
   constexpr int HB = FN / 2;
   const int d = args.d, f = args.f;
   const size_t e = (size_t)ti.e;
@@ -129,6 +138,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
     constexpr int i = I.value;
     const int m = wm * WM + i * 16 + lm;  // row within the tile
     const bool row_ok = RAGGED ? (m < ti.rows) : (ti.m0 + m < M);
+    float pr = 1.0f, dp = 0.0f;            // RS: the row's probability, <h, dh'> partial
+    if constexpr (RS) pr = row_ok ? args.row_prob[ti.row0 + m] : 0.0f;
     if constexpr (OP == OP_FC1_FWD) {
       // pairs jp < HB/2 hold W1 columns (a), pair jp + HB/2 the same W3 columns (b)
       static_for<0, HB / 2>([&](auto JP) __attribute__((always_inline)) {
@@ -140,6 +151,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
         for (int q = 0; q < 4; ++q) {
           h0[q] = silu_f32(a0[q]) * b0v[q];
           h1[q] = silu_f32(a1[q]) * b1v[q];
+          if constexpr (RS) {
+            h0[q] *= pr;
+            h1[q] *= pr;
+          }
         }
         const u32x4_t av = pair_bf16(a0, a1), bv = pair_bf16(b0v, b1v), hv = pair_bf16(h0, h1);
         const int fcol = ti.n0 / 2 + (wn * HB + j0) * 16 + pc;
@@ -171,8 +186,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
                 const uint32_t aw = av[q >> 1], bw = bv[q >> 1];
                 const float aq = (q & 1) ? hi_bf16(aw) : lo_bf16(aw);
                 const float bq = (q & 1) ? hi_bf16(bw) : lo_bf16(bw);
-                const float c = q < 4 ? x[q] : y[q - 4];
+                float c = q < 4 ? x[q] : y[q - 4];
                 const float sg = sigmoid_f32(aq);
+                if constexpr (RS) {
+                  dp = fmaf(aq * sg * bq, c, dp);  // h = silu(a) b from the saved a, b
+                  c *= pr;
+                }
                 da[q] = c * bq * sg * (1.0f + aq * (1.0f - sg));
                 db[q] = c * aq * sg;
               }
@@ -201,8 +220,24 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
           }
         }
       });
+      if constexpr (RS && OP == OP_FC2_DGRAD) {
+        dp += __shfl_xor(dp, 16, 64);
+        dp += __shfl_xor(dp, 32, 64);
+        if (lane < 16) red[wn * 256 + m] = dp;
+      }
     }
   });
+  if constexpr (RS && OP == OP_FC2_DGRAD) {
+    constexpr int WAVES_N = 256 / WN;
+    block_barrier();
+    const int t = (int)threadIdx.x;
+    if (t < 256 && t < ti.rows) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES_N; ++w) s += red[w * 256 + t];
+      args.dp_part[(size_t)(ti.row0 + t) * (size_t)((f + 255) / 256) + ti.n0 / 256] = s;
+    }
+  }
 }
 
 }  // namespace gemm

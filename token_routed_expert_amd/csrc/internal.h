@@ -30,6 +30,12 @@ int route_bwd_launch(const float* logits, int T, int E, int k, const int32_t* id
                      const float* prob, const float* dprob, const int32_t* counts, float alpha,
                      float aux_scale, float* dlogits, hipStream_t s);
 size_t aux_ws_bytes(int64_t T, int64_t E);
+// row-scaled products: row_prob[row_of[i]] = prob[i] (i < n = T*k); and
+// out[i] = sum over the N-tiles of part[r][.] with r = row_of[i] (or i)
+int row_probs_launch(const int32_t* row_of, const float* prob, int n, float* row_prob,
+                     hipStream_t s);
+int dp_rows_launch(const float* part, int NT, const int32_t* row_of, int n, float* out,
+                   hipStream_t s);
 int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* counts, float alpha,
                     float* loss, void* ws, hipStream_t s);
 
@@ -76,6 +82,11 @@ struct GemmArgs {
   const float* b_s2;
   const int32_t* blk;  // [E+1] token-block table (wgrad)
   int64_t ldt;         // row length in bytes of the token-block operands (wgrad)
+  // row-scaled products (probabilities applied before W2), bf16 only: the
+  // routing probability of every permuted row, and the fc2 dgrad's partial
+  // probability gradients [P][ceil(f/256)]
+  const float* row_prob;
+  float* dp_part;
 };
 
 // gemm_bf16.hip: MFMA kernels, bf16 in/out, fp32 accumulation

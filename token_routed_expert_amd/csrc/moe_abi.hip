@@ -156,6 +156,14 @@ int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
 int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream);
 bool aux_ws_ok(const moe_shape* sh, const moe_layer_io* io, size_t ws_bytes);
+int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                        void* stream);
+int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                        void* stream);
+// per-row partials of the row-scaled fc2 dgrad: [P][ceil(f/256)] fp32
+size_t dp_part_bytes(const moe_shape* sh) {
+  return align_up((size_t)(sh->T * sh->k) * (size_t)((sh->f + 255) / 256) * sizeof(float), 256);
+}
 int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream);
 
 }  // namespace
@@ -189,6 +197,8 @@ size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
   switch (kind) {
     case MOE_WS_AUX_LOSS: return aux_ws_bytes(sh->T, sh->E);
     case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
+    case MOE_WS_GEMM_BWD_ROWSCALED: return sh->dtype == MOE_BF16 ? dp_part_bytes(sh) : 0;
+    case MOE_WS_LAYER_BWD_ROWSCALED: return sh->dtype == MOE_BF16 ? 256 + dp_part_bytes(sh) : 0;
     case MOE_WS_GEMM_FWD:
     case MOE_WS_GEMM_BWD: return 0;
     case MOE_WS_LAYER_FWD: return permute_ws_bytes(sh->T, sh->E) + 256;
@@ -267,6 +277,61 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   a.xp = xp; a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
   a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
   return bwd_sequence(sh, a, (hipStream_t)stream);
+}
+
+int moe_row_probs(const moe_shape* sh, const int32_t* row_of, const float* topk_prob,
+                  float* row_prob, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (!row_of || !topk_prob || !row_prob) return MOE_ERR_INVALID;
+  return row_probs_launch(row_of, topk_prob, (int)(sh->T * sh->k), row_prob, (hipStream_t)stream);
+}
+
+int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                                   const void* W1, const void* W3, const void* W2,
+                                   const float* row_prob, void* ab, void* h, void* o,
+                                   void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!offsets || !xp || !W1 || !W3 || !W2 || !row_prob || !ab || !h || !o) return MOE_ERR_INVALID;
+  GemmArgs a = expert_args(sh, offsets);
+  a.xp = xp; a.W1 = W1; a.W3 = W3; a.W2 = W2; a.row_prob = row_prob;
+  a.ab_out = ab; a.h_out = h; a.h = h; a.o_out = o;
+  return fwd_sequence(sh, a, (hipStream_t)stream);
+}
+
+int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
+                                   const void* ab, const void* h, const void* dO, const void* W1,
+                                   const void* W3, const void* W2, const float* row_prob,
+                                   void* dab, void* dXp, void* dW1, void* dW3, void* dW2,
+                                   const int32_t* row_of, float* dprob, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!offsets || !xp || !ab || !h || !dO || !W1 || !W3 || !W2 || !row_prob || !dab || !dXp ||
+      !dW1 || !dW3 || !dW2)
+    return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < dp_part_bytes(sh)) return MOE_ERR_WORKSPACE;
+  GemmArgs a = expert_args(sh, offsets);
+  a.xp = xp; a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
+  a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
+  a.row_prob = row_prob;
+  a.dp_part = (float*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  // fc2 dgrad alone is row-scaled; the other products take the plain path
+  if ((st = gemm_bf16_launch(OP_FC2_DGRAD, a, s))) return st;
+  a.row_prob = nullptr;
+  a.dab = a.dab_out;
+  if ((st = gemm_bf16_launch(OP_FC1_DGRAD, a, s))) return st;
+  if ((st = gemm_bf16_launch(OP_FC2_WGRAD, a, s))) return st;
+  if ((st = gemm_bf16_launch(OP_FC1_WGRAD, a, s))) return st;
+  if (!dprob) return MOE_OK;
+  return dp_rows_launch((const float*)ws, (int)((sh->f + 255) / 256), row_of,
+                        (int)(sh->T * sh->k), dprob, s);
 }
 
 int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* counts,
@@ -433,7 +498,11 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (sh->dtype == MOE_E4M3) return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
+  if (sh->dtype == MOE_E4M3) {
+    if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
+    return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
+  }
+  if (io && io->memory_efficient) return layer_fwd_rowscaled(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
   if (!io || !io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
@@ -474,7 +543,11 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (sh->dtype == MOE_E4M3) return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
+  if (sh->dtype == MOE_E4M3) {
+    if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
+    return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
+  }
+  if (io && io->memory_efficient) return layer_bwd_rowscaled(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
   if (!io || !io->dY || !io->W1 || !io->W3 || !io->W2 || !io->topk_prob || !io->offsets ||
@@ -573,6 +646,97 @@ int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
   if (ws_bytes < base + need) return MOE_ERR_WORKSPACE;
   return moe_aux_loss(io->logits, sh->T, sh->E, sh->k, io->counts, io->aux_alpha, io->aux_loss,
                       (char*)ws + base, need, stream);
+}
+
+// Memory-efficient layer (probabilities applied before W2), bf16 only.
+int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int st;
+  if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if (!io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
+      !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xp ||
+      !io->ab || !io->h || !io->o || !io->y || !io->row_prob)
+    return MOE_ERR_INVALID;
+  if (sh->f_shared &&
+      (!io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h || !io->ys))
+    return MOE_ERR_INVALID;
+  const size_t pws = permute_ws_bytes(sh->T, sh->E);
+  if (!ws || ws_bytes < pws + 256 || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
+    return st;
+  if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
+                        io->token_of, io->xp, ws, pws, stream)))
+    return st;
+  if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
+  if ((st = moe_row_probs(sh, io->row_of, io->topk_prob, io->row_prob, stream))) return st;
+  if ((st = moe_grouped_gemm_fwd_rowscaled(sh, io->offsets, io->xp, io->W1, io->W3, io->W2,
+                                           io->row_prob, io->ab, io->h, io->o, stream)))
+    return st;
+  const void* add = nullptr;
+  if (sh->f_shared) {
+    int32_t* off2 = (int32_t*)((char*)ws + pws);
+    fill_offsets_kernel<<<1, 64, 0, s>>>(off2, (int32_t)sh->T);
+    TRE_LAUNCH_CHECK();
+    GemmArgs a = shared_args(sh, off2);
+    a.xp = io->x; a.W1 = io->Ws1; a.W3 = io->Ws3; a.W2 = io->Ws2;
+    a.ab_out = io->s_ab; a.h_out = io->s_h; a.h = io->s_h; a.o_out = io->ys;
+    if ((st = fwd_sequence(sh, a, s))) return st;
+    add = io->ys;
+  }
+  // o rows already carry their probability: unweighted combine
+  return moe_unpermute(sh, io->o, io->row_of, nullptr, add, io->y, stream);
+}
+
+int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int st;
+  if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if (!io->dY || !io->W1 || !io->W3 || !io->W2 || !io->offsets || !io->row_of || !io->xp ||
+      !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX || !io->dW1 || !io->dW3 ||
+      !io->dW2 || !io->row_prob)
+    return MOE_ERR_INVALID;
+  if (sh->f_shared && (!io->x || !io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h ||
+                       !io->s_dab || !io->dXs || !io->dWs1 || !io->dWs3 || !io->dWs2))
+    return MOE_ERR_INVALID;
+  if (io->dlogits && (!io->dprob || !io->logits || !io->topk_idx || !io->topk_prob || !io->counts))
+    return MOE_ERR_INVALID;
+  const size_t part = dp_part_bytes(sh);
+  if (!ws || ws_bytes < 256 + part) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float* dp_part = (float*)((char*)ws + 256);
+  // dO = dY permuted, unscaled
+  if ((st = moe_permute(sh, io->dY, nullptr, nullptr, 0, nullptr, nullptr, io->row_of, nullptr,
+                        io->dO, nullptr, 0, stream)))
+    return st;
+  // dprob[t][j] too when the router gradient is asked for
+  if ((st = moe_grouped_gemm_bwd_rowscaled(sh, io->offsets, io->xp, io->ab, io->h, io->dO, io->W1,
+                                           io->W3, io->W2, io->row_prob, io->dab, io->dXp, io->dW1,
+                                           io->dW3, io->dW2, io->row_of,
+                                           io->dlogits ? io->dprob : nullptr, dp_part, part,
+                                           stream)))
+    return st;
+  const void* add = nullptr;
+  if (sh->f_shared) {
+    int32_t* off2 = (int32_t*)ws;
+    fill_offsets_kernel<<<1, 64, 0, s>>>(off2, (int32_t)sh->T);
+    TRE_LAUNCH_CHECK();
+    GemmArgs a = shared_args(sh, off2);
+    a.xp = io->x; a.ab = io->s_ab; a.h = io->s_h; a.dO = io->dY;
+    a.W1 = io->Ws1; a.W3 = io->Ws3; a.W2 = io->Ws2;
+    a.dab_out = io->s_dab; a.dXp_out = io->dXs;
+    a.dW1 = io->dWs1; a.dW3 = io->dWs3; a.dW2 = io->dWs2;
+    if ((st = bwd_sequence(sh, a, s))) return st;
+    add = io->dXs;
+  }
+  if ((st = moe_unpermute(sh, io->dXp, io->row_of, nullptr, add, io->dX, stream))) return st;
+  if (!io->dlogits) return MOE_OK;
+  return moe_route_bwd(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, io->dprob,
+                       io->counts, io->aux_alpha, 1.0f, io->dlogits, stream);
 }
 
 // dO for the expert backward, plus dprob and dlogits when io->dlogits is set

@@ -286,6 +286,28 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict
   if (threadIdx.x == 0) *loss = scale * ((red[0] + red[1]) + (red[2] + red[3]));
 }
 
+// ---------------------------------------------------------------- row-scaled products
+// Probabilities applied before W2: each permuted row's probability, and the
+// sum of the fc2 dgrad's per-N-tile partials of <h, dh'> in N-tile order.
+__global__ __launch_bounds__(256) void row_probs_kernel(const int32_t* __restrict__ row_of,
+                                                        const float* __restrict__ prob, int n,
+                                                        float* __restrict__ row_prob) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) row_prob[row_of[i]] = prob[i];
+}
+
+// out[i] = sum_nt part[r * NT + nt] with r = row_of[i] (or r = i without a map)
+__global__ __launch_bounds__(256) void dp_rows_kernel(const float* __restrict__ part, int NT,
+                                                      const int32_t* __restrict__ row_of, int n,
+                                                      float* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const size_t r = row_of ? (size_t)row_of[i] : (size_t)i;
+  float s = 0.0f;
+  for (int nt = 0; nt < NT; ++nt) s += part[r * NT + nt];
+  out[i] = s;
+}
+
 template <typename T, int CPT>
 void combine_bwd_typed(const void* dY, const void* o, const int32_t* row_of, const float* prob,
                        int T_, int k, int C, void* dO, float* dprob, hipStream_t s) {
@@ -323,6 +345,22 @@ int route_bwd_launch(const float* logits, int T, int E, int k, const int32_t* id
           : 0.0f;
   route_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, idx, prob, dprob, counts, gscale,
                                               dlogits);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int row_probs_launch(const int32_t* row_of, const float* prob, int n, float* row_prob,
+                     hipStream_t s) {
+  if (n <= 0) return MOE_OK;
+  row_probs_kernel<<<(n + 255) / 256, 256, 0, s>>>(row_of, prob, n, row_prob);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int dp_rows_launch(const float* part, int NT, const int32_t* row_of, int n, float* out,
+                   hipStream_t s) {
+  if (n <= 0) return MOE_OK;
+  dp_rows_kernel<<<(n + 255) / 256, 256, 0, s>>>(part, NT, row_of, n, out);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

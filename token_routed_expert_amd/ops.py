@@ -175,7 +175,33 @@ def _io(buffers: dict) -> N.moe_layer_io:
     if wq is not None:
         io.wq = C.cast(C.pointer(wq.struct), C.c_void_p).value
     io.aux_alpha = float(buffers.get("aux_alpha", 0.0))
+    io.memory_efficient = int(bool(buffers.get("memory_efficient", False)))
     return io
+
+
+def moe_row_probs(sh, row_of, topk_prob, row_prob, stream=None):
+    """row_prob[row_of[t][j]] = topk_prob[t][j]."""
+    _check(N.lib().moe_row_probs(C.byref(sh), _ptr(row_of, I32), _ptr(topk_prob, F32),
+                                 _ptr(row_prob, F32), _stream(stream)), "moe_row_probs")
+
+
+def moe_grouped_gemm_fwd_rowscaled(sh, offsets, xp, W1, W3, W2, row_prob, ab, h, o, stream=None):
+    """Expert forward with h = p * silu(a) * b (probabilities applied before W2)."""
+    _check(N.lib().moe_grouped_gemm_fwd_rowscaled(
+        C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(W1), _ptr(W3), _ptr(W2),
+        _ptr(row_prob, F32), _ptr(ab), _ptr(h), _ptr(o), _stream(stream)),
+        "moe_grouped_gemm_fwd_rowscaled")
+
+
+def moe_grouped_gemm_bwd_rowscaled(sh, offsets, xp, ab, h, dO, W1, W3, W2, row_prob, dab, dXp,
+                                   dW1, dW3, dW2, row_of, dprob, ws, stream=None):
+    """Backward of the row-scaled forward for the unscaled permuted dO; dprob is
+    [P] in row order (row_of None) or [T][k]."""
+    _check(N.lib().moe_grouped_gemm_bwd_rowscaled(
+        C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(ab), _ptr(h), _ptr(dO), _ptr(W1),
+        _ptr(W3), _ptr(W2), _ptr(row_prob, F32), _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3),
+        _ptr(dW2), _ptr(row_of, I32), _ptr(dprob, F32), _ptr(ws), _nbytes(ws), _stream(stream)),
+        "moe_grouped_gemm_bwd_rowscaled")
 
 
 def moe_aux_loss(logits, k, counts, alpha, loss, ws, stream=None):
