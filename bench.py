@@ -125,7 +125,7 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
         shared = (sh_s, off_s)
 
     if memory_efficient:
-        return build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg)
+        return build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg, memory_efficient)
 
     def step(ev):
         ev["start"].record()
@@ -168,7 +168,7 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
     return step
 
 
-def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg):
+def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg, memory_efficient):
     """The memory-efficient step: probabilities applied to h before W2, an
     unweighted combine, the unscaled permutation of dY, and the row-scaled
     expert backward (which also yields dprob when the router gradient is on)."""
@@ -200,7 +200,8 @@ def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg):
                                            b["W1"], b["W3"], b["W2"], b["row_prob"], b["dab"],
                                            b["dXp"], b["dW1"], b["dW3"], b["dW2"],
                                            b["row_of"] if rg else None,
-                                           b["dprob"] if rg else None, wsb)
+                                           b["dprob"] if rg else None, wsb,
+                                           recompute_h=memory_efficient == 2)
         if shared:
             tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
                                      b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
@@ -357,6 +358,8 @@ def main():
                     help="also the load-balancing loss, dprob and the router backward (dlogits)")
     ap.add_argument("--memory-efficient", action="store_true",
                     help="probabilities applied before W2 (bf16 workloads)")
+    ap.add_argument("--recompute-h", action="store_true",
+                    help="with --memory-efficient: recompute p*h in the backward instead of keeping it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run two 1 GiB device copies first (for hardware-counter runs)")
     args = ap.parse_args()
@@ -380,7 +383,8 @@ def main():
     if args.memory_efficient and wl.dtype != "bf16":
         log("bench.py: --memory-efficient needs a bf16 workload")
         sys.exit(2)
-    step = build_step(wl, inp, args.router_grad, args.memory_efficient)
+    me = (2 if args.recompute_h else 1) if args.memory_efficient else 0
+    step = build_step(wl, inp, args.router_grad, me)
 
     def marks():
         return {m: torch.cuda.Event(enable_timing=True) for m in MARKS}
@@ -450,7 +454,7 @@ def main():
                 "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},
     }
     if args.memory_efficient:
-        out["config"]["memory_efficient"] = True
+        out["config"]["memory_efficient"] = "recompute_h" if me == 2 else True
         out["breakdown_ms"]["combine_bwd_permute"] = round(t_permb, 4)
     if args.router_grad and args.memory_efficient:
         # dprob comes out of the expert backward; the router backward is timed with it

@@ -208,7 +208,8 @@ typedef struct {
      the probabilities are applied before W2 (h and o hold p-scaled values),
      the backward reads neither o nor a scaled dO, and row_prob [P] (written
      by the forward, read by the backward) holds each permuted row's
-     probability */
+     probability; memory_efficient == 2 also recomputes h in the backward
+     (the forward's h need not be kept, io->h is then overwritten) */
   float* row_prob;
   int32_t memory_efficient;
 } moe_layer_io;
@@ -426,7 +427,9 @@ int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
 /*
  * moe_grouped_gemm_bwd_rowscaled -- backward of the row-scaled forward: dO
  * [P][d] is the UNSCALED permuted upstream gradient (moe_permute without
- * row_scale), h the p-scaled h of the forward.  Writes dab, dXp, dW1, dW3,
+ * row_scale), h the p-scaled h of the forward, or, when recompute_h != 0, a
+ * [P][f] buffer that the call first fills with p * silu(a) * b recomputed
+ * from ab (so the forward's h need not be kept).  Writes dab, dXp, dW1, dW3,
  * dW2 as moe_grouped_gemm_bwd, and, when dprob is not NULL, the probability
  * gradient <silu(a_r) b_r, dO_r W2^T> of each permuted row r: dprob [P] in
  * row order when row_of is NULL, else dprob [T][k] with
@@ -434,11 +437,11 @@ int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
  * MOE_WS_GEMM_BWD_ROWSCALED) (per-row partials of the dot product).
  */
 int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
-                                   const void* ab, const void* h, const void* dO, const void* W1,
-                                   const void* W3, const void* W2, const float* row_prob,
-                                   void* dab, void* dXp, void* dW1, void* dW3, void* dW2,
-                                   const int32_t* row_of, float* dprob, void* ws, size_t ws_bytes,
-                                   void* stream);
+                                   const void* ab, void* h, int32_t recompute_h, const void* dO,
+                                   const void* W1, const void* W3, const void* W2,
+                                   const float* row_prob, void* dab, void* dXp, void* dW1,
+                                   void* dW3, void* dW2, const int32_t* row_of, float* dprob,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);

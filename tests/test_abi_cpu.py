@@ -170,15 +170,16 @@ def test_rowscaled_validation():
     for dtype, expect in (("f32", N.MOE_ERR_UNSUPPORTED), ("e4m3", N.MOE_ERR_UNSUPPORTED)):
         sh = make_shape(64, 256, 8, 2, 256, 0, dtype)
         assert lib.moe_grouped_gemm_fwd_rowscaled(C.byref(sh), *([P] * 10)) == expect
-        assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 17), 1 << 20, None) == expect
+        assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 4), 0, *([P] * 13), 1 << 20,
+                                                  None) == expect
     sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")
     args = [P] * 10
     args[6] = None                                           # row_prob
     assert lib.moe_grouped_gemm_fwd_rowscaled(C.byref(sh), *args) == N.MOE_ERR_INVALID
     need = moe_workspace_bytes(sh, N.MOE_WS_GEMM_BWD_ROWSCALED)
     assert need == -(-128 * 1 * 4 // 256) * 256
-    assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 17), need - 1, None) == \
-        N.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_gemm_bwd_rowscaled(C.byref(sh), *([P] * 4), 1, *([P] * 13), need - 1,
+                                              None) == N.MOE_ERR_WORKSPACE
     assert lib.moe_row_probs(C.byref(sh), None, P, P, None) == N.MOE_ERR_INVALID
     assert moe_workspace_bytes(make_shape(64, 256, 8, 2, 256, 0, "f32"),
                                N.MOE_WS_LAYER_BWD_ROWSCALED) == 0

@@ -51,10 +51,11 @@ def check_dprob(wl, st, h, dp):
     assert (err <= 2e-2 * mag).all(), f"dprob: worst |err|/sum|terms| {(err / mag).max():.3e}"
 
 
+@pytest.mark.parametrize("mode", [1, 2], ids=["keep_h", "recompute_h"])
 @pytest.mark.parametrize("wl", BF16, ids=lambda w: w.name)
-def test_layer_memory_efficient(wl):
+def test_layer_memory_efficient(wl, mode):
     inp = make_inputs(wl, seed=0, device="cuda")
-    b = run_layer(wl, inp, memory_efficient=True)
+    b = run_layer(wl, inp, memory_efficient=mode)
     h = host_inputs(inp)
     st, g = oracle_layer(wl, h)
     check_routing_and_map(wl, b, inp, st)
@@ -73,20 +74,24 @@ def test_layer_memory_efficient(wl):
         assert not b["dW1"][e].any() and not b["dW3"][e].any() and not b["dW2"][e].any()
 
 
+@pytest.mark.parametrize("mode", [1, 2], ids=["keep_h", "recompute_h"])
 @pytest.mark.parametrize("wl", [Workload("me_rg_bf16", T=777, d=256, E=16, k=4, f=384),
                                 Workload("me_rg_skew_bf16", T=500, d=384, E=16, k=4, f=256,
                                          skew=True)],
                          ids=lambda w: w.name)
-def test_memory_efficient_router_grad(wl):
+def test_memory_efficient_router_grad(wl, mode):
     """dprob from the fc2 dgrad epilogue, dlogits and the loss; the backward
-    does not read o (poisoned between forward and backward)."""
+    does not read o, nor h when it recomputes it (poisoned between forward
+    and backward)."""
     import token_routed_expert_amd as tre
     from token_routed_expert_amd.buffers import layer_buffers
     inp = make_inputs(wl, seed=4, device="cuda")
     sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, 0, "bf16", "cuda", inp,
-                                    router_grad=True, aux_alpha=0.01, memory_efficient=True)
+                                    router_grad=True, aux_alpha=0.01, memory_efficient=mode)
     tre.moe_layer_fwd(sh, b, wsf)
     b["o"].fill_(float("nan"))
+    if mode == 2:
+        b["h"].fill_(float("nan"))
     tre.moe_layer_bwd(sh, b, wsb)
     torch.cuda.synchronize()
     h = host_inputs(inp)
@@ -105,11 +110,12 @@ def test_memory_efficient_router_grad(wl):
     assert abs(float(b["aux_loss"].item()) - ref_loss) <= 5e-5 * ref_loss
 
 
-def test_memory_efficient_is_deterministic():
+@pytest.mark.parametrize("mode", [1, 2], ids=["keep_h", "recompute_h"])
+def test_memory_efficient_is_deterministic(mode):
     wl = Workload("me_det_bf16", T=900, d=256, E=16, k=4, f=256)
     inp = make_inputs(wl, seed=2, device="cuda")
-    b1 = run_layer(wl, inp, memory_efficient=True, router_grad=True)
-    b2 = run_layer(wl, inp, memory_efficient=True, router_grad=True)
+    b1 = run_layer(wl, inp, memory_efficient=mode, router_grad=True)
+    b2 = run_layer(wl, inp, memory_efficient=mode, router_grad=True)
     for n in ("y", "dX", "dW1", "dW3", "dW2", "h", "o", "dprob", "dlogits"):
         assert torch.equal(b1[n], b2[n]), n
 
@@ -153,9 +159,19 @@ def test_rowscaled_entry_points():
                                        inp["W2"], rp, out["dab"], out["dXp"], out["dW1"],
                                        out["dW3"], out["dW2"], b["row_of"], dtk, ws)
     assert torch.equal(dtk, dpr[b["row_of"].long()])
+    # recompute_h: h is refilled from ab before fc2 wgrad reads it
+    out2 = {n: torch.empty_like(b[n]) for n in ("dab", "dXp", "dW1", "dW3", "dW2")}
+    hr = torch.full_like(hs, float("nan"))
+    tre.moe_grouped_gemm_bwd_rowscaled(sh, b["offsets"], b["xp"], ab, hr, dO, inp["W1"], inp["W3"],
+                                       inp["W2"], rp, out2["dab"], out2["dXp"], out2["dW1"],
+                                       out2["dW3"], out2["dW2"], None, None, ws, recompute_h=True)
+    assert_close("recomputed p h", to_f64(hr), pr[:, None] * st["h"], TOL["bf16"])
+    for n in ("dab", "dXp", "dW1", "dW3"):
+        assert torch.equal(out2[n], out[n]), n          # h enters only fc2 wgrad
+    assert_close("dW2 (recomputed h)", to_f64(out2["dW2"]), g["dW2"], TOL["bf16"])
 
 
 @pytest.mark.parametrize("wl", [WORKLOADS["qwen3_bf16"], WORKLOADS["deepseek_v3_bf16"]],
                          ids=lambda w: w.name)
 def test_memory_efficient_full_size_sampled(wl):
-    full_size_sampled(wl, memory_efficient=True)
+    full_size_sampled(wl, memory_efficient=2)

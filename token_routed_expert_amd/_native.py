@@ -79,7 +79,8 @@ _PROTOS = {
                                 _P]),
     "moe_row_probs": (C.c_int, [_SH, _P, _P, _P, _P]),
     "moe_grouped_gemm_fwd_rowscaled": (C.c_int, [_SH] + [_P] * 10),
-    "moe_grouped_gemm_bwd_rowscaled": (C.c_int, [_SH] + [_P] * 17 + [C.c_size_t, _P]),
+    "moe_grouped_gemm_bwd_rowscaled": (C.c_int, [_SH] + [_P] * 4 + [C.c_int32] + [_P] * 13
+                                       + [C.c_size_t, _P]),
     "moe_workspace_bytes": (C.c_size_t, [_SH, C.c_int]),
     "moe_status_str": (C.c_char_p, [C.c_int]),
 }

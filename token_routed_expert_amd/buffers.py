@@ -14,7 +14,8 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
     router_grad: also the load-balancing loss (coefficient aux_alpha) and the
     router gradient (aux_loss, dprob, dlogits).
-    memory_efficient: probabilities applied before W2 (bf16; row_prob [P]).
+    memory_efficient: probabilities applied before W2 (bf16; row_prob [P]);
+    2 also recomputes h in the backward.
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """
     sh = make_shape(T, d, E, k, f, f_shared, dtype)
@@ -49,7 +50,7 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     ws_f = torch.empty(max(256, ws_f_bytes), dtype=torch.uint8, device=device)
     bwd_kind = N.MOE_WS_LAYER_BWD
     if memory_efficient:
-        b.update(row_prob=z(P, dtype=torch.float32), memory_efficient=True)
+        b.update(row_prob=z(P, dtype=torch.float32), memory_efficient=int(memory_efficient))
         bwd_kind = N.MOE_WS_LAYER_BWD_ROWSCALED
     ws_b = torch.empty(max(256, moe_workspace_bytes(sh, bwd_kind)), dtype=torch.uint8,
                        device=device)

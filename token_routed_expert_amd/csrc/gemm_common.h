@@ -115,7 +115,8 @@ __device__ __forceinline__ void pair_f32(f32x4_t& x, f32x4_t& y) {
 // RS (row-scaled products, routing probabilities applied before W2; only
 // fc1 forward and fc2 dgrad differ): fc1 forward stores h = p_r silu(a) b;
 // fc2 dgrad takes its accumulators as dh' = dO' W2^T for the unscaled dO',
-// applies the SwiGLU backward to dh = p_r dh', and adds <silu(a) b, dh'> over
+// applies the SwiGLU backward to dh = p_r dh' (and, when args.h_out is set,
+// stores the recomputed p_r silu(a) b there), and adds <silu(a) b, dh'> over
 // the tile's columns into args.dp_part[r][n-tile] (per lane over its columns
 // in order, then xor shuffles over the 4 lanes of a row, then the WAVES_N
 // wavefronts of a row in order through `red`, [WAVES_N][256] floats of LDS;
@@ -180,7 +181,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
               const bf16_t* abr = (const bf16_t*)args.ab + row * (2 * (size_t)f);
               const u32x4_t av = *(const u32x4_t*)(abr + col);
               const u32x4_t bv = *(const u32x4_t*)(abr + f + col);
-              float da[8], db[8];
+              float da[8], db[8], hr[8];
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
                 const uint32_t aw = av[q >> 1], bw = bv[q >> 1];
@@ -189,7 +190,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
                 float c = q < 4 ? x[q] : y[q - 4];
                 const float sg = sigmoid_f32(aq);
                 if constexpr (RS) {
-                  dp = fmaf(aq * sg * bq, c, dp);  // h = silu(a) b from the saved a, b
+                  hr[q] = aq * sg * bq;  // h = silu(a) b from the saved a, b
+                  dp = fmaf(hr[q], c, dp);
                   c *= pr;
                 }
                 da[q] = c * bq * sg * (1.0f + aq * (1.0f - sg));
@@ -200,6 +202,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
                                                pack_bf16x2(da[4], da[5]), pack_bf16x2(da[6], da[7])};
               *(u32x4_t*)(dab + f + col) = u32x4_t{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]),
                                                    pack_bf16x2(db[4], db[5]), pack_bf16x2(db[6], db[7])};
+              if constexpr (RS) {
+                if (args.h_out) {
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) hr[q] *= pr;
+                  *(u32x4_t*)((bf16_t*)args.h_out + row * (size_t)f + col) =
+                      u32x4_t{pack_bf16x2(hr[0], hr[1]), pack_bf16x2(hr[2], hr[3]),
+                              pack_bf16x2(hr[4], hr[5]), pack_bf16x2(hr[6], hr[7])};
+                }
+              }
             }
           } else {
             const u32x4_t v = pair_bf16(acc[i][j0], acc[i][j0 + 1]);

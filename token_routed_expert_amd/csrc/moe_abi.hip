@@ -303,11 +303,11 @@ int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
 }
 
 int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
-                                   const void* ab, const void* h, const void* dO, const void* W1,
-                                   const void* W3, const void* W2, const float* row_prob,
-                                   void* dab, void* dXp, void* dW1, void* dW3, void* dW2,
-                                   const int32_t* row_of, float* dprob, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   const void* ab, void* h, int32_t recompute_h, const void* dO,
+                                   const void* W1, const void* W3, const void* W2,
+                                   const float* row_prob, void* dab, void* dXp, void* dW1,
+                                   void* dW3, void* dW2, const int32_t* row_of, float* dprob,
+                                   void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
@@ -321,10 +321,12 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
   a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
   a.row_prob = row_prob;
   a.dp_part = (float*)ws;
+  a.h_out = recompute_h ? h : nullptr;  // fc2 dgrad's epilogue refills h for fc2 wgrad
   hipStream_t s = (hipStream_t)stream;
   // fc2 dgrad alone is row-scaled; the other products take the plain path
   if ((st = gemm_bf16_launch(OP_FC2_DGRAD, a, s))) return st;
   a.row_prob = nullptr;
+  a.h_out = nullptr;
   a.dab = a.dab_out;
   if ((st = gemm_bf16_launch(OP_FC1_DGRAD, a, s))) return st;
   if ((st = gemm_bf16_launch(OP_FC2_WGRAD, a, s))) return st;
@@ -714,8 +716,9 @@ int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
                         io->dO, nullptr, 0, stream)))
     return st;
   // dprob[t][j] too when the router gradient is asked for
-  if ((st = moe_grouped_gemm_bwd_rowscaled(sh, io->offsets, io->xp, io->ab, io->h, io->dO, io->W1,
-                                           io->W3, io->W2, io->row_prob, io->dab, io->dXp, io->dW1,
+  if ((st = moe_grouped_gemm_bwd_rowscaled(sh, io->offsets, io->xp, io->ab, io->h,
+                                           io->memory_efficient == 2, io->dO, io->W1, io->W3,
+                                           io->W2, io->row_prob, io->dab, io->dXp, io->dW1,
                                            io->dW3, io->dW2, io->row_of,
                                            io->dlogits ? io->dprob : nullptr, dp_part, part,
                                            stream)))

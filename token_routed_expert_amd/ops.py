@@ -175,7 +175,7 @@ def _io(buffers: dict) -> N.moe_layer_io:
     if wq is not None:
         io.wq = C.cast(C.pointer(wq.struct), C.c_void_p).value
     io.aux_alpha = float(buffers.get("aux_alpha", 0.0))
-    io.memory_efficient = int(bool(buffers.get("memory_efficient", False)))
+    io.memory_efficient = int(buffers.get("memory_efficient", 0))
     return io
 
 
@@ -194,11 +194,13 @@ def moe_grouped_gemm_fwd_rowscaled(sh, offsets, xp, W1, W3, W2, row_prob, ab, h,
 
 
 def moe_grouped_gemm_bwd_rowscaled(sh, offsets, xp, ab, h, dO, W1, W3, W2, row_prob, dab, dXp,
-                                   dW1, dW3, dW2, row_of, dprob, ws, stream=None):
+                                   dW1, dW3, dW2, row_of, dprob, ws, recompute_h=False,
+                                   stream=None):
     """Backward of the row-scaled forward for the unscaled permuted dO; dprob is
-    [P] in row order (row_of None) or [T][k]."""
+    [P] in row order (row_of None) or [T][k]; recompute_h refills h first."""
     _check(N.lib().moe_grouped_gemm_bwd_rowscaled(
-        C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(ab), _ptr(h), _ptr(dO), _ptr(W1),
+        C.byref(sh), _ptr(offsets, I32), _ptr(xp), _ptr(ab), _ptr(h), int(bool(recompute_h)),
+        _ptr(dO), _ptr(W1),
         _ptr(W3), _ptr(W2), _ptr(row_prob, F32), _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3),
         _ptr(dW2), _ptr(row_of, I32), _ptr(dprob, F32), _ptr(ws), _nbytes(ws), _stream(stream)),
         "moe_grouped_gemm_bwd_rowscaled")
