@@ -20,3 +20,4 @@ from .moe import *  # noqa: F401,F403
 from .e4m3 import *  # noqa: F401,F403
 from .moe_e4m3 import *  # noqa: F401,F403
 from .router import *  # noqa: F401,F403
+from .mx import *  # noqa: F401,F403
