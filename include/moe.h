@@ -37,7 +37,10 @@
  *    saved activations bf16, fp32 accumulation, one round-to-nearest-even per
  *    output element) or MOE_E4M3 (the expert GEMMs take OCP E4M3FN operands
  *    with fp32 block scales -- see "e4m3 expert GEMMs" below -- while x, dY,
- *    y, dX, the saved activations and the weight gradients are bf16).  Router
+ *    y, dX, the saved activations and the weight gradients are bf16) or
+ *    MOE_MXFP8 (the same with MXFP8 operands: E4M3FN codes with one
+ *    power-of-two E8M0 scale byte per 32 values -- see "MXFP8 expert GEMMs"
+ *    below).  Router
  *    logits and probabilities are always fp32 (German summary, section 2 E:
  *    the router stays in high precision).
  */
@@ -59,7 +62,7 @@ typedef enum {
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef struct {
   int64_t T, d, E, k, f;
@@ -212,6 +215,10 @@ typedef struct {
      (the forward's h need not be kept, io->h is then overwritten) */
   float* row_prob;
   int32_t memory_efficient;
+  /* MXFP8 layers (sh->dtype == MOE_MXFP8): the quantised weights (W1, W3, W2
+     may be NULL); xq, xpq hold codes as for e4m3 and xs, xps hold E8M0 scale
+     bytes, [T][d/32] and [P][d/32] (the same byte count as the e4m3 scales) */
+  const struct moe_mx_weights* wmx;
 } moe_layer_io;
 
 /*
@@ -220,7 +227,8 @@ typedef struct {
  * moe_route, moe_permute(build_map=1), moe_grouped_gemm_fwd and
  * moe_unpermute in sequence on one stream.  For MOE_E4M3: moe_route,
  * moe_quantize_rows of x into xq/xs, moe_permute_e4m3 into xpq/xps,
- * moe_grouped_gemm_fwd_e4m3, moe_unpermute.  With io->aux_loss set, also
+ * moe_grouped_gemm_fwd_e4m3, moe_unpermute (MOE_MXFP8: the _mx calls, weights
+ * io->wmx).  With io->aux_loss set, also
  * moe_aux_loss (alpha = io->aux_alpha) after the permutation; ws_bytes then
  * needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient (bf16):
  * moe_row_probs into io->row_prob, moe_grouped_gemm_fwd_rowscaled and an
@@ -442,6 +450,75 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
                                    const float* row_prob, void* dab, void* dXp, void* dW1,
                                    void* dW3, void* dW2, const int32_t* row_of, float* dprob,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MXFP8 expert GEMMs
+ * ------------------
+ * The pages run the Blackwell results in MXFP8 (French summary, section 2 E;
+ * Spanish summary, section 2.4) and name it without a definition; the format
+ * is the OCP Microscaling one.  Every block of 32 consecutive values along a
+ * product's contraction axis has one scale 2^s, stored as the E8M0 byte
+ * s + 127, with s the smallest integer such that max|v| <= 448 * 2^s (the
+ * scale rounded up, so nothing saturates; s clamped to [-127, 127]; an
+ * all-zero block has s = 0 and +0 codes); codes are E4M3FN(v * 2^-s), round
+ * to nearest even.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0
+ * scale per lane, which is one 32-value block of one row, so the scales go
+ * straight into the matrix instruction.  Scale bytes are stored row-major next
+ * to the codes they scale:
+ *  - activation rows [rows][K] -> bytes [rows][K/32];
+ *  - each weight matrix in both orientations (the blocks of the two differ):
+ *    codes [E][R][C] with row-block bytes [E][R][C/32] (read by the
+ *    data-gradient products), and transposed codes [E][C][R] with
+ *    column-block bytes [E][C][R/32] (read by the forward products);
+ *  - weight-gradient operands as moe_quantize_token_blocks lays them out,
+ *    with bytes [C][ldt/32] (32-row blocks restart at each expert).
+ * Shapes: d, f multiples of 128, no shared expert.
+ */
+
+/* Quantised expert weights as written by moe_quantize_weights_mx. */
+typedef struct moe_mx_weights {
+  const uint8_t *W1, *W3, *W2;       /* codes [E][d][f], [E][d][f], [E][f][d] */
+  const uint8_t *W1t, *W3t, *W2t;    /* transposed codes [E][f][d], [E][f][d], [E][d][f] */
+  const uint8_t *W1s, *W3s, *W2s;    /* row-block bytes [E][d][f/32], .., [E][f][d/32] */
+  const uint8_t *W1ts, *W3ts, *W2ts; /* column-block bytes [E][f][d/32], .., [E][d][f/32] */
+} moe_mx_weights;
+
+/* moe_quantize_rows_mx -- 1 x 32 blocks along each row of src [rows][cols]
+ * (MOE_BF16 or MOE_F32, cols a multiple of 32): codes [rows][cols], scale
+ * bytes [rows][cols/32]. */
+int moe_quantize_rows_mx(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* scales, void* stream);
+
+/* moe_quantize_weights_mx -- both orientations of E fp32 matrices W [E][R][C]
+ * (R, C multiples of 128): codes [E][R][C] + bytes [E][R][C/32], codes_t
+ * [E][C][R] + bytes [E][C][R/32]; one pass over W. */
+int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                            uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream);
+
+/* moe_quantize_token_blocks_mx -- as moe_quantize_token_blocks, with 32-row
+ * scale blocks: codes_t [C][ldt] (ldt = 128 * capacity), scale bytes
+ * [C][ldt/32]; blocks with no rows have s = 0. */
+int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
+                                 const int32_t* src_row, int64_t C, int32_t* blk,
+                                 uint8_t* codes_t, uint8_t* scales, void* stream);
+
+/* moe_permute_mx -- moe_permute_e4m3 for MXFP8 rows: codes [T][d] and scale
+ * bytes [T][d/32] moved to the permuted order (bit copies). */
+int moe_permute_mx(const moe_shape* sh, const uint8_t* codes, const uint8_t* scales,
+                   const int32_t* topk_idx, int build_map, int32_t* counts, int32_t* offsets,
+                   int32_t* row_of, int32_t* token_of, uint8_t* dst_codes, uint8_t* dst_scales,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* moe_grouped_gemm_fwd_mx / moe_grouped_gemm_bwd_mx -- the e4m3 calls' MXFP8
+ * counterparts (sh->dtype == MOE_MXFP8; xps are scale bytes [P][d/32]); the
+ * same workspace sizes (MOE_WS_GEMM_FWD / MOE_WS_GEMM_BWD). */
+int moe_grouped_gemm_fwd_mx(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq,
+                            const uint8_t* xps, const moe_mx_weights* w, void* ab, void* h,
+                            void* o, void* ws, size_t ws_bytes, void* stream);
+int moe_grouped_gemm_bwd_mx(const moe_shape* sh, const int32_t* offsets, const int32_t* token_of,
+                            const void* x, const void* ab, const void* h, const void* dO,
+                            const moe_mx_weights* w, void* dab, void* dXp, void* dW1, void* dW3,
+                            void* dW2, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);

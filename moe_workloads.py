@@ -33,7 +33,7 @@ class Workload:
     k: int
     f: int
     f_shared: int = 0
-    dtype: str = "bf16"          # storage dtype of x, weights, dY: "f32" | "bf16" | "e4m3"
+    dtype: str = "bf16"          # "f32" | "bf16" | "e4m3" | "mxfp8" (fp8: bf16 x, dY; fp32 weights)
     skew: bool = False           # add a Zipf-rank bias to the logits (hot/cold experts)
 
     @property
@@ -70,6 +70,11 @@ WORKLOADS = {
     "skewed_fp8": Workload("skewed_fp8", T=8200, d=4096, E=128, k=8, f=1536, dtype="e4m3",
                            skew=True),
 }
+# The skewed fp8 shape with MXFP8 operands (E8M0 scales per 32 values) in place
+# of the blockwise e4m3 recipe.
+VARIANTS = {
+    "skewed_mxfp8": WORKLOADS["skewed_fp8"].with_(name="skewed_mxfp8", dtype="mxfp8"),
+}
 
 # Order in which per-tensor streams are named (each gets its own generator).
 TENSOR_NAMES = ("bias_perm", "logits", "x", "W1", "W3", "W2", "Ws1", "Ws3", "Ws2", "dY")
@@ -93,7 +98,7 @@ def storage_dtype(wl: Workload) -> torch.dtype:
 
 def weight_dtype(wl: Workload) -> torch.dtype:
     """The fp8 workload draws fp32 master weights; the path quantises them itself."""
-    if wl.dtype == "e4m3":
+    if wl.dtype in ("e4m3", "mxfp8"):
         return torch.float32
     return storage_dtype(wl)
 
@@ -178,8 +183,8 @@ def to_f64(t: torch.Tensor):
 
 
 def bytes_per_elem(dtype: str) -> int:
-    return {"f32": 4, "bf16": 2, "e4m3": 1}[dtype]
+    return {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1}[dtype]
 
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "skew_bias", "tied_logits", "to_f64",
+__all__ = ["Workload", "WORKLOADS", "VARIANTS", "make_inputs", "skew_bias", "tied_logits", "to_f64",
            "storage_dtype", "weight_dtype", "bytes_per_elem"]

@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtre_moe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_MXFP8 = 0, 1, 2, 3
 (MOE_WS_PERMUTE, MOE_WS_GEMM_FWD, MOE_WS_GEMM_BWD, MOE_WS_LAYER_FWD,
  MOE_WS_LAYER_BWD, MOE_WS_AUX_LOSS, MOE_WS_GEMM_BWD_ROWSCALED,
  MOE_WS_LAYER_BWD_ROWSCALED) = range(8)
@@ -40,10 +40,15 @@ _IO_FIELDS_ROUTER = ["aux_loss", "dprob", "dlogits"]
 class moe_layer_io(C.Structure):
     _fields_ = ([(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3 + _IO_FIELDS_ROUTER]
                 + [("aux_alpha", C.c_float), ("row_prob", C.c_void_p),
-                   ("memory_efficient", C.c_int32)])
+                   ("memory_efficient", C.c_int32), ("wmx", C.c_void_p)])
 
 
 IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:] + _IO_FIELDS_ROUTER + ["row_prob"])
+
+
+class moe_mx_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("W1", "W3", "W2", "W1t", "W3t", "W2t", "W1s", "W3s", "W2s", "W1ts", "W3ts", "W2ts")]
 
 
 class moe_e4m3_weights(C.Structure):
@@ -73,6 +78,16 @@ _PROTOS = {
     "moe_grouped_gemm_bwd_e4m3": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P,
                                             C.POINTER(moe_e4m3_weights), _P, _P, _P, _P, _P, _P,
                                             C.c_size_t, _P]),
+    "moe_quantize_rows_mx": (C.c_int, [_P, C.c_int32, _I64, _I64, _P, _P, _P]),
+    "moe_quantize_weights_mx": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "moe_quantize_token_blocks_mx": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "moe_permute_mx": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
+                                 C.c_size_t, _P]),
+    "moe_grouped_gemm_fwd_mx": (C.c_int, [_SH, _P, _P, _P, C.POINTER(moe_mx_weights), _P, _P,
+                                          _P, _P, C.c_size_t, _P]),
+    "moe_grouped_gemm_bwd_mx": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P,
+                                          C.POINTER(moe_mx_weights), _P, _P, _P, _P, _P, _P,
+                                          C.c_size_t, _P]),
     "moe_aux_loss": (C.c_int, [_P, _I64, _I64, _I64, _P, C.c_float, _P, _P, C.c_size_t, _P]),
     "moe_combine_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, C.c_float, C.c_float, _P,

@@ -4,7 +4,8 @@ from __future__ import annotations
 import torch
 
 from . import _native as N
-from .ops import E4M3Weights, make_shape, moe_quantize_weights, moe_workspace_bytes
+from .ops import (E4M3Weights, MXWeights, make_shape, moe_quantize_weights,
+                  moe_quantize_weights_mx, moe_workspace_bytes)
 
 
 def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None,
@@ -39,6 +40,13 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
                  xpq=z(P, d, dtype=u8), xps=z(P, d // 128, dtype=torch.float32))
         if "W1" in b and b["W1"].dtype == torch.float32:
             b["wq"] = quantized_weights(b["W1"], b["W3"], b["W2"])
+    if dtype == "mxfp8":
+        u8 = torch.uint8
+        b.pop("xp")
+        b.update(xq=z(T, d, dtype=u8), xs=z(T, d // 32, dtype=u8),
+                 xpq=z(P, d, dtype=u8), xps=z(P, d // 32, dtype=u8))
+        if "W1" in b and b["W1"].dtype == torch.float32:
+            b["wmx"] = quantized_weights_mx(b["W1"], b["W3"], b["W2"])
     if f_shared:
         b.update(s_ab=z(T, 2 * f_shared), s_h=z(T, f_shared), ys=z(T, d), s_dab=z(T, 2 * f_shared),
                  dXs=z(T, d), dWs1=z(d, f_shared), dWs3=z(d, f_shared), dWs2=z(f_shared, d))
@@ -72,7 +80,28 @@ def quantized_weights(W1, W3, W2, stream=None) -> E4M3Weights:
     return wq
 
 
-def requantize_weights(wq: E4M3Weights, W1, W3, W2, stream=None):
-    """Refresh wq from the fp32 masters (e.g. after an optimizer step)."""
+def requantize_weights(wq, W1, W3, W2, stream=None):
+    """Refresh wq (E4M3Weights or MXWeights) from the fp32 masters (e.g. after an
+    optimizer step)."""
     for name, W in (("W1", W1), ("W3", W3), ("W2", W2)):
-        moe_quantize_weights(W, wq[name], wq[name + "t"], wq[name + "s"], stream)
+        if isinstance(wq, MXWeights):
+            moe_quantize_weights_mx(W, wq[name], wq[name + "s"], wq[name + "t"], wq[name + "ts"],
+                                    stream)
+        else:
+            moe_quantize_weights(W, wq[name], wq[name + "t"], wq[name + "s"], stream)
+
+
+def quantized_weights_mx(W1, W3, W2, stream=None) -> MXWeights:
+    """MXFP8 codes and E8M0 scale bytes of fp32 expert weights in both
+    orientations, made by moe_quantize_weights_mx."""
+    E, d, f = W1.shape
+    dev = W1.device
+    t = {}
+    for name, W, R, Cc in (("W1", W1, d, f), ("W3", W3, d, f), ("W2", W2, f, d)):
+        t[name] = torch.empty(E, R, Cc, dtype=torch.uint8, device=dev)
+        t[name + "s"] = torch.empty(E, R, Cc // 32, dtype=torch.uint8, device=dev)
+        t[name + "t"] = torch.empty(E, Cc, R, dtype=torch.uint8, device=dev)
+        t[name + "ts"] = torch.empty(E, Cc, R // 32, dtype=torch.uint8, device=dev)
+    wq = MXWeights(t)
+    requantize_weights(wq, W1, W3, W2, stream)
+    return wq

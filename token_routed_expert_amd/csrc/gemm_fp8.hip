@@ -57,6 +57,19 @@ __device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int c0, int sw
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The scaled MFMA's operand layout (measured): lane group g = lane >> 4 holds
+// K values [16 g, 16 g + 16) in its bytes 0..15 and [64 + 16 g, 64 + 16 g + 16)
+// in bytes 16..31, and the scale of 32-value block g of the row comes from
+// lane group g.  So an MXFP8 fragment takes 16-byte chunks g and g + 4 of the
+// 128-byte K row (the plain MFMA of the e4m3 path accepts any K order that A
+// and B share, and takes chunks 2g, 2g + 1).
+__device__ __forceinline__ i32x8_t lds_frag_mx(const char* row_base, int g, int sw) {
+  const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((g ^ sw) << 4));
+  const i32x4_t hi =
+      *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((g + 4) ^ sw) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& b, const i32x8_t& a) {
   const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, z, 0, 0, 0, 0, 0, 0);
@@ -66,7 +79,17 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-template <int OP>
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// MX = true: MXFP8 operands.  v_mfma_scale_f32_16x16x128_f8f6f4 takes one
+// E8M0 scale per lane and operand -- that of 32-value block (lane >> 4) of the
+// lane's row (see lds_frag_mx for the matching fragment layout) -- so the
+// scales go straight into the MFMA, which accumulates in place: no promotion.
+// A lane's scale byte for fragment row r and stage kt is byte (lane >> 4) of
+// the word at r * ld + 4 kt.
+template <int OP, bool MX>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
@@ -76,7 +99,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
   // weight-gradient products: per stage the 256 A-row and 256 B-column scales
-  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][256];
+  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][MX ? 4 : 256];
   __shared__ int sched[NW + 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
@@ -171,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // consecutive floats each) go to LDS with one DMA instruction each
   // (wavefronts 0 and 1); rows past the matrix read as zero.
   rsrc_t sca_src, scb_src;
-  if constexpr (WGRAD) {
+  if constexpr (WGRAD && !MX) {
     const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
     sca_src = make_rsrc(args.a_s + (size_t)kb0 * Mt + ti.m0, (uint32_t)((K / BK) * Mt - ti.m0) * 4u);
     scb_src = make_rsrc(args.b_s + (size_t)kb0 * N + ti.n0, (uint32_t)((K / BK) * N - ti.n0) * 4u);
@@ -179,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   auto issue_stage = [&](int kt) __attribute__((always_inline)) {
     const uint32_t st = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
     const uint32_t ka = (uint32_t)kt * BK;
-    if constexpr (WGRAD) {
+    if constexpr (WGRAD && !MX) {
       const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
       const uint32_t sc = sc_base + (uint32_t)((kt & (NSTAGE - 1)) * 2048);
       if (wid == 0) dma16(sca_src, (uint32_t)kt * (uint32_t)Mt * 4u + (uint32_t)lane * 16u, sc);
@@ -205,11 +228,118 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     }
   };
 
+  const int lm = lane & 15, lg = lane >> 4;
+  // B rows of fragment j within the B tile (fc1 forward: W1 rows then W3 rows)
+  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (OP == OP_FC1_FWD) return (j < FN / 2 ? 0 : 128) + wn * (WN / 2) + 16 * (j % (FN / 2)) + lm;
+    else return wn * WN + 16 * j + lm;
+  };
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (MX) {
+    // ------------------------------------------------------------ MXFP8 scales
+    __amdgpu_buffer_rsrc_t xa, xb, xb2;
+    uint32_t xa_ld, xb_ld;
+    if constexpr (RAGGED) {
+      xa_ld = (uint32_t)(K / 32);
+      xa = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_sx + (size_t)ti.row0 * xa_ld), 0,
+                                             ti.rows * (int)xa_ld, 0x00020000);
+      size_t b0;
+      int brows;
+      if constexpr (OP == OP_FC1_FWD) {
+        xb_ld = (uint32_t)(d / 32); b0 = (e * f + ti.n0 / 2) * xb_ld; brows = 128;
+      } else if constexpr (OP == OP_FC2_FWD) {
+        xb_ld = (uint32_t)(f / 32); b0 = (e * d + ti.n0) * xb_ld; brows = d - ti.n0;
+      } else if constexpr (OP == OP_FC2_DGRAD) {
+        xb_ld = (uint32_t)(d / 32); b0 = (e * f + ti.n0) * xb_ld; brows = f - ti.n0;
+      } else {
+        xb_ld = (uint32_t)(f / 32); b0 = (e * d + ti.n0) * xb_ld; brows = d - ti.n0;
+      }
+      xb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_sx + b0), 0, brows * (int)xb_ld,
+                                             0x00020000);
+      xb2 = (OP == OP_FC1_FWD || OP == OP_FC1_DGRAD)
+                ? __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_sx2 + b0), 0,
+                                                    brows * (int)xb_ld, 0x00020000)
+                : xb;
+    } else {
+      xa_ld = xb_ld = (uint32_t)(args.ldt / 32);
+      xa = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(args.a_sx + (size_t)ti.m0 * xa_ld + (size_t)kb0 * 4), 0,
+          (M - ti.m0) * (int)xa_ld - kb0 * 4, 0x00020000);
+      xb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(args.b_sx + (size_t)ti.n0 * xb_ld + (size_t)kb0 * 4), 0,
+          (N - ti.n0) * (int)xb_ld - kb0 * 4, 0x00020000);
+      xb2 = xb;
+    }
+    auto load_scales = [&](int kt, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        sa[i] = buf_u32(xa, (uint32_t)(wm * WM + 16 * i + lm) * xa_ld + (uint32_t)kt * 4u);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (OP == OP_FC1_FWD) {
+          sb[j] = buf_u32(j < FN / 2 ? xb : xb2, (uint32_t)(b_row(j) & 127) * xb_ld + (uint32_t)kt * 4u);
+        } else if constexpr (OP == OP_FC1_DGRAD) {
+          const int fb = f / 128;
+          sb[j] = buf_u32(kt < fb ? xb : xb2,
+                          (uint32_t)b_row(j) * xb_ld + (uint32_t)(kt < fb ? kt : kt - fb) * 4u);
+        } else {
+          sb[j] = buf_u32(xb, (uint32_t)b_row(j) * xb_ld + (uint32_t)kt * 4u);
+        }
+      }
+    };
+    uint32_t sa[FM], sb[FN], sa_n[FM], sb_n[FN];
+    if (KT > 0) {
+      load_scales(0, sa, sb);
+      issue_stage(0);
+    }
+    wait_vmcnt<0>();
+    block_barrier();
+    const int sh8 = 8 * lg;
+    for (int kt = 0; kt < KT; ++kt) {
+      const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
+      if (kt + 1 < KT) {
+        load_scales(kt + 1, sa_n, sb_n);
+        issue_stage(kt + 1);
+      }
+      i32x8_t bf[FN];
+      int sbb[FN];
+      static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+        const int r = b_row(J.value);
+        bf[J.value] = lds_frag_mx(cur + OPND_BYTES + r * BK, lg, swz(r));
+        sbb[J.value] = (int)((sb[J.value] >> sh8) & 0xffu);
+      });
+      static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = I.value;
+        const int r = wm * WM + 16 * i + lm;
+        const i32x8_t af = lds_frag_mx(cur + r * BK, lg, swz(r));
+        const int sab = (int)((sa[i] >> sh8) & 0xffu);
+        static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+          constexpr int j = J.value;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0,
+                                                                         0, sbb[j], 0, sab);
+        });
+      });
+      wait_vmcnt<0>();
+      block_barrier();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
+    }
+    store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
+    return;
+  }
+
   // ---------------------------------------------------------------- scales
   // sa[i]: scale of the A block of fragment row m = wm*WM + 16 i + (lane & 15);
   // ragged ops: a_s[(row0 + m) * K/128 + kt] (0 past the expert's rows);
   // wgrad: a_s[(kb0 + kt) * M_total + m0 + m].
-  const int lm = lane & 15, lg = lane >> 4;
   __amdgpu_buffer_rsrc_t sa_src;
   uint32_t sa_stride;  // bytes between the scales of consecutive stages
   uint32_t sa_off0;
@@ -250,12 +380,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   };
 
   // ---------------------------------------------------------------- main loop
-  f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   float sa[FM], sa_n[FM];  // ragged ops: this stage's and the next stage's A scales
   f32x4_t sb[FN];           // weight gradients: this stage's B scales (4 columns per fragment)
   if (KT > 0) {
@@ -264,12 +388,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   }
   wait_vmcnt<0>();
   block_barrier();
-
-  // B rows of fragment j within the B tile (fc1 forward: W1 rows then W3 rows)
-  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (OP == OP_FC1_FWD) return (j < FN / 2 ? 0 : 128) + wn * (WN / 2) + 16 * (j % (FN / 2)) + lm;
-    else return wn * WN + 16 * j + lm;
-  };
 
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
@@ -342,7 +460,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
 }
 
-template <int OP>
+template <int OP, bool MX>
 int launch(const GemmArgs& a, hipStream_t s) {
   int NT, MT = 0;
   int64_t grid;
@@ -358,7 +476,7 @@ int launch(const GemmArgs& a, hipStream_t s) {
     grid = (int64_t)a.E * MT * NT;
   }
   if (grid == 0) return MOE_OK;
-  gemm_fp8_kernel<OP><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+  gemm_fp8_kernel<OP, MX><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -367,12 +485,24 @@ int launch(const GemmArgs& a, hipStream_t s) {
 
 int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_FC1_FWD: return launch<OP_FC1_FWD>(a, s);
-    case OP_FC2_FWD: return launch<OP_FC2_FWD>(a, s);
-    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD>(a, s);
-    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD>(a, s);
-    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD>(a, s);
-    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD>(a, s);
+    case OP_FC1_FWD: return launch<OP_FC1_FWD, false>(a, s);
+    case OP_FC2_FWD: return launch<OP_FC2_FWD, false>(a, s);
+    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, false>(a, s);
+    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, false>(a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, false>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, false>(a, s);
+  }
+  return MOE_ERR_INVALID;
+}
+
+int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_FC1_FWD: return launch<OP_FC1_FWD, true>(a, s);
+    case OP_FC2_FWD: return launch<OP_FC2_FWD, true>(a, s);
+    case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, true>(a, s);
+    case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, true>(a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, true>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, true>(a, s);
   }
   return MOE_ERR_INVALID;
 }

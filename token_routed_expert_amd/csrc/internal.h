@@ -87,6 +87,14 @@ struct GemmArgs {
   // probability gradients [P][ceil(f/256)]
   const float* row_prob;
   float* dp_part;
+  // MXFP8 products (gemm_fp8.hip with E8M0 scales): the same code operands as
+  // e4m3, with one scale byte per 32 contraction values, stored row-major per
+  // operand row: A rows [.][K/32] (wgrad: [M][ldt/32]); B: the byte array of
+  // each weight matrix in the orientation read ([E][n][K/32]; fc1 forward and
+  // fc1 dgrad use b_sx2 for W3), wgrad [N][ldt/32].
+  const uint8_t* a_sx;
+  const uint8_t* b_sx;
+  const uint8_t* b_sx2;
 };
 
 // gemm_bf16.hip: MFMA kernels, bf16 in/out, fp32 accumulation
@@ -95,13 +103,25 @@ int gemm_bf16_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 int gemm_f32_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // gemm_fp8.hip: e4m3 x e4m3 MFMA with per-128-K scale promotion, bf16 outputs
 int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
+// the same products with MXFP8 operands (hardware block-scaled MFMA)
+int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 
 // quant.hip: e4m3 block quantisers
 int quant_rows_launch(const void* src, bool src_f32, int64_t rows, int64_t cols, uint8_t* codes,
                       float* scales, hipStream_t s);
 int quant_tiles_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
                        uint8_t* codes_t, float* scales, hipStream_t s);
-int64_t tokblk_max_blocks(int64_t P, int64_t E);  // bound on sum_e ceil(m_e / 128)
+int64_t tokblk_max_blocks(int64_t P, int64_t E);
+// MXFP8 quantisers (E8M0 byte scales per 32 values): rows [rows][cols] ->
+// codes + bytes [rows][cols/32]; both orientations of expert weights; token
+// blocks (32-row scale blocks inside the 128-row blocks of quant_tokblk)
+int quant_rows_mx_launch(const void* src, bool src_f32, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* sb, hipStream_t s);
+int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                            uint8_t* sb, uint8_t* codes_t, uint8_t* sbt, hipStream_t s);
+int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
+                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                           uint8_t* sbt, hipStream_t s);  // bound on sum_e ceil(m_e / 128)
 int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t s);
 int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
                         const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,

@@ -17,6 +17,8 @@ __global__ void fill_offsets_kernel(int32_t* off, int32_t T) {
 }
 
 int elem_bytes(const moe_shape* sh) { return sh->dtype == MOE_F32 ? 4 : 2; }
+// e4m3 or MXFP8 expert GEMMs (bf16 activations)
+bool is_fp8(const moe_shape* sh) { return sh->dtype == MOE_E4M3 || sh->dtype == MOE_MXFP8; }
 
 // Shape checks shared by every call.  Returns MOE_OK or an error code.
 int check_shape(const moe_shape* sh) {
@@ -24,9 +26,10 @@ int check_shape(const moe_shape* sh) {
   if (sh->T < 1 || sh->d < 1 || sh->E < 1 || sh->k < 1 || sh->f < 1 || sh->f_shared < 0)
     return MOE_ERR_INVALID;
   if (sh->k > sh->E || sh->reserved != 0) return MOE_ERR_INVALID;
-  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16 && sh->dtype != MOE_E4M3)
+  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16 && sh->dtype != MOE_E4M3 &&
+      sh->dtype != MOE_MXFP8)
     return MOE_ERR_UNSUPPORTED;
-  if (sh->dtype == MOE_E4M3 && sh->f_shared != 0) return MOE_ERR_UNSUPPORTED;
+  if (is_fp8(sh) && sh->f_shared != 0) return MOE_ERR_UNSUPPORTED;
   if (sh->E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (sh->T * sh->k >= ((int64_t)1 << 31) || sh->d >= (1 << 30) || sh->f >= (1 << 30) ||
       sh->f_shared >= (1 << 30))
@@ -108,6 +111,46 @@ size_t bwd8_ws_bytes(const moe_shape* sh) {
 bool weights_ok(const moe_e4m3_weights* w) {
   return w && w->W1 && w->W3 && w->W2 && w->W1t && w->W3t && w->W2t && w->W1s && w->W3s && w->W2s;
 }
+bool weights_ok(const moe_mx_weights* w) {
+  return w && w->W1 && w->W3 && w->W2 && w->W1t && w->W3t && w->W2t && w->W1s && w->W3s &&
+         w->W2s && w->W1ts && w->W3ts && w->W2ts;
+}
+
+// The weight operands of the fp8 products: codes in both orientations and
+// the scales read with each (e4m3: one tile-scale array serves both; MXFP8:
+// row-block bytes with W1/W3/W2, column-block bytes with the transposed codes).
+struct Wq8 {
+  const uint8_t *W1, *W3, *W2, *W1t, *W3t, *W2t;
+  const void *s1, *s3, *s2, *s1t, *s3t, *s2t;
+};
+Wq8 wq8_of(const moe_e4m3_weights* w) {
+  return Wq8{w->W1, w->W3, w->W2, w->W1t, w->W3t, w->W2t,
+             w->W1s, w->W3s, w->W2s, w->W1s, w->W3s, w->W2s};
+}
+Wq8 wq8_of(const moe_mx_weights* w) {
+  return Wq8{w->W1, w->W3, w->W2, w->W1t, w->W3t, w->W2t,
+             w->W1s, w->W3s, w->W2s, w->W1ts, w->W3ts, w->W2ts};
+}
+void set_a_scales(GemmArgs& a, const void* sc, bool mx) {
+  if (mx) a.a_sx = (const uint8_t*)sc; else a.a_s = (const float*)sc;
+}
+void set_b_scales(GemmArgs& a, const void* sc, const void* sc2, bool mx) {
+  if (mx) { a.b_sx = (const uint8_t*)sc; a.b_sx2 = (const uint8_t*)sc2; }
+  else { a.b_s = (const float*)sc; a.b_s2 = (const float*)sc2; }
+}
+int gemm8(GemmOp op, const GemmArgs& a, hipStream_t s, bool mx) {
+  return mx ? gemm_mx_launch(op, a, s) : gemm_fp8_launch(op, a, s);
+}
+int qrows8(const void* src, int64_t rows, int64_t cols, uint8_t* codes, void* sc, hipStream_t s,
+           bool mx) {
+  return mx ? quant_rows_mx_launch(src, false, rows, cols, codes, (uint8_t*)sc, s)
+            : quant_rows_launch(src, false, rows, cols, codes, (float*)sc, s);
+}
+int qtok8(const void* src, const int32_t* src_row, const int32_t* offsets, const int32_t* blk,
+          int E, int64_t P, int64_t C, uint8_t* codes_t, void* sc, hipStream_t s, bool mx) {
+  return mx ? quant_tokblk_mx_launch(src, src_row, offsets, blk, E, P, C, codes_t, (uint8_t*)sc, s)
+            : quant_tokblk_launch(src, src_row, offsets, blk, E, P, C, codes_t, (float*)sc, s);
+}
 
 int run_gemm(const moe_shape* sh, GemmOp op, const GemmArgs& a, hipStream_t s) {
   return sh->dtype == MOE_F32 ? gemm_f32_launch(op, a, s) : gemm_bf16_launch(op, a, s);
@@ -166,6 +209,68 @@ size_t dp_part_bytes(const moe_shape* sh) {
 }
 int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream);
 
+// Expert forward of the fp8 products (e4m3 or MXFP8); arguments checked by the caller.
+int gemm_fwd8(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq, const void* xps,
+              const Wq8& w, void* ab, void* h, void* o, void* ws, size_t ws_bytes, void* stream,
+              bool mx) {
+  int st;
+  size_t need;
+  Fwd8Ws W = carve_fwd8(sh, ws, &need);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t P = sh->T * sh->k;
+  GemmArgs a = expert_args(sh, offsets);
+  a.a_q = xpq; set_a_scales(a, xps, mx);
+  a.b_q = w.W1t; a.b_q2 = w.W3t; set_b_scales(a, w.s1t, w.s3t, mx);
+  a.ab_out = ab; a.h_out = h;
+  if ((st = gemm8(OP_FC1_FWD, a, s, mx))) return st;
+  if ((st = qrows8(h, P, sh->f, W.hq, W.hs, s, mx))) return st;
+  a.a_q = W.hq; set_a_scales(a, W.hs, mx);
+  a.b_q = w.W2t; a.b_q2 = nullptr; set_b_scales(a, w.s2t, nullptr, mx);
+  a.o_out = o;
+  return gemm8(OP_FC2_FWD, a, s, mx);
+}
+
+
+// Expert backward of the fp8 products (e4m3 or MXFP8); arguments checked by the caller.
+int gemm_bwd8(const moe_shape* sh, const int32_t* offsets, const int32_t* token_of, const void* x,
+              const void* ab, const void* h, const void* dO, const Wq8& w, void* dab, void* dXp,
+              void* dW1, void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream, bool mx) {
+  int st;
+  size_t need;
+  Bwd8Ws W = carve_bwd8(sh, ws, &need);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int64_t P = sh->T * sh->k, d = sh->d, f = sh->f, E = sh->E;
+  if ((std::max(d, 2 * f) + 256) * 128 * W.cap >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs a = expert_args(sh, offsets);
+  // data gradients: dH = dO W2^T (+ SwiGLU backward -> dab), dXp = dab [W1|W3]^T
+  if ((st = qrows8(dO, P, d, W.dOq, W.dOs, s, mx))) return st;
+  a.a_q = W.dOq; set_a_scales(a, W.dOs, mx); a.b_q = w.W2; set_b_scales(a, w.s2, nullptr, mx);
+  a.ab = ab; a.dab_out = dab;
+  if ((st = gemm8(OP_FC2_DGRAD, a, s, mx))) return st;
+  if ((st = qrows8(dab, P, 2 * f, W.dabq, W.dabs, s, mx))) return st;
+  a.a_q = W.dabq; set_a_scales(a, W.dabs, mx);
+  a.b_q = w.W1; a.b_q2 = w.W3; set_b_scales(a, w.s1, w.s3, mx);
+  a.dXp_out = dXp;
+  if ((st = gemm8(OP_FC1_DGRAD, a, s, mx))) return st;
+  // weight gradients on 128-row token blocks: dW2 = h^T dO, [dW1|dW3] = xp^T dab
+  if ((st = tokblk_table_launch(offsets, (int)E, W.blk, s))) return st;
+  a.blk = W.blk;
+  a.ldt = 128 * W.cap;
+  if ((st = qtok8(h, nullptr, offsets, W.blk, (int)E, P, f, W.AT, W.sA, s, mx))) return st;
+  if ((st = qtok8(dO, nullptr, offsets, W.blk, (int)E, P, d, W.BT, W.sB, s, mx))) return st;
+  a.a_q = W.AT; set_a_scales(a, W.sA, mx);
+  a.b_q = W.BT; a.b_q2 = nullptr; set_b_scales(a, W.sB, nullptr, mx);
+  a.dW2 = dW2;
+  if ((st = gemm8(OP_FC2_WGRAD, a, s, mx))) return st;
+  if ((st = qtok8(x, token_of, offsets, W.blk, (int)E, P, d, W.AT, W.sA, s, mx))) return st;
+  if ((st = qtok8(dab, nullptr, offsets, W.blk, (int)E, P, 2 * f, W.BT, W.sB, s, mx))) return st;
+  a.dW1 = dW1; a.dW3 = dW3;
+  return gemm8(OP_FC1_WGRAD, a, s, mx);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -183,7 +288,7 @@ const char* moe_status_str(int status) {
 
 size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
   if (check_shape(sh) != MOE_OK) return 0;
-  if (sh->dtype == MOE_E4M3) {
+  if (is_fp8(sh)) {
     switch (kind) {
       case MOE_WS_AUX_LOSS: return aux_ws_bytes(sh->T, sh->E);
       case MOE_WS_PERMUTE: return permute_ws_bytes(sh->T, sh->E);
@@ -252,7 +357,7 @@ int moe_grouped_gemm_fwd(const moe_shape* sh, const int32_t* offsets, const void
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->dtype == MOE_E4M3) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_fwd_e4m3
+  if (is_fp8(sh)) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_fwd_e4m3 / _mx
   if (!offsets || !xp || !W1 || !W3 || !W2 || !ab || !h || !o) return MOE_ERR_INVALID;
   GemmArgs a = expert_args(sh, offsets);
   a.xp = xp; a.W1 = W1; a.W3 = W3; a.W2 = W2;
@@ -269,7 +374,7 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->dtype == MOE_E4M3) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_bwd_e4m3
+  if (is_fp8(sh)) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_bwd_e4m3 / _mx
   if (!offsets || !xp || !ab || !h || !dO || !W1 || !W3 || !W2 || !dab || !dXp || !dW1 || !dW3 ||
       !dW2)
     return MOE_ERR_INVALID;
@@ -434,21 +539,18 @@ int moe_grouped_gemm_fwd_e4m3(const moe_shape* sh, const int32_t* offsets, const
   if (sh->dtype != MOE_E4M3) return MOE_ERR_INVALID;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (!offsets || !xpq || !xps || !weights_ok(w) || !ab || !h || !o) return MOE_ERR_INVALID;
-  size_t need;
-  Fwd8Ws W = carve_fwd8(sh, ws, &need);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t P = sh->T * sh->k;
-  GemmArgs a = expert_args(sh, offsets);
-  a.a_q = xpq; a.a_s = xps;
-  a.b_q = w->W1t; a.b_q2 = w->W3t; a.b_s = w->W1s; a.b_s2 = w->W3s;
-  a.ab_out = ab; a.h_out = h;
-  if ((st = gemm_fp8_launch(OP_FC1_FWD, a, s))) return st;
-  if ((st = quant_rows_launch(h, false, P, sh->f, W.hq, W.hs, s))) return st;
-  a.a_q = W.hq; a.a_s = W.hs;
-  a.b_q = w->W2t; a.b_q2 = nullptr; a.b_s = w->W2s; a.b_s2 = nullptr;
-  a.o_out = o;
-  return gemm_fp8_launch(OP_FC2_FWD, a, s);
+  return gemm_fwd8(sh, offsets, xpq, xps, wq8_of(w), ab, h, o, ws, ws_bytes, stream, false);
+}
+
+int moe_grouped_gemm_fwd_mx(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq,
+                            const uint8_t* xps, const moe_mx_weights* w, void* ab, void* h,
+                            void* o, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (sh->dtype != MOE_MXFP8) return MOE_ERR_INVALID;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!offsets || !xpq || !xps || !weights_ok(w) || !ab || !h || !o) return MOE_ERR_INVALID;
+  return gemm_fwd8(sh, offsets, xpq, xps, wq8_of(w), ab, h, o, ws, ws_bytes, stream, true);
 }
 
 int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
@@ -463,44 +565,74 @@ int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
   if (!offsets || !token_of || !x || !ab || !h || !dO || !weights_ok(w) || !dab || !dXp || !dW1 ||
       !dW3 || !dW2)
     return MOE_ERR_INVALID;
-  size_t need;
-  Bwd8Ws W = carve_bwd8(sh, ws, &need);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  const int64_t P = sh->T * sh->k, d = sh->d, f = sh->f, E = sh->E;
-  if ((std::max(d, 2 * f) + 256) * 128 * W.cap >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  return gemm_bwd8(sh, offsets, token_of, x, ab, h, dO, wq8_of(w), dab, dXp, dW1, dW3, dW2, ws,
+                   ws_bytes, stream, false);
+}
+
+int moe_grouped_gemm_bwd_mx(const moe_shape* sh, const int32_t* offsets, const int32_t* token_of,
+                            const void* x, const void* ab, const void* h, const void* dO,
+                            const moe_mx_weights* w, void* dab, void* dXp, void* dW1, void* dW3,
+                            void* dW2, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (sh->dtype != MOE_MXFP8) return MOE_ERR_INVALID;
+  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if (!offsets || !token_of || !x || !ab || !h || !dO || !weights_ok(w) || !dab || !dXp || !dW1 ||
+      !dW3 || !dW2)
+    return MOE_ERR_INVALID;
+  return gemm_bwd8(sh, offsets, token_of, x, ab, h, dO, wq8_of(w), dab, dXp, dW1, dW3, dW2, ws,
+                   ws_bytes, stream, true);
+}
+
+int moe_quantize_rows_mx(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!src || !codes || !scales || rows < 0 || cols < 0) return MOE_ERR_INVALID;
+  if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (cols % 32 != 0 || rows * (cols / 32) >= ((int64_t)1 << 36)) return MOE_ERR_UNSUPPORTED;
+  return quant_rows_mx_launch(src, src_dtype == MOE_F32, rows, cols, codes, scales,
+                              (hipStream_t)stream);
+}
+
+int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                            uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream) {
+  if (!W || !codes || !scales || !codes_t || !scales_t || E < 0 || R < 0 || C < 0)
+    return MOE_ERR_INVALID;
+  if (R % 128 != 0 || C % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (R >= (1 << 30) || C >= (1 << 30) || E > 65535 || C / 128 > 65535 || R / 128 > 65535)
+    return MOE_ERR_UNSUPPORTED;
+  return quant_weights_mx_launch(W, E, R, C, codes, scales, codes_t, scales_t,
+                                 (hipStream_t)stream);
+}
+
+int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
+                                 const int32_t* src_row, int64_t C, int32_t* blk,
+                                 uint8_t* codes_t, uint8_t* scales, void* stream) {
+  if (!offsets || !src || !blk || !codes_t || !scales) return MOE_ERR_INVALID;
+  if (E < 1 || P < 0 || C < 0) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (C % 128 != 0 || C >= (1 << 30) || P >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((C + 256) * 128 * tokblk_max_blocks(P, E) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
-  GemmArgs a = expert_args(sh, offsets);
-  // data gradients: dH = dO W2^T (+ SwiGLU backward -> dab), dXp = dab [W1|W3]^T
-  if ((st = quant_rows_launch(dO, false, P, d, W.dOq, W.dOs, s))) return st;
-  a.a_q = W.dOq; a.a_s = W.dOs; a.b_q = w->W2; a.b_s = w->W2s;
-  a.ab = ab; a.dab_out = dab;
-  if ((st = gemm_fp8_launch(OP_FC2_DGRAD, a, s))) return st;
-  if ((st = quant_rows_launch(dab, false, P, 2 * f, W.dabq, W.dabs, s))) return st;
-  a.a_q = W.dabq; a.a_s = W.dabs;
-  a.b_q = w->W1; a.b_q2 = w->W3; a.b_s = w->W1s; a.b_s2 = w->W3s;
-  a.dXp_out = dXp;
-  if ((st = gemm_fp8_launch(OP_FC1_DGRAD, a, s))) return st;
-  // weight gradients on 128-row token blocks: dW2 = h^T dO, [dW1|dW3] = xp^T dab
-  if ((st = tokblk_table_launch(offsets, (int)E, W.blk, s))) return st;
-  a.blk = W.blk;
-  a.ldt = 128 * W.cap;
-  if ((st = quant_tokblk_launch(h, nullptr, offsets, W.blk, (int)E, P, f, W.AT, W.sA, s))) return st;
-  if ((st = quant_tokblk_launch(dO, nullptr, offsets, W.blk, (int)E, P, d, W.BT, W.sB, s))) return st;
-  a.a_q = W.AT; a.a_s = W.sA; a.b_q = W.BT; a.b_q2 = nullptr; a.b_s = W.sB; a.b_s2 = nullptr;
-  a.dW2 = dW2;
-  if ((st = gemm_fp8_launch(OP_FC2_WGRAD, a, s))) return st;
-  if ((st = quant_tokblk_launch(x, token_of, offsets, W.blk, (int)E, P, d, W.AT, W.sA, s))) return st;
-  if ((st = quant_tokblk_launch(dab, nullptr, offsets, W.blk, (int)E, P, 2 * f, W.BT, W.sB, s)))
-    return st;
-  a.dW1 = dW1; a.dW3 = dW3;
-  return gemm_fp8_launch(OP_FC1_WGRAD, a, s);
+  int st = tokblk_table_launch(offsets, (int)E, blk, s);
+  if (st) return st;
+  return quant_tokblk_mx_launch(src, src_row, offsets, blk, (int)E, P, C, codes_t, scales, s);
+}
+
+int moe_permute_mx(const moe_shape* sh, const uint8_t* codes, const uint8_t* scales,
+                   const int32_t* topk_idx, int build_map, int32_t* counts, int32_t* offsets,
+                   int32_t* row_of, int32_t* token_of, uint8_t* dst_codes, uint8_t* dst_scales,
+                   void* ws, size_t ws_bytes, void* stream) {
+  // d/32 scale bytes per row are the byte count of d/128 fp32 scales: the
+  // e4m3 row move copies them bit for bit
+  return moe_permute_e4m3(sh, codes, (const float*)scales, topk_idx, build_map, counts, offsets,
+                          row_of, token_of, dst_codes, (float*)dst_scales, ws, ws_bytes, stream);
 }
 
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (sh->dtype == MOE_E4M3) {
+  if (is_fp8(sh)) {
     if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
     return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
   }
@@ -545,7 +677,7 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (sh->dtype == MOE_E4M3) {
+  if (is_fp8(sh)) {
     if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
     return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
   }
@@ -588,11 +720,14 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
 
 namespace {
 
+// e4m3 and MXFP8 layers
 int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream) {
   int st;
+  const bool mx = sh->dtype == MOE_MXFP8;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (!io || !io->logits || !io->x || !weights_ok(io->wq) || !io->topk_idx || !io->topk_prob ||
+  if (!io || !(mx ? weights_ok(io->wmx) : weights_ok(io->wq))) return MOE_ERR_INVALID;
+  if (!io->logits || !io->x || !io->topk_idx || !io->topk_prob ||
       !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xq || !io->xs ||
       !io->xpq || !io->xps || !io->ab || !io->h || !io->o || !io->y)
     return MOE_ERR_INVALID;
@@ -601,13 +736,16 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
   if (!ws || ws_bytes < pws + gws || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
   if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
     return st;
-  if ((st = moe_quantize_rows(io->x, MOE_BF16, sh->T, sh->d, io->xq, io->xs, stream))) return st;
+  if ((st = (mx ? moe_quantize_rows_mx(io->x, MOE_BF16, sh->T, sh->d, io->xq,
+                                       (uint8_t*)io->xs, stream)
+                 : moe_quantize_rows(io->x, MOE_BF16, sh->T, sh->d, io->xq, io->xs, stream))))
+    return st;
   if ((st = moe_permute_e4m3(sh, io->xq, io->xs, io->topk_idx, 1, io->counts, io->offsets,
                              io->row_of, io->token_of, io->xpq, io->xps, ws, pws, stream)))
     return st;
   if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
-  if ((st = moe_grouped_gemm_fwd_e4m3(sh, io->offsets, io->xpq, io->xps, io->wq, io->ab, io->h,
-                                      io->o, (char*)ws + pws, gws, stream)))
+  if ((st = gemm_fwd8(sh, io->offsets, io->xpq, io->xps, mx ? wq8_of(io->wmx) : wq8_of(io->wq),
+                      io->ab, io->h, io->o, (char*)ws + pws, gws, stream, mx)))
     return st;
   return moe_unpermute(sh, io->o, io->row_of, io->topk_prob, nullptr, io->y, stream);
 }
@@ -615,16 +753,18 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
 int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream) {
   int st;
+  const bool mx = sh->dtype == MOE_MXFP8;
   if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (!io || !io->dY || !io->x || !weights_ok(io->wq) || !io->topk_prob || !io->offsets ||
+  if (!io || !(mx ? weights_ok(io->wmx) : weights_ok(io->wq))) return MOE_ERR_INVALID;
+  if (!io->dY || !io->x || !io->topk_prob || !io->offsets ||
       !io->row_of || !io->token_of || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp ||
       !io->dX || !io->dW1 || !io->dW3 || !io->dW2)
     return MOE_ERR_INVALID;
   if (!ws || ws_bytes < bwd8_ws_bytes(sh)) return MOE_ERR_WORKSPACE;
   if ((st = layer_combine_bwd(sh, io, stream))) return st;
-  if ((st = moe_grouped_gemm_bwd_e4m3(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
-                                      io->wq, io->dab, io->dXp, io->dW1, io->dW3, io->dW2, ws,
-                                      ws_bytes, stream)))
+  if ((st = gemm_bwd8(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
+                      mx ? wq8_of(io->wmx) : wq8_of(io->wq), io->dab, io->dXp, io->dW1, io->dW3,
+                      io->dW2, ws, ws_bytes, stream, mx)))
     return st;
   return moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream);
 }

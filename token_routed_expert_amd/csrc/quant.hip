@@ -270,7 +270,240 @@ __global__ __launch_bounds__(256) void quant_tokblk_kernel(
   }
 }
 
+// ================================================================ MXFP8
+// OCP microscaling: blocks of 32 values along the contraction axis share a
+// power-of-two scale 2^s, stored as the E8M0 byte s + 127; s is the smallest
+// integer with amax <= 448 * 2^s (clamped to [-127, 127]; 0 for an all-zero
+// block), so the block maximum maps into (224, 448] and nothing saturates.
+// Codes are E4M3(v * 2^-s) (exact scaling), all-zero blocks give +0 codes.
+
+// amax = f * 2^E, f in [1, 2): s = E - 8 if f <= 1.75 (448 = 1.75 * 2^8), else E - 7.
+__device__ __forceinline__ int mx_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  if (u == 0) return 0;
+  const int ef = (int)(u >> 23);
+  if (ef == 0) return -127;  // subnormal amax: below any reachable scale
+  const int s = ef - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return s < -127 ? -127 : s;
+}
+// 2^-s as an fp32 (s in [-127, 120])
+__device__ __forceinline__ float mx_inv(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
+__device__ __forceinline__ uint32_t mx_code(float v, float inv, bool zero_block) {
+  return zero_block ? 0u : e4m3_code(v * inv);
+}
+
+// 1 x 32 blocks along rows: 4 lanes per block (8 values each), 64 blocks per
+// 256 threads; block g covers values [32 g, 32 g + 32), scale byte sb[g].
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_mx_kernel(const T* __restrict__ src, int64_t nblk,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ sb) {
+  const int64_t g = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int sub = threadIdx.x & 3;
+  if (g >= nblk) return;  // whole 4-lane groups leave together
+  float v[8];
+  load8<T>(src + g * 32 + sub * 8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  const int s = mx_exp(m);
+  const float inv = mx_inv(s);
+  const bool z = m == 0.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= mx_code(v[i], inv, z) << (8 * i);
+    hi |= mx_code(v[4 + i], inv, z) << (8 * i);
+  }
+  *(uint2*)(codes + g * 32 + sub * 8) = make_uint2(lo, hi);
+  if (sub == 0) sb[g] = (uint8_t)(s + 127);
+}
+
+// Both MX orientations of expert weights from the fp32 masters, one block per
+// 128 x 128 tile (grid: C/128, R/128, E).  Row blocks (1 x 32 along a row):
+// codes [E][R][C], bytes sb [E][R][C/32].  Column blocks (32 x 1 along a
+// column): codes_t [E][C][R], bytes sbt [E][C][R/32].  Thread (rg, cl) =
+// (tid / 32, tid % 32) holds rows 16 rg .. + 15 and columns 4 cl .. + 3: a row
+// block spans the 8 lanes cl / 8 = const (xor shuffles 1, 2, 4), a column
+// block the row groups rg = 2 g, 2 g + 1 (lanes l and l + 32, xor 32).
+__global__ __launch_bounds__(256) void quant_weights_mx_kernel(
+    const float* __restrict__ W, int R, int C, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ sb, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ sbt) {
+  __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row], padded rows
+  const int cb = blockIdx.x, rb = blockIdx.y, e = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int rg = tid >> 5, cl = tid & 31, col = cl * 4;
+  const size_t mat = (size_t)e * R * C;
+  const float* Wt = W + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
+  f32x4_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = *(const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col);
+  // row blocks
+  uint8_t* Ct = codes + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float m = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    const int s = mx_exp(m);
+    const float inv = mx_inv(s);
+    const bool z = m == 0.0f;
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w |= mx_code(v[i][q], inv, z) << (8 * q);
+    const int r = rb * 128 + 16 * rg + i;
+    *(uint32_t*)(Ct + (size_t)(16 * rg + i) * C + col) = w;
+    if ((cl & 7) == 0) sb[((size_t)e * R + r) * (C / 32) + cb * 4 + (cl >> 3)] = (uint8_t)(s + 127);
+  }
+  // column blocks: rows 32 g .. 32 g + 31 with g = rg / 2
+  uint32_t colw[4][4] = {};  // [column q][word w]: rows 16 rg + 4 w .. + 3
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i][q]));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const int s = mx_exp(m);
+    const float inv = mx_inv(s);
+    const bool z = m == 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) colw[q][i >> 2] |= mx_code(v[i][q], inv, z) << (8 * (i & 3));
+    if ((rg & 1) == 0)
+      sbt[((size_t)e * C + (size_t)cb * 128 + col + q) * (R / 32) + rb * 4 + (rg >> 1)] =
+          (uint8_t)(s + 127);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(u32x4_t*)&tt[col + q][16 * rg] = u32x4_t{colw[q][0], colw[q][1], colw[q][2], colw[q][3]};
+  __syncthreads();
+  uint8_t* Tt = codes_t + mat + (size_t)cb * 128 * R + (size_t)rb * 128;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int id = pass * 256 + tid;
+    const int c = id >> 3, r16 = (id & 7) * 16;
+    *(u32x4_t*)(Tt + (size_t)c * R + r16) = *(const u32x4_t*)&tt[c][r16];
+  }
+}
+
+// Token blocks in MX form: as quant_tokblk_kernel, with four 32-row scale
+// blocks per column in each 128-row block.  codes_t [C][ldt] as there; scale
+// bytes sbt [C][ldt / 32], byte 4 b + g for rows 32 g .. 32 g + 31 of block b
+// (groups past the expert's rows: s = 0).  Thread rg = tid / 16 holds rows
+// rg + 16 i (i < 8), which lie in group i / 2.
+__global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
+    const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
+    int64_t ldt, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ sbt) {
+  __shared__ float red[16][4][128];
+  __shared__ int sx[4][128];
+  __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row]
+  const int b = blockIdx.x, cb = blockIdx.y, tid = threadIdx.x;
+  if (b >= blk[E]) return;
+  int lo = 0, hi = E;  // owner expert: the last e with blk[e] <= b
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (blk[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (b - blk[e]) * 128;
+  const int nr = min(128, offsets[e + 1] - r0);
+  const int cg = (tid & 15) * 8;
+  const int rg = tid >> 4;
+  float v[8][8];
+  float m[4][8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m[g][q] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rg + 16 * i;
+    if (r < nr) {
+      const int s = src_row ? src_row[r0 + r] : r0 + r;
+      load8<bf16_t>(src + (size_t)s * C + (size_t)cb * 128 + cg, v[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[i][q] = 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m[i >> 1][q] = fmaxf(m[i >> 1][q], fabsf(v[i][q]));
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) red[rg][g][cg + q] = m[g][q];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int id = k * 256 + tid;  // (g, c) pairs
+    const int g = id >> 7, c = id & 127;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, red[i][g][c]);
+    const int s = mx_exp(a);
+    sx[g][c] = a == 0.0f ? 1000 : s;  // 1000 marks an all-zero group
+    sbt[((size_t)cb * 128 + c) * (size_t)(ldt / 32) + (size_t)b * 4 + g] = (uint8_t)(s + 127);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = rg + 16 * i;
+      const int s = sx[i >> 1][cg + q];
+      const bool z = s == 1000 || r >= nr;
+      tt[cg + q][r] = (uint8_t)mx_code(v[i][q], z ? 1.0f : mx_inv(s), z);
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = codes_t + (size_t)cb * 128 * ldt + (size_t)b * 128;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int id = pass * 256 + tid;
+    const int c = id >> 3, r16 = (id & 7) * 16;
+    *(u32x4_t*)(dst + (size_t)c * ldt + r16) = *(const u32x4_t*)&tt[c][r16];
+  }
+}
+
 }  // namespace
+
+int quant_rows_mx_launch(const void* src, bool src_f32, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* sb, hipStream_t s) {
+  const int64_t nblk = rows * (cols / 32);
+  if (nblk == 0) return MOE_OK;
+  const int64_t grid = (nblk + 63) / 64;
+  if (src_f32)
+    quant_rows_mx_kernel<float><<<dim3((unsigned)grid), 256, 0, s>>>((const float*)src, nblk,
+                                                                      codes, sb);
+  else
+    quant_rows_mx_kernel<bf16_t><<<dim3((unsigned)grid), 256, 0, s>>>((const bf16_t*)src, nblk,
+                                                                       codes, sb);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
+                            uint8_t* sb, uint8_t* codes_t, uint8_t* sbt, hipStream_t s) {
+  if (E == 0) return MOE_OK;
+  quant_weights_mx_kernel<<<dim3((unsigned)(C / 128), (unsigned)(R / 128), (unsigned)E), 256, 0,
+                            s>>>(W, (int)R, (int)C, codes, sb, codes_t, sbt);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
+                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                           uint8_t* sbt, hipStream_t s) {
+  const int64_t nb = tokblk_max_blocks(P, E);
+  if (nb == 0) return MOE_OK;
+  quant_tokblk_mx_kernel<<<dim3((unsigned)nb, (unsigned)(C / 128)), 256, 0, s>>>(
+      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, nb * 128, codes_t, sbt);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
 
 int quant_rows_launch(const void* src, bool src_f32, int64_t rows, int64_t cols, uint8_t* codes,
                       float* scales, hipStream_t s) {

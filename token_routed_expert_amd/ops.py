@@ -48,7 +48,7 @@ def _check(status, call):
 
 
 def make_shape(T, d, E, k, f, f_shared=0, dtype="bf16") -> N.moe_shape:
-    code = {"f32": N.MOE_F32, "bf16": N.MOE_BF16, "e4m3": N.MOE_E4M3}[dtype]
+    code = {"f32": N.MOE_F32, "bf16": N.MOE_BF16, "e4m3": N.MOE_E4M3, "mxfp8": N.MOE_MXFP8}[dtype]
     return N.moe_shape(int(T), int(d), int(E), int(k), int(f), int(f_shared), code, 0)
 
 
@@ -166,6 +166,73 @@ def moe_grouped_gemm_bwd_e4m3(sh, offsets, token_of, x, ab, h, dO, wq: E4M3Weigh
            "moe_grouped_gemm_bwd_e4m3")
 
 
+U8 = torch.uint8
+
+
+def moe_quantize_rows_mx(src, codes, scales, stream=None):
+    """1 x 32 MXFP8 blocks along the rows of a bf16 or fp32 matrix (E8M0 scale bytes)."""
+    rows, cols = src.shape
+    code = {torch.bfloat16: N.MOE_BF16, torch.float32: N.MOE_F32}[src.dtype]
+    _check(N.lib().moe_quantize_rows_mx(_ptr(src), code, rows, cols, _ptr(codes, U8),
+                                        _ptr(scales, U8), _stream(stream)), "moe_quantize_rows_mx")
+
+
+def moe_quantize_weights_mx(W, codes, scales, codes_t, scales_t, stream=None):
+    """Both MXFP8 orientations of fp32 matrices W [E][R][C]."""
+    E, R, Cc = W.shape
+    _check(N.lib().moe_quantize_weights_mx(_ptr(W, F32), E, R, Cc, _ptr(codes, U8),
+                                           _ptr(scales, U8), _ptr(codes_t, U8),
+                                           _ptr(scales_t, U8), _stream(stream)),
+           "moe_quantize_weights_mx")
+
+
+def moe_quantize_token_blocks_mx(offsets, E, P, src, src_row, blk, codes_t, scales, stream=None):
+    """Per-expert token blocks with 32-row MXFP8 scale blocks, written transposed."""
+    Cc = src.shape[1]
+    _check(N.lib().moe_quantize_token_blocks_mx(_ptr(offsets, I32), int(E), int(P), _ptr(src),
+                                                _ptr(src_row, I32), Cc, _ptr(blk, I32),
+                                                _ptr(codes_t, U8), _ptr(scales, U8),
+                                                _stream(stream)), "moe_quantize_token_blocks_mx")
+
+
+def moe_permute_mx(sh, codes, scales, topk_idx, build_map, counts, offsets, row_of, token_of,
+                   dst_codes, dst_scales, ws, stream=None):
+    _check(N.lib().moe_permute_mx(C.byref(sh), _ptr(codes, U8), _ptr(scales, U8),
+                                  _ptr(topk_idx, I32), int(build_map), _ptr(counts, I32),
+                                  _ptr(offsets, I32), _ptr(row_of, I32), _ptr(token_of, I32),
+                                  _ptr(dst_codes, U8), _ptr(dst_scales, U8), _ptr(ws),
+                                  _nbytes(ws), _stream(stream)), "moe_permute_mx")
+
+
+class MXWeights:
+    """The moe_mx_weights struct over torch tensors (kept alive here)."""
+
+    NAMES = ("W1", "W3", "W2", "W1t", "W3t", "W2t", "W1s", "W3s", "W2s", "W1ts", "W3ts", "W2ts")
+
+    def __init__(self, tensors: dict):
+        self.tensors = {n: tensors[n] for n in self.NAMES}
+        self.struct = N.moe_mx_weights(*[_ptr(self.tensors[n], U8).value for n in self.NAMES])
+
+    def __getitem__(self, name):
+        return self.tensors[name]
+
+
+def moe_grouped_gemm_fwd_mx(sh, offsets, xpq, xps, w: MXWeights, ab, h, o, ws, stream=None):
+    _check(N.lib().moe_grouped_gemm_fwd_mx(C.byref(sh), _ptr(offsets, I32), _ptr(xpq, U8),
+                                           _ptr(xps, U8), C.byref(w.struct), _ptr(ab), _ptr(h),
+                                           _ptr(o), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_grouped_gemm_fwd_mx")
+
+
+def moe_grouped_gemm_bwd_mx(sh, offsets, token_of, x, ab, h, dO, w: MXWeights, dab, dXp, dW1, dW3,
+                            dW2, ws, stream=None):
+    _check(N.lib().moe_grouped_gemm_bwd_mx(C.byref(sh), _ptr(offsets, I32), _ptr(token_of, I32),
+                                           _ptr(x), _ptr(ab), _ptr(h), _ptr(dO), C.byref(w.struct),
+                                           _ptr(dab), _ptr(dXp), _ptr(dW1), _ptr(dW3), _ptr(dW2),
+                                           _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_grouped_gemm_bwd_mx")
+
+
 def _io(buffers: dict) -> N.moe_layer_io:
     io = N.moe_layer_io()
     for name in N.IO_FIELDS:
@@ -174,6 +241,9 @@ def _io(buffers: dict) -> N.moe_layer_io:
     wq = buffers.get("wq")
     if wq is not None:
         io.wq = C.cast(C.pointer(wq.struct), C.c_void_p).value
+    wmx = buffers.get("wmx")
+    if wmx is not None:
+        io.wmx = C.cast(C.pointer(wmx.struct), C.c_void_p).value
     io.aux_alpha = float(buffers.get("aux_alpha", 0.0))
     io.memory_efficient = int(buffers.get("memory_efficient", 0))
     return io
