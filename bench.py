@@ -31,7 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "e4m3": 5000.0, "mxfp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 METRIC = "MoE layer fwd+bwd TFLOPS/GPU & % MFMA peak; permute/combine HBM GB/s"
 
@@ -115,7 +115,7 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
     if router_grad:
         base = tre.moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
         rg = router_grad_calls(wl, sh, b, wsf[base:])
-    if wl.dtype == "e4m3":
+    if wl.dtype in ("e4m3", "mxfp8"):
         return build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg)
     shared = None
     if wl.f_shared:
@@ -217,15 +217,20 @@ def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg, memory_efficient):
 
 
 def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
-    """The e4m3 step: the expert weights are re-quantised from their fp32
-    masters (as after an optimizer step), x is quantised in 1 x 128 blocks
-    and its codes permuted; the GEMM calls quantise h, dO, [da|db] and the
-    weight-gradient token blocks themselves."""
+    """The fp8 step (e4m3 or MXFP8): the expert weights are re-quantised from
+    their fp32 masters (as after an optimizer step), x is quantised (1 x 128
+    blocks, MXFP8: 1 x 32) and its codes permuted; the GEMM calls quantise h,
+    dO, [da|db] and the weight-gradient token blocks themselves."""
     import token_routed_expert_amd as tre
     from token_routed_expert_amd.buffers import requantize_weights
     from token_routed_expert_amd import _native as N
 
-    wq = b["wq"]
+    mx = wl.dtype == "mxfp8"
+    wq = b["wmx"] if mx else b["wq"]
+    quant_rows = tre.moe_quantize_rows_mx if mx else tre.moe_quantize_rows
+    permute8 = tre.moe_permute_mx if mx else tre.moe_permute_e4m3
+    gemm_fwd8 = tre.moe_grouped_gemm_fwd_mx if mx else tre.moe_grouped_gemm_fwd_e4m3
+    gemm_bwd8 = tre.moe_grouped_gemm_bwd_mx if mx else tre.moe_grouped_gemm_bwd_e4m3
     pws = tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE)
     ws_perm = wsf[:max(256, pws)]
     ws_gf = wsf[pws:]
@@ -235,14 +240,14 @@ def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
         ev["start"].record()
         tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
         ev["route"].record()
-        tre.moe_quantize_rows(b["x"], b["xq"], b["xs"])
-        tre.moe_permute_e4m3(sh, b["xq"], b["xs"], b["topk_idx"], 1, b["counts"], b["offsets"],
+        quant_rows(b["x"], b["xq"], b["xs"])
+        permute8(sh, b["xq"], b["xs"], b["topk_idx"], 1, b["counts"], b["offsets"],
                              b["row_of"], b["token_of"], b["xpq"], b["xps"], ws_perm)
         ev["permute"].record()
         if rg:
             rg[0]()
         ev["aux_loss"].record()
-        tre.moe_grouped_gemm_fwd_e4m3(sh, b["offsets"], b["xpq"], b["xps"], wq, b["ab"], b["h"],
+        gemm_fwd8(sh, b["offsets"], b["xpq"], b["xps"], wq, b["ab"], b["h"],
                                       b["o"], ws_gf)
         ev["gemm_fwd"].record()
         tre.moe_unpermute(sh, b["o"], b["row_of"], b["topk_prob"], None, b["y"])
@@ -256,7 +261,7 @@ def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
         if rg:
             rg[2]()
         ev["route_bwd"].record()
-        tre.moe_grouped_gemm_bwd_e4m3(sh, b["offsets"], b["token_of"], b["x"], b["ab"], b["h"],
+        gemm_bwd8(sh, b["offsets"], b["token_of"], b["x"], b["ab"], b["h"],
                                       b["dO"], wq, b["dab"], b["dXp"], b["dW1"], b["dW3"],
                                       b["dW2"], wsb)
         ev["gemm_bwd"].record()
@@ -266,6 +271,24 @@ def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
         ev["quantize_weights"].record()
 
     return step
+
+
+def mx_expert_fwd_bwd(oracle, X, dO, W1, W3, W2):
+    """One expert's MXFP8 forward and backward with the oracle's functions."""
+    import numpy as np
+    one = np.array([0, X.shape[0]])
+    Wq = [oracle.quant_mx_weights(W[None]) for W in (W1, W3, W2)]
+    rowd = [oracle.dequant_mx_weights(q[0], q[1]) for q in Wq]
+    cold = [oracle.dequant_mx_weights(q[2], q[3]) for q in Wq]
+    xq, xs = oracle.quant_mx_rows(X)
+    a, b = oracle.fc1_fwd_mx(xq, xs, one, cold[0], cold[1])
+    h = oracle.silu(a) * b
+    oracle.fc2_fwd_mx(h, one, cold[2])
+    da, db = oracle.fc2_dgrad_mx(dO, a, b, one, rowd[2])
+    dab = np.concatenate([da, db], axis=1)
+    oracle.fc1_dgrad_mx(dab, one, rowd[0], rowd[1])
+    oracle.wgrad_mx(h, dO, one)
+    oracle.wgrad_mx(X, dab, one)
 
 
 def e4m3_expert_fwd_bwd(oracle, X, dO, W1, W3, W2):
@@ -317,10 +340,10 @@ def cpu_baseline(wl, inp, budget_s: float):
         toks = torch.from_numpy(token_of[r0:r1]).to(inp["x"].device)
         X = to_f64(inp["x"][toks])
         dO = p_rows[r0:r1, None] * to_f64(inp["dY"][toks])
-        if wl.dtype == "e4m3":
+        if wl.dtype in ("e4m3", "mxfp8"):
             Wm = [inp[n][e].cpu().numpy() for n in ("W1", "W3", "W2")]
             t0 = time.perf_counter()
-            e4m3_expert_fwd_bwd(oracle, X, dO, *Wm)
+            (mx_expert_fwd_bwd if wl.dtype == "mxfp8" else e4m3_expert_fwd_bwd)(oracle, X, dO, *Wm)
             t_exp += time.perf_counter() - t0
         else:
             W1, W3, W2 = (to_f64(inp[n][e]) for n in ("W1", "W3", "W2"))
@@ -338,7 +361,7 @@ def cpu_baseline(wl, inp, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle{' (e4m3 chain: quantise, dequantise, fp64 products)' if wl.dtype == 'e4m3' else ''}: "
+        "sample": (f"fp64 NumPy oracle{f' ({wl.dtype} chain: quantise, dequantise, fp64 products)' if wl.dtype in ('e4m3', 'mxfp8') else ''}: "
                    f"route + permutation map of all {wl.T} tokens "
                    f"({t_route:.2f} s), then SwiGLU fwd+bwd of experts 0..{n_exp - 1} "
                    f"({rows_done} of {wl.P} routed rows) in {t_exp:.1f} s; host has "
@@ -370,9 +393,9 @@ def main():
 
     import torch
 
-    from moe_workloads import WORKLOADS, make_inputs
+    from moe_workloads import VARIANTS, WORKLOADS, make_inputs
 
-    wl = WORKLOADS[args.workload]
+    wl = {**WORKLOADS, **VARIANTS}[args.workload]
     if wl.dtype not in MFMA_PEAK_TFLOPS:
         log(f"bench.py: workload {wl.name} ({wl.dtype}) is not supported by this build")
         sys.exit(2)
@@ -417,8 +440,9 @@ def main():
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     move_bytes = (wl.T * wl.d + wl.P * wl.d) * s          # bf16 / fp32 rows in and out
     perm_bytes = move_bytes
-    if wl.dtype == "e4m3":
+    if wl.dtype in ("e4m3", "mxfp8"):
         # quantise x (read bf16, write codes + scales), then move codes + scales
+        # (fp32 per 128 values or one byte per 32: the same count)
         qx = wl.T * wl.d * (2 + 1) + wl.T * (wl.d // 128) * 4
         perm_bytes = qx + (wl.T + wl.P) * (wl.d + (wl.d // 128) * 4)
     perm_gbs = (perm_bytes + 16 * wl.P) / (t_perm * 1e-3) / 1e9
@@ -438,8 +462,9 @@ def main():
         "data": "synthetic (seeded N(0,1) logits and activations, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "f": wl.f,
                    "f_shared": wl.f_shared},
-        "roofline": {"kernel": ("grouped GEMM (all fwd+bwd launches of a step)" if wl.dtype != "e4m3"
-                                else "e4m3 grouped-GEMM calls (fwd+bwd, with the h, dO, dab and "
+        "roofline": {"kernel": ("grouped GEMM (all fwd+bwd launches of a step)"
+                                if wl.dtype not in ("e4m3", "mxfp8")
+                                else f"{wl.dtype} grouped-GEMM calls (fwd+bwd, with the h, dO, dab and "
                                      "token-block quantisations they run)"), "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": gemm_traffic(wl),

@@ -471,7 +471,8 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
  *    data-gradient products), and transposed codes [E][C][R] with
  *    column-block bytes [E][C][R/32] (read by the forward products);
  *  - weight-gradient operands as moe_quantize_token_blocks lays them out,
- *    with bytes [C][ldt/32] (32-row blocks restart at each expert).
+ *    with bytes [ldt/128][C][4] (byte g of word (b, c): rows 32 g.. of
+ *    128-row block b; 32-row blocks restart at each expert).
  * Shapes: d, f multiples of 128, no shared expert.
  */
 
@@ -497,7 +498,8 @@ int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uin
 
 /* moe_quantize_token_blocks_mx -- as moe_quantize_token_blocks, with 32-row
  * scale blocks: codes_t [C][ldt] (ldt = 128 * capacity), scale bytes
- * [C][ldt/32]; blocks with no rows have s = 0. */
+ * [capacity][C][4] (the four 32-row blocks of each 128-row block and column
+ * in one word); blocks with no rows have s = 0. */
 int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
                                  const int32_t* src_row, int64_t C, int32_t* blk,
                                  uint8_t* codes_t, uint8_t* scales, void* stream);

@@ -107,15 +107,16 @@ def dequant_mx_weights(codes, sbytes):
 def quant_mx_token_blocks(X, offsets):
     """Weight-gradient operand X [P][C]: per column, 32-row blocks of each
     expert's rows (restarting at the expert's first row).  Returns codes_t
-    [C][128 cap] and scale bytes [C][4 cap] in the padded token-block layout
-    (cap = number of 128-row blocks, expert e from block blk[e] on); padding
-    codes are 0 and padding blocks have s = 0."""
+    [C][128 cap] in the padded token-block layout (cap = number of 128-row
+    blocks, expert e from block blk[e] on) and scale bytes [cap][C][4], byte
+    g of (b, c) for rows 32 g .. 32 g + 31 of block b; padding codes are 0 and
+    padding blocks have s = 0."""
     X = np.asarray(X, dtype=np.float32)
     P, C = X.shape
     blk = token_block_offsets(offsets, 128)
     cap = int(blk[-1])
     codes_t = np.zeros((C, 128 * cap), dtype=np.uint8)
-    sb_t = np.full((C, 4 * cap), 127, dtype=np.uint8)
+    sb_t = np.full((C, 4 * cap), 127, dtype=np.uint8)       # [C][32-row block]
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         m = r1 - r0
@@ -128,13 +129,14 @@ def quant_mx_token_blocks(X, offsets):
         c0 = 128 * int(blk[e])
         codes_t[:, c0:c0 + m] = codes.reshape(C, n32 * MX_BLOCK)[:, :m]
         sb_t[:, 4 * int(blk[e]):4 * int(blk[e]) + n32] = sb
-    return codes_t, sb_t
+    return codes_t, np.ascontiguousarray(sb_t.reshape(C, cap, 4).transpose(1, 0, 2))
 
 
 def dequant_mx_token_blocks(codes_t, sb_t, offsets):
-    """Values [P][C] of the token-block operand."""
+    """Values [P][C] of the token-block operand (scale bytes [cap][C][4])."""
     blk = token_block_offsets(offsets, 128)
     C = codes_t.shape[0]
+    sb_t = np.asarray(sb_t).transpose(1, 0, 2).reshape(C, -1)  # [C][32-row block]
     P = int(offsets[-1])
     out = np.zeros((P, C))
     vals = e4m3_decode(codes_t)

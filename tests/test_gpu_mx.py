@@ -93,7 +93,7 @@ def test_quantize_token_blocks_mx_bit_exact(gather):
     cap = tre.moe_token_block_capacity(P, E)
     blk = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     codes_t = torch.full((C, 128 * cap), 0xAB, dtype=torch.uint8, device="cuda")
-    sbt = torch.full((C, 4 * cap), 0xCD, dtype=torch.uint8, device="cuda")
+    sbt = torch.full((cap, C, 4), 0xCD, dtype=torch.uint8, device="cuda")
     tre.moe_quantize_token_blocks_mx(torch.from_numpy(off).cuda(), E, P, src.cuda(),
                                      None if src_row is None else torch.from_numpy(src_row).cuda(),
                                      blk, codes_t, sbt)
@@ -102,7 +102,7 @@ def test_quantize_token_blocks_mx_bit_exact(gather):
     NB = int(oracle.token_block_offsets(off)[-1])
     assert np.array_equal(blk.cpu().numpy(), oracle.token_block_offsets(off))
     assert np.array_equal(u8(codes_t)[:, :128 * NB], rq)
-    assert np.array_equal(u8(sbt)[:, :4 * NB], rs)
+    assert np.array_equal(u8(sbt)[:NB], rs)
 
 
 def test_permute_mx_bit_exact():

@@ -118,10 +118,11 @@ def test_token_block_layout():
     off = small_offsets()
     P, C = int(off[-1]), 64
     X = RNG.standard_normal((P, C)).astype(np.float32)
-    qt, sbt = quant_mx_token_blocks(X, off)
+    qt, sbw = quant_mx_token_blocks(X, off)
     blk = token_block_offsets(off, 128)
     cap = int(blk[-1])
-    assert qt.shape == (C, 128 * cap) and sbt.shape == (C, 4 * cap)
+    assert qt.shape == (C, 128 * cap) and sbw.shape == (cap, C, 4)
+    sbt = sbw.transpose(1, 0, 2).reshape(C, 4 * cap)         # [C][32-row block]
     for e in range(len(off) - 1):
         r0, r1 = int(off[e]), int(off[e + 1])
         c0 = 128 * int(blk[e])
@@ -140,7 +141,7 @@ def test_token_block_layout():
                 assert sbt[c, 4 * int(blk[e]) + g] == s1[0, 0]
                 assert np.array_equal(qt[c, c0 + 32 * g:c0 + 32 * g + n], c1[0, :n])
                 assert (qt[c, c0 + 32 * g + n:c0 + 32 * g + 32] == 0).all()
-    D = dequant_mx_token_blocks(qt, sbt, off)
+    D = dequant_mx_token_blocks(qt, sbw, off)
     assert np.abs(D - X).max() <= np.abs(X).max() * 2.0 ** -4
 
 

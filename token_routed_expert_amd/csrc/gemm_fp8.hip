@@ -99,7 +99,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
   // weight-gradient products: per stage the 256 A-row and 256 B-column scales
-  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][MX ? 4 : 256];
+  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][256];
   __shared__ int sched[NW + 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
@@ -193,16 +193,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // weight gradients: the stage's scale rows ([NB][M] and [NB][N], 256
   // consecutive floats each) go to LDS with one DMA instruction each
   // (wavefronts 0 and 1); rows past the matrix read as zero.
+  // (MXFP8: the same 4 bytes per block and row, holding the four 32-row E8M0 scales)
   rsrc_t sca_src, scb_src;
-  if constexpr (WGRAD && !MX) {
+  if constexpr (WGRAD) {
     const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
-    sca_src = make_rsrc(args.a_s + (size_t)kb0 * Mt + ti.m0, (uint32_t)((K / BK) * Mt - ti.m0) * 4u);
-    scb_src = make_rsrc(args.b_s + (size_t)kb0 * N + ti.n0, (uint32_t)((K / BK) * N - ti.n0) * 4u);
+    const float* as = MX ? (const float*)args.a_sx : args.a_s;
+    const float* bs = MX ? (const float*)args.b_sx : args.b_s;
+    sca_src = make_rsrc(as + (size_t)kb0 * Mt + ti.m0, (uint32_t)((K / BK) * Mt - ti.m0) * 4u);
+    scb_src = make_rsrc(bs + (size_t)kb0 * N + ti.n0, (uint32_t)((K / BK) * N - ti.n0) * 4u);
   }
   auto issue_stage = [&](int kt) __attribute__((always_inline)) {
     const uint32_t st = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
     const uint32_t ka = (uint32_t)kt * BK;
-    if constexpr (WGRAD && !MX) {
+    if constexpr (WGRAD) {
       const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
       const uint32_t sc = sc_base + (uint32_t)((kt & (NSTAGE - 1)) * 2048);
       if (wid == 0) dma16(sca_src, (uint32_t)kt * (uint32_t)Mt * 4u + (uint32_t)lane * 16u, sc);
@@ -242,8 +245,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 
   if constexpr (MX) {
     // ------------------------------------------------------------ MXFP8 scales
+    // ragged products: buffer loads of the lane's rows' words, one stage
+    // ahead; weight gradients: the stage's words for the tile's 256 A rows and
+    // 256 B rows arrive in sc_lds with the stage's codes (issue_stage).
     __amdgpu_buffer_rsrc_t xa, xb, xb2;
-    uint32_t xa_ld, xb_ld;
+    uint32_t xa_ld = 0, xb_ld = 0;
     if constexpr (RAGGED) {
       xa_ld = (uint32_t)(K / 32);
       xa = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_sx + (size_t)ti.row0 * xa_ld), 0,
@@ -265,31 +271,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
                 ? __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_sx2 + b0), 0,
                                                     brows * (int)xb_ld, 0x00020000)
                 : xb;
-    } else {
-      xa_ld = xb_ld = (uint32_t)(args.ldt / 32);
-      xa = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(args.a_sx + (size_t)ti.m0 * xa_ld + (size_t)kb0 * 4), 0,
-          (M - ti.m0) * (int)xa_ld - kb0 * 4, 0x00020000);
-      xb = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(args.b_sx + (size_t)ti.n0 * xb_ld + (size_t)kb0 * 4), 0,
-          (N - ti.n0) * (int)xb_ld - kb0 * 4, 0x00020000);
-      xb2 = xb;
     }
     auto load_scales = [&](int kt, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
         __attribute__((always_inline)) {
+      if constexpr (RAGGED) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        sa[i] = buf_u32(xa, (uint32_t)(wm * WM + 16 * i + lm) * xa_ld + (uint32_t)kt * 4u);
+        for (int i = 0; i < FM; ++i)
+          sa[i] = buf_u32(xa, (uint32_t)(wm * WM + 16 * i + lm) * xa_ld + (uint32_t)kt * 4u);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (OP == OP_FC1_FWD) {
-          sb[j] = buf_u32(j < FN / 2 ? xb : xb2, (uint32_t)(b_row(j) & 127) * xb_ld + (uint32_t)kt * 4u);
-        } else if constexpr (OP == OP_FC1_DGRAD) {
-          const int fb = f / 128;
-          sb[j] = buf_u32(kt < fb ? xb : xb2,
-                          (uint32_t)b_row(j) * xb_ld + (uint32_t)(kt < fb ? kt : kt - fb) * 4u);
-        } else {
-          sb[j] = buf_u32(xb, (uint32_t)b_row(j) * xb_ld + (uint32_t)kt * 4u);
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (OP == OP_FC1_FWD) {
+            sb[j] = buf_u32(j < FN / 2 ? xb : xb2,
+                            (uint32_t)(b_row(j) & 127) * xb_ld + (uint32_t)kt * 4u);
+          } else if constexpr (OP == OP_FC1_DGRAD) {
+            const int fb = f / 128;
+            sb[j] = buf_u32(kt < fb ? xb : xb2,
+                            (uint32_t)b_row(j) * xb_ld + (uint32_t)(kt < fb ? kt : kt - fb) * 4u);
+          } else {
+            sb[j] = buf_u32(xb, (uint32_t)b_row(j) * xb_ld + (uint32_t)kt * 4u);
+          }
         }
       }
     };
@@ -307,6 +307,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         load_scales(kt + 1, sa_n, sb_n);
         issue_stage(kt + 1);
       }
+      if constexpr (WGRAD) {
+        const uint32_t* sct = (const uint32_t*)&sc_lds[kt & (NSTAGE - 1)][0][0];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa[i] = sct[wm * WM + 16 * i + lm];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb[j] = sct[256 + b_row(j)];
+      }
       i32x8_t bf[FN];
       int sbb[FN];
       static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
@@ -314,23 +321,33 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         bf[J.value] = lds_frag_mx(cur + OPND_BYTES + r * BK, lg, swz(r));
         sbb[J.value] = (int)((sb[J.value] >> sh8) & 0xffu);
       });
+      // the next row's A fragment is read while this row's MFMAs run
+      i32x8_t af = lds_frag_mx(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
       static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = I.value;
-        const int r = wm * WM + 16 * i + lm;
-        const i32x8_t af = lds_frag_mx(cur + r * BK, lg, swz(r));
+        i32x8_t af_next;
+        if constexpr (i + 1 < FM) {
+          const int r = wm * WM + 16 * (i + 1) + lm;
+          af_next = lds_frag_mx(cur + r * BK, lg, swz(r));
+        }
         const int sab = (int)((sa[i] >> sh8) & 0xffu);
+        __builtin_amdgcn_sched_barrier(0);
         static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
           constexpr int j = J.value;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0,
                                                                          0, sbb[j], 0, sab);
         });
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i + 1 < FM) af = af_next;
       });
       wait_vmcnt<0>();
       block_barrier();
+      if constexpr (RAGGED) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
+        for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
+        for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
+      }
     }
     store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
     return;

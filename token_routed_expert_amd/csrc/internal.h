@@ -89,9 +89,10 @@ struct GemmArgs {
   float* dp_part;
   // MXFP8 products (gemm_fp8.hip with E8M0 scales): the same code operands as
   // e4m3, with one scale byte per 32 contraction values, stored row-major per
-  // operand row: A rows [.][K/32] (wgrad: [M][ldt/32]); B: the byte array of
-  // each weight matrix in the orientation read ([E][n][K/32]; fc1 forward and
-  // fc1 dgrad use b_sx2 for W3), wgrad [N][ldt/32].
+  // operand row: A rows [.][K/32]; B: the byte array of each weight matrix in
+  // the orientation read ([E][n][K/32]; fc1 forward and fc1 dgrad use b_sx2
+  // for W3).  Weight gradients: words [ldt/128][M] and [ldt/128][N], the four
+  // 32-row scales of each 128-row token block and column.
   const uint8_t* a_sx;
   const uint8_t* b_sx;
   const uint8_t* b_sx2;

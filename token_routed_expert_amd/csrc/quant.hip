@@ -390,9 +390,11 @@ __global__ __launch_bounds__(256) void quant_weights_mx_kernel(
 
 // Token blocks in MX form: as quant_tokblk_kernel, with four 32-row scale
 // blocks per column in each 128-row block.  codes_t [C][ldt] as there; scale
-// bytes sbt [C][ldt / 32], byte 4 b + g for rows 32 g .. 32 g + 31 of block b
-// (groups past the expert's rows: s = 0).  Thread rg = tid / 16 holds rows
-// rg + 16 i (i < 8), which lie in group i / 2.
+// bytes sbt [ldt / 128][C][4]: byte g of word (b, c) for rows 32 g .. 32 g + 31
+// of block b (groups past the expert's rows: s = 0) -- one 4-byte word per
+// (block, column), block-major like the e4m3 token-block scales, so a GEMM
+// stage's words for 256 columns are 1 KB in a row.  Thread rg = tid / 16 holds
+// rows rg + 16 i (i < 8), which lie in group i / 2.
 __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
     for (int i = 0; i < 16; ++i) a = fmaxf(a, red[i][g][c]);
     const int s = mx_exp(a);
     sx[g][c] = a == 0.0f ? 1000 : s;  // 1000 marks an all-zero group
-    sbt[((size_t)cb * 128 + c) * (size_t)(ldt / 32) + (size_t)b * 4 + g] = (uint8_t)(s + 127);
+    sbt[((size_t)b * C + (size_t)cb * 128 + c) * 4 + g] = (uint8_t)(s + 127);
   }
   __syncthreads();
 #pragma unroll
