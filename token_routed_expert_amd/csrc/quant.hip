@@ -35,20 +35,13 @@ constexpr float kE4M3Max = 448.0f;
 // E4M3FN code of a finite fp32 value, from the format: sign bit, 4 exponent
 // bits with bias 7, 3 mantissa bits; normals from 2^-6 to 448, subnormals
 // m * 2^-9.  Round to nearest, ties to even; |v| >= 448 gives 448 (0x7e).
+// gfx950's v_cvt_pk_fp8_f32 produces exactly these codes for |v| < 464 (a
+// comparison over every fp32 value of magnitude below 2^9, both signs,
+// subnormals and ties included) and NaN above, so the value is clamped to
+// +-448 first (the sign of -0 is kept).
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t mag;
-  if (a >= 0x43e00000u) {          // |v| >= 448
-    mag = 0x7eu;
-  } else if (a >= 0x3c800000u) {  // 2^-6 <= |v| < 448: keep 3 mantissa bits
-    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // ties to even at bit 20
-    mag = (r >> 20) - (120u << 3);                       // exponent bias 127 -> 7
-  } else {                         // below the normal range: multiples of 2^-9
-    mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);  // exact scaling, then RNE
-  }
-  return sign | mag;
+  const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xffu;
 }
 
 __device__ __forceinline__ float block_scale(float amax) {
