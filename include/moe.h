@@ -207,7 +207,7 @@ typedef struct {
   float* dprob;                           /* [T][k] */
   float* dlogits;                         /* [T][E] */
   float aux_alpha;                        /* coefficient alpha of the loss; 0 = none */
-  /* memory-efficient permutation (bf16 layers): when memory_efficient != 0
+  /* memory-efficient permutation (bf16, e4m3, MXFP8): when memory_efficient != 0
      the probabilities are applied before W2 (h and o hold p-scaled values),
      the backward reads neither o nor a scaled dO, and row_prob [P] (written
      by the forward, read by the backward) holds each permuted row's
@@ -230,9 +230,10 @@ typedef struct {
  * moe_grouped_gemm_fwd_e4m3, moe_unpermute (MOE_MXFP8: the _mx calls, weights
  * io->wmx).  With io->aux_loss set, also
  * moe_aux_loss (alpha = io->aux_alpha) after the permutation; ws_bytes then
- * needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient (bf16):
- * moe_row_probs into io->row_prob, moe_grouped_gemm_fwd_rowscaled and an
- * unweighted moe_unpermute.
+ * needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient:
+ * moe_row_probs into io->row_prob, the row-scaled expert forward (bf16:
+ * moe_grouped_gemm_fwd_rowscaled; e4m3 / MXFP8: fc1's epilogue scales h by p
+ * before h is quantised) and an unweighted moe_unpermute.
  */
 int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -247,7 +248,8 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
  * MOE_E4M3 the expert backward is moe_grouped_gemm_bwd_e4m3.  With
  * io->memory_efficient: dO = dY permuted without scaling, then
  * moe_grouped_gemm_bwd_rowscaled (io->o is not read; dprob comes from its
- * partials); ws_bytes >= moe_workspace_bytes(sh, MOE_WS_LAYER_BWD_ROWSCALED).
+ * partials; e4m3 and MXFP8 layers run the same steps with their products);
+ * ws_bytes >= moe_workspace_bytes(sh, MOE_WS_LAYER_BWD_ROWSCALED).
  */
 int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                   void* stream);
@@ -412,7 +414,9 @@ int moe_route_bwd(const float* logits, int64_t T, int64_t E, int64_t k, const in
  * epilogue, the combine is an unweighted sum, and the backward needs neither
  * the expert outputs o nor a scaled dO: with dh' = dY[t] W2^T (unscaled
  * rows), dh = p dh' and dp = <h, dh'>, taken in the fc2 dgrad epilogue.
- * Results equal the plain layer's up to rounding.  bf16 only.
+ * Results equal the plain layer's up to rounding.  The stand-alone row-scaled
+ * GEMM calls below are bf16; e4m3 and MXFP8 layers take the same form through
+ * moe_layer_fwd / moe_layer_bwd (io->memory_efficient).
  */
 
 /*

@@ -200,3 +200,10 @@ def test_layer_memory_efficient_validation():
     assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_INVALID
     sh = make_shape(64, 256, 8, 2, 256, 0, "f32")
     assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
+
+
+def test_fp8_memory_efficient_workspace():
+    for dtype in ("e4m3", "mxfp8"):
+        sh = make_shape(64, 256, 8, 2, 256, 0, dtype)
+        assert moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD_ROWSCALED) == \
+            moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD) + -(-128 * 1 * 4 // 256) * 256

@@ -175,3 +175,105 @@ def test_rowscaled_entry_points():
                          ids=lambda w: w.name)
 def test_memory_efficient_full_size_sampled(wl):
     full_size_sampled(wl, memory_efficient=2)
+
+
+# ---------------------------------------------------------------- e4m3 and MXFP8 layers
+def fp8_ops(dtype):
+    """The oracle's product functions of one fp8 recipe and the dequantised
+    weights (forward orientation, data-gradient orientation) of the device's
+    quantised weights, which the quantiser tests prove equal to the oracle's."""
+    if dtype == "e4m3":
+        return (oracle.quant_rows, oracle.dequant_rows, oracle.fc1_fwd_e4m3, oracle.fc2_fwd_e4m3,
+                oracle.fc2_dgrad_e4m3, oracle.fc1_dgrad_e4m3, oracle.wgrad_e4m3)
+    return (oracle.quant_mx_rows, oracle.dequant_mx_rows, oracle.fc1_fwd_mx, oracle.fc2_fwd_mx,
+            oracle.fc2_dgrad_mx, oracle.fc1_dgrad_mx, oracle.wgrad_mx)
+
+
+def fp8_weights(dtype, inp):
+    fwd, bwd = {}, {}
+    for n in ("W1", "W3", "W2"):
+        W = inp[n].cpu().numpy()
+        if dtype == "e4m3":
+            q, s_ = oracle.quant_expert_weights(W)
+            fwd[n] = bwd[n] = oracle.dequant_expert_weights(q, s_)
+        else:
+            q, s_, qt, st_ = oracle.quant_mx_weights(W)
+            bwd[n] = oracle.dequant_mx_weights(q, s_)
+            fwd[n] = oracle.dequant_mx_weights(qt, st_)
+    return fwd, bwd
+
+
+FP8_ME = [Workload("me_e4m3", T=700, d=384, E=16, k=4, f=256, dtype="e4m3", skew=True),
+          Workload("me_mxfp8", T=700, d=384, E=16, k=4, f=256, dtype="mxfp8", skew=True),
+          Workload("me_mxfp8_ragged", T=301, d=256, E=8, k=2, f=384, dtype="mxfp8")]
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["keep_h", "recompute_h"])
+@pytest.mark.parametrize("wl", FP8_ME, ids=lambda w: w.name)
+def test_fp8_layer_memory_efficient(wl, mode):
+    """Each product of the memory-efficient fp8 layer against the oracle on the
+    device's own stored intermediates: h = p silu(a) b, o = Q(h) W2, y the
+    unweighted combine, dO the unscaled permutation of dY, [da|db] p times the
+    SwiGLU backward of Q(dO) W2^T, dXp, dX, the weight gradients, and dprob
+    = <silu(a) b, Q(dO) W2^T> (o poisoned between forward and backward)."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd.buffers import layer_buffers
+    from test_gpu_e4m3 import TOL8
+    inp = make_inputs(wl, seed=6, device="cuda")
+    sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, 0, wl.dtype, "cuda", inp,
+                                    router_grad=True, aux_alpha=0.01, memory_efficient=mode)
+    tre.moe_layer_fwd(sh, b, wsf)
+    h_fwd = b["h"].clone()
+    b["o_saved"] = b["o"].clone()
+    b["o"].fill_(float("nan"))
+    if mode == 2:
+        b["h"].fill_(float("nan"))
+    tre.moe_layer_bwd(sh, b, wsb)
+    torch.cuda.synchronize()
+    quant_rows, dequant_rows, fc1, fc2, fc2_dgrad, fc1_dgrad, wgrad = fp8_ops(wl.dtype)
+    L = inp["logits"].cpu().numpy()
+    idx, p = oracle.route(L, wl.k)
+    counts, off, row_of, token_of = oracle.permute_map(idx, wl.E)
+    assert np.array_equal(b["row_of"].cpu().numpy(), row_of)
+    pr = p.reshape(-1)[np.argsort(row_of.reshape(-1))]
+    Wf, Wb = fp8_weights(wl.dtype, inp)
+    f = wl.f
+    xpq = b["xpq"].cpu().numpy()
+    xps = b["xps"].cpu().numpy()
+    a_r, b_r = fc1(xpq, xps, off, Wf["W1"], Wf["W3"])
+    ab = to_f64(b["ab"]); a_g, b_g = ab[:, :f], ab[:, f:]
+    assert_close("a", a_g, a_r, TOL8)
+    h_g = to_f64(h_fwd)
+    assert_close("p h", h_g, pr[:, None] * oracle.silu(a_r) * b_r, TOL8)
+    o_g = to_f64(b["o_saved"])
+    assert_close("o", o_g, fc2(h_g, off, Wf["W2"]), TOL8)
+    assert_close("y", to_f64(b["y"]), oracle.combine(o_g, row_of), TOL8)
+    assert torch.equal(b["dO"], inp["dY"][torch.from_numpy(token_of).cuda()])
+    dO_g = to_f64(b["dO"])
+    da_r, db_r = fc2_dgrad(dO_g, a_g, b_g, off, Wb["W2"])
+    dab_g = to_f64(b["dab"])
+    assert_close("da", dab_g[:, :f], pr[:, None] * da_r, TOL8)
+    assert_close("db", dab_g[:, f:], pr[:, None] * db_r, TOL8)
+    assert_close("dXp", to_f64(b["dXp"]), fc1_dgrad(dab_g, off, Wb["W1"], Wb["W3"]), TOL8)
+    assert_close("dX", to_f64(b["dX"]), oracle.combine(to_f64(b["dXp"]), row_of), TOL8)
+    h_w = to_f64(b["h"]) if mode == 2 else h_g            # the h the fc2 weight gradient read
+    if mode == 2:
+        assert_close("recomputed p h", h_w, pr[:, None] * oracle.silu(a_g) * b_g, TOL8)
+    assert_close("dW2", to_f64(b["dW2"]), wgrad(h_w, dO_g, off), TOL8)
+    dW13 = wgrad(to_f64(inp["x"])[token_of], dab_g, off)
+    assert_close("dW1", to_f64(b["dW1"]), dW13[:, :, :f], TOL8)
+    assert_close("dW3", to_f64(b["dW3"]), dW13[:, :, f:], TOL8)
+    # dprob = <silu(a) b, Q(dO) W2^T> from the stored a, b
+    G = dequant_rows(*quant_rows(dO_g))
+    dH = np.zeros((wl.P, f))
+    for e in range(wl.E):
+        R = slice(int(off[e]), int(off[e + 1]))
+        dH[R] = G[R] @ Wb["W2"][e].T
+    hh = oracle.silu(a_g) * b_g
+    dp_rows = (hh * dH).sum(1)
+    mag = np.abs(hh * dH).sum(1)
+    dp = b["dprob"].cpu().numpy().astype(np.float64)
+    err = np.abs(dp - dp_rows[row_of])
+    assert (err <= 1e-4 * mag[row_of] + 1e-30).all(), f"dprob worst {(err / mag[row_of]).max():.3e}"
+    ref = oracle.router_bwd(dp, p, idx, wl.E) + oracle.aux_loss(L, counts, wl.k, 0.01)[1]
+    assert_close("dlogits", b["dlogits"].cpu().numpy().astype(np.float64), ref, 1e-4)

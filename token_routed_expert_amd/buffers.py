@@ -15,7 +15,7 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
     router_grad: also the load-balancing loss (coefficient aux_alpha) and the
     router gradient (aux_loss, dprob, dlogits).
-    memory_efficient: probabilities applied before W2 (bf16; row_prob [P]);
+    memory_efficient: probabilities applied before W2 (row_prob [P]);
     2 also recomputes h in the backward.
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """

@@ -89,7 +89,9 @@ __device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t o
 // scales go straight into the MFMA, which accumulates in place: no promotion.
 // A lane's scale byte for fragment row r and stage kt is byte (lane >> 4) of
 // the word at r * ld + 4 kt.
-template <int OP, bool MX>
+// RS: row-scaled epilogues (probabilities applied before W2; fc1 forward and
+// fc2 dgrad only), as in the bf16 kernels.
+template <int OP, bool MX, bool RS>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // weight-gradient products: per stage the 256 A-row and 256 B-column scales
   __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][256];
   __shared__ int sched[NW + 4];
+  __shared__ float dp_red[RS ? (NW / 2) * 256 : 1];  // row-scaled fc2 dgrad: <h, dh'> partials
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         for (int j = 0; j < FN; ++j) sb[j] = sb_n[j];
       }
     }
-    store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
+    store_tile<OP, FM, FN, WM, WN, RAGGED, RS>(args, acc, ti, M, N, wm, wn, lane, dp_red);
     return;
   }
 
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   }
 
   // ---------------------------------------------------------------- epilogue
-  store_tile<OP, FM, FN, WM, WN, RAGGED>(args, acc, ti, M, N, wm, wn, lane);
+  store_tile<OP, FM, FN, WM, WN, RAGGED, RS>(args, acc, ti, M, N, wm, wn, lane, dp_red);
 }
 
 template <int OP, bool MX>
@@ -493,7 +496,14 @@ int launch(const GemmArgs& a, hipStream_t s) {
     grid = (int64_t)a.E * MT * NT;
   }
   if (grid == 0) return MOE_OK;
-  gemm_fp8_kernel<OP, MX><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+  bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
+  if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
+    if (a.row_prob) {
+      gemm_fp8_kernel<OP, MX, true><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+      scaled = true;
+    }
+  }
+  if (!scaled) gemm_fp8_kernel<OP, MX, false><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

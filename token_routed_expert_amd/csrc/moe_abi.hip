@@ -210,9 +210,10 @@ size_t dp_part_bytes(const moe_shape* sh) {
 int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream);
 
 // Expert forward of the fp8 products (e4m3 or MXFP8); arguments checked by the caller.
+// row_prob != NULL: the memory-efficient form, h = p silu(a) b.
 int gemm_fwd8(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq, const void* xps,
               const Wq8& w, void* ab, void* h, void* o, void* ws, size_t ws_bytes, void* stream,
-              bool mx) {
+              bool mx, const float* row_prob = nullptr) {
   int st;
   size_t need;
   Fwd8Ws W = carve_fwd8(sh, ws, &need);
@@ -223,7 +224,9 @@ int gemm_fwd8(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq, c
   a.a_q = xpq; set_a_scales(a, xps, mx);
   a.b_q = w.W1t; a.b_q2 = w.W3t; set_b_scales(a, w.s1t, w.s3t, mx);
   a.ab_out = ab; a.h_out = h;
+  a.row_prob = row_prob;
   if ((st = gemm8(OP_FC1_FWD, a, s, mx))) return st;
+  a.row_prob = nullptr;
   if ((st = qrows8(h, P, sh->f, W.hq, W.hs, s, mx))) return st;
   a.a_q = W.hq; set_a_scales(a, W.hs, mx);
   a.b_q = w.W2t; a.b_q2 = nullptr; set_b_scales(a, w.s2t, nullptr, mx);
@@ -233,9 +236,13 @@ int gemm_fwd8(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq, c
 
 
 // Expert backward of the fp8 products (e4m3 or MXFP8); arguments checked by the caller.
+// row_prob != NULL: the memory-efficient form (dO unscaled; fc2 dgrad scales
+// dh by p and writes its <h, dh'> partials to dp_part; with recompute_h it
+// also refills h = p silu(a) b for the fc2 weight gradient).
 int gemm_bwd8(const moe_shape* sh, const int32_t* offsets, const int32_t* token_of, const void* x,
               const void* ab, const void* h, const void* dO, const Wq8& w, void* dab, void* dXp,
-              void* dW1, void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream, bool mx) {
+              void* dW1, void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream, bool mx,
+              const float* row_prob = nullptr, float* dp_part = nullptr, bool recompute_h = false) {
   int st;
   size_t need;
   Bwd8Ws W = carve_bwd8(sh, ws, &need);
@@ -248,7 +255,12 @@ int gemm_bwd8(const moe_shape* sh, const int32_t* offsets, const int32_t* token_
   if ((st = qrows8(dO, P, d, W.dOq, W.dOs, s, mx))) return st;
   a.a_q = W.dOq; set_a_scales(a, W.dOs, mx); a.b_q = w.W2; set_b_scales(a, w.s2, nullptr, mx);
   a.ab = ab; a.dab_out = dab;
+  a.row_prob = row_prob;
+  a.dp_part = dp_part;
+  a.h_out = row_prob && recompute_h ? (void*)h : nullptr;
   if ((st = gemm8(OP_FC2_DGRAD, a, s, mx))) return st;
+  a.row_prob = nullptr;
+  a.h_out = nullptr;
   if ((st = qrows8(dab, P, 2 * f, W.dabq, W.dabs, s, mx))) return st;
   a.a_q = W.dabq; set_a_scales(a, W.dabs, mx);
   a.b_q = w.W1; a.b_q2 = w.W3; set_b_scales(a, w.s1, w.s3, mx);
@@ -296,6 +308,7 @@ size_t moe_workspace_bytes(const moe_shape* sh, int kind) {
       case MOE_WS_GEMM_BWD: return bwd8_ws_bytes(sh);
       case MOE_WS_LAYER_FWD: return permute_ws_bytes(sh->T, sh->E) + fwd8_ws_bytes(sh);
       case MOE_WS_LAYER_BWD: return bwd8_ws_bytes(sh);
+      case MOE_WS_LAYER_BWD_ROWSCALED: return bwd8_ws_bytes(sh) + dp_part_bytes(sh);
     }
     return 0;
   }
@@ -632,10 +645,7 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (is_fp8(sh)) {
-    if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
-    return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
-  }
+  if (is_fp8(sh)) return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
   if (io && io->memory_efficient) return layer_fwd_rowscaled(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
@@ -677,10 +687,7 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
                   void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (is_fp8(sh)) {
-    if (io && io->memory_efficient) return MOE_ERR_UNSUPPORTED;
-    return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
-  }
+  if (is_fp8(sh)) return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
   if (io && io->memory_efficient) return layer_bwd_rowscaled(sh, io, ws, ws_bytes, stream);
   if ((st = check_gemm_dims(sh, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
@@ -731,6 +738,8 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
       !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xq || !io->xs ||
       !io->xpq || !io->xps || !io->ab || !io->h || !io->o || !io->y)
     return MOE_ERR_INVALID;
+  const bool me = io->memory_efficient != 0;  // probabilities applied before W2
+  if (me && !io->row_prob) return MOE_ERR_INVALID;
   const size_t pws = permute_ws_bytes(sh->T, sh->E);
   const size_t gws = fwd8_ws_bytes(sh);
   if (!ws || ws_bytes < pws + gws || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
@@ -744,10 +753,14 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
                              io->row_of, io->token_of, io->xpq, io->xps, ws, pws, stream)))
     return st;
   if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
+  if (me && (st = moe_row_probs(sh, io->row_of, io->topk_prob, io->row_prob, stream))) return st;
   if ((st = gemm_fwd8(sh, io->offsets, io->xpq, io->xps, mx ? wq8_of(io->wmx) : wq8_of(io->wq),
-                      io->ab, io->h, io->o, (char*)ws + pws, gws, stream, mx)))
+                      io->ab, io->h, io->o, (char*)ws + pws, gws, stream, mx,
+                      me ? io->row_prob : nullptr)))
     return st;
-  return moe_unpermute(sh, io->o, io->row_of, io->topk_prob, nullptr, io->y, stream);
+  // memory-efficient: o rows already carry their probability
+  return moe_unpermute(sh, io->o, io->row_of, me ? nullptr : io->topk_prob, nullptr, io->y,
+                       stream);
 }
 
 int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
@@ -760,13 +773,38 @@ int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
       !io->row_of || !io->token_of || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp ||
       !io->dX || !io->dW1 || !io->dW3 || !io->dW2)
     return MOE_ERR_INVALID;
-  if (!ws || ws_bytes < bwd8_ws_bytes(sh)) return MOE_ERR_WORKSPACE;
-  if ((st = layer_combine_bwd(sh, io, stream))) return st;
+  const bool me = io->memory_efficient != 0;  // probabilities applied before W2
+  const size_t gws = bwd8_ws_bytes(sh);
+  if (!me) {
+    if (!ws || ws_bytes < gws) return MOE_ERR_WORKSPACE;
+    if ((st = layer_combine_bwd(sh, io, stream))) return st;
+    if ((st = gemm_bwd8(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
+                        mx ? wq8_of(io->wmx) : wq8_of(io->wq), io->dab, io->dXp, io->dW1, io->dW3,
+                        io->dW2, ws, ws_bytes, stream, mx)))
+      return st;
+    return moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream);
+  }
+  if (!io->row_prob) return MOE_ERR_INVALID;
+  if (io->dlogits && (!io->dprob || !io->logits || !io->topk_idx || !io->counts))
+    return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < gws + dp_part_bytes(sh)) return MOE_ERR_WORKSPACE;
+  float* dp_part = (float*)((char*)ws + gws);
+  // dO = dY permuted, unscaled; the fc2 dgrad epilogue yields the dprob partials
+  if ((st = moe_permute(sh, io->dY, nullptr, nullptr, 0, nullptr, nullptr, io->row_of, nullptr,
+                        io->dO, nullptr, 0, stream)))
+    return st;
   if ((st = gemm_bwd8(sh, io->offsets, io->token_of, io->x, io->ab, io->h, io->dO,
                       mx ? wq8_of(io->wmx) : wq8_of(io->wq), io->dab, io->dXp, io->dW1, io->dW3,
-                      io->dW2, ws, ws_bytes, stream, mx)))
+                      io->dW2, ws, gws, stream, mx, io->row_prob, dp_part,
+                      io->memory_efficient == 2)))
     return st;
-  return moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream);
+  if ((st = moe_unpermute(sh, io->dXp, io->row_of, nullptr, nullptr, io->dX, stream))) return st;
+  if (!io->dlogits) return MOE_OK;
+  if ((st = dp_rows_launch(dp_part, (int)((sh->f + 255) / 256), io->row_of,
+                           (int)(sh->T * sh->k), io->dprob, (hipStream_t)stream)))
+    return st;
+  return moe_route_bwd(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, io->dprob,
+                       io->counts, io->aux_alpha, 1.0f, io->dlogits, stream);
 }
 
 }  // namespace
