@@ -116,6 +116,8 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
         base = tre.moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
         rg = router_grad_calls(wl, sh, b, wsf[base:])
     if wl.dtype in ("e4m3", "mxfp8"):
+        if memory_efficient:
+            return build_step_layer(wl, inp, sh, b, wsf, wsb)
         return build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg)
     shared = None
     if wl.f_shared:
@@ -163,6 +165,33 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
         ev["gemm_bwd"].record()
         tre.moe_unpermute(sh, b["dXp"], b["row_of"], None, b.get("dXs"), b["dX"])
         ev["unpermute"].record()
+        ev["quantize_weights"].record()
+
+    return step
+
+
+def build_step_layer(wl, inp, sh, b, wsf, wsb):
+    """The fp8 memory-efficient step through the layer entry points (its
+    row-scaled fp8 products have no stand-alone calls): moe_layer_fwd, then
+    moe_layer_bwd, then the weights' re-quantisation; the forward and backward
+    are timed as wholes (gemm_fwd / gemm_bwd marks)."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd.buffers import requantize_weights
+
+    wq = b["wmx"] if wl.dtype == "mxfp8" else b["wq"]
+    W = (inp["W1"], inp["W3"], inp["W2"])
+
+    def step(ev):
+        ev["start"].record()
+        for m in ("route", "permute", "aux_loss"):
+            ev[m].record()
+        tre.moe_layer_fwd(sh, b, wsf)
+        for m in ("gemm_fwd", "combine", "combine_bwd", "route_bwd"):
+            ev[m].record()
+        tre.moe_layer_bwd(sh, b, wsb)
+        for m in ("gemm_bwd", "unpermute"):
+            ev[m].record()
+        requantize_weights(wq, *W)
         ev["quantize_weights"].record()
 
     return step
@@ -403,8 +432,8 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     inp = make_inputs(wl, seed=0, device="cuda")
-    if args.memory_efficient and wl.dtype != "bf16":
-        log("bench.py: --memory-efficient needs a bf16 workload")
+    if args.memory_efficient and wl.dtype not in ("bf16", "e4m3", "mxfp8"):
+        log("bench.py: --memory-efficient needs a bf16, e4m3 or mxfp8 workload")
         sys.exit(2)
     me = (2 if args.recompute_h else 1) if args.memory_efficient else 0
     step = build_step(wl, inp, args.router_grad, me)
@@ -480,6 +509,11 @@ def main():
     }
     if args.memory_efficient:
         out["config"]["memory_efficient"] = "recompute_h" if me == 2 else True
+        if wl.dtype in ("e4m3", "mxfp8"):
+            # timed through moe_layer_fwd / moe_layer_bwd: the "GEMM" figure is the whole layer's
+            out["roofline"]["kernel"] = (f"{wl.dtype} layer calls (moe_layer_fwd + moe_layer_bwd, "
+                                         "all steps)")
+            out["roofline"]["traffic"] = None
         out["breakdown_ms"]["combine_bwd_permute"] = round(t_permb, 4)
     if args.router_grad and args.memory_efficient:
         # dprob comes out of the expert backward; the router backward is timed with it
