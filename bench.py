@@ -40,12 +40,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of every HIP source and header of the library: a traffic record
-    taken from hardware counters is valid only for the sources it was taken on."""
+# The source file of each dtype's grouped-GEMM kernels.
+GEMM_SOURCE = {"bf16": "gemm_bf16.hip", "f32": "gemm_f32.hip", "e4m3": "gemm_fp8.hip",
+               "mxfp8": "gemm_fp8.hip"}
+
+
+def kernel_sources_sha256(dtype: str) -> str:
+    """Hash of the grouped-GEMM kernel source of `dtype` and of every header of
+    the library: a traffic record taken from hardware counters is valid only
+    for the kernel sources it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_routed_expert_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    for path in sorted([os.path.join(csrc, GEMM_SOURCE[dtype])] +
+                       glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as fh:
             h.update(fh.read())
@@ -62,7 +69,7 @@ def gemm_traffic(wl):
         return None
     with open(path) as fh:
         rec = json.loads("".join(ln for ln in fh if not ln.startswith("#")))
-    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256(wl.dtype):
         log(f"bench: {os.path.basename(path)} was taken on other kernel sources; traffic = null")
         return None
     return int(rec["hbm_bytes_per_step"])
@@ -513,7 +520,8 @@ def main():
             # timed through moe_layer_fwd / moe_layer_bwd: the "GEMM" figure is the whole layer's
             out["roofline"]["kernel"] = (f"{wl.dtype} layer calls (moe_layer_fwd + moe_layer_bwd, "
                                          "all steps)")
-            out["roofline"]["traffic"] = None
+        # the row-scaled GEMM variants run here; the counters were taken on the plain ones
+        out["roofline"]["traffic"] = None
         out["breakdown_ms"]["combine_bwd_permute"] = round(t_permb, 4)
     if args.router_grad and args.memory_efficient:
         # dprob comes out of the expert backward; the router backward is timed with it
