@@ -151,6 +151,11 @@ SMALL = [
     Workload("small_bf16", T=512, d=256, E=8, k=2, f=256),
     Workload("multitile_bf16", T=1100, d=512, E=4, k=2, f=640),
     Workload("ragged_skew_bf16", T=700, d=384, E=16, k=4, f=384, skew=True),
+    # more tiles than compute units: every persistent block runs several
+    # tiles, across experts with hundreds of rows, a few rows and none
+    Workload("persistent_skew_bf16", T=2048, d=1024, E=32, k=4, f=768, skew=True),
+    # ... and weight-gradient tiles of 1 to 3 K stages (about 32 rows an expert)
+    Workload("persistent_short_k_bf16", T=1024, d=1024, E=64, k=2, f=512),
     Workload("shared_bf16", T=300, d=256, E=8, k=2, f=128, f_shared=256),
     Workload("wide_e_bf16", T=512, d=128, E=256, k=8, f=128),
     Workload("dense_bf16", T=200, d=256, E=1, k=1, f=384),

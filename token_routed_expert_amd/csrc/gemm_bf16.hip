@@ -15,17 +15,18 @@
 //   FC1_WGRAD  dW13  d x 2f               xp^T(M-contig)   dab   (N-contig)    K
 //
 // Tile schedule (no host sync): for ragged-M products every block reads the
-// device offsets, counts ceil(m_e/BM) M-tiles per expert, scans them, and
-// finds its (expert, M-tile, N-tile); blocks past the real tile count exit.
+// device offsets, counts ceil(m_e/BM) M-tiles per expert and scans them once;
+// a tile number then maps to its (expert, M-tile, N-tile) by a search over
+// that prefix.  One persistent block per compute unit walks the tile numbers
+// with a stride of the grid; numbers past the device-side count end it.
 // Block ids are remapped so that the blocks one XCD runs at a time (ids with
 // the same value mod 8) take consecutive tiles: they share A rows and expert
 // weights in that XCD's L2.  Weight-gradient products have a fixed grid of
 // E x (M/BM) x (N/BN) tiles; K is the expert's row count, 0 for an empty
 // expert, which then writes zeros.
 //
-// Block tile 256 x 256, 4 wavefronts in a 2x2 grid, each owning a 128 x 128
-// sub-tile of 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, fp32 accumulators
-// in AGPRs).  K advances in stages of 32 through a 4-deep LDS ring (32 KB per
+// Block tile 256 x 256, 8 wavefronts in a 2x4 grid, each owning a 128 x 64
+// sub-tile of 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances in stages of 32 through a 4-deep LDS ring (32 KB per
 // stage): every operand byte is moved by buffer_load ... lds (global -> LDS
 // without registers; rows past an expert's end or past K are zero-filled by
 // the buffer range check), issued three stages ahead.  LDS layouts:
@@ -39,9 +40,9 @@
 //    4 x 16 block), which turns the MN-contiguous tile into the K-contiguous
 //    8-element vectors the MFMA takes.
 // For fc1 the two halves of the B tile are the same 128 f-columns of W1 and
-// of W3; a wavefront's B fragments 0..3 come from W1 and 4..7 from the same
-// columns of W3, so a lane holds a and b of one element (accumulators j and
-// j + 4) and applies SwiGLU in the epilogue.
+// of W3; the first half of a wavefront's B fragments come from W1 and the
+// second half from the same columns of W3, so a lane holds a and b of one
+// element (accumulators j and j + FN/2) and applies SwiGLU in the epilogue.
 // One barrier per stage sits in the middle of the stage's MFMAs, after which
 // the next stage's fragments are prefetched; the MFMA computes C^T = B^T A^T
 // so that a lane ends with four consecutive columns of one row.
@@ -90,6 +91,17 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // NW wavefronts per block in a 2 x (NW/2) grid: NW = 4 gives 128 x 128
 // wavefront tiles (one wavefront per SIMD), NW = 8 gives 128 x 64 (two per
 // SIMD, so one wavefront's stalls leave the matrix core to the other).
+//
+// Persistent: a block takes tiles slot = blockIdx.x, blockIdx.x + gridDim.x,
+// ... (gridDim.x is a multiple of 8, so a block's slots stay on its XCD and
+// the XCD remap of the tile numbering holds).  The K stages of a block's
+// tiles form one stream through the LDS ring: the loads the pipeline issues
+// past the current tile's last stage fetch the first three stages of the
+// next tile (decoded when the current one starts), so the next tile's
+// prologue runs under the current tile's last stages and its epilogue
+// stores.  When the next tile has fewer than three stages (a weight gradient
+// of an expert with under 96 rows) those loads read nothing (a zero-length
+// buffer range) and the next tile starts its own prologue after a full wait.
 template <int OP, int NW, bool RS>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
@@ -103,7 +115,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   using TR = OpTraits<OP>;
 
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
-  __shared__ int sched[NW + 4];
+  __shared__ int sched[NW];
+  // ragged M: inclusive prefix of the experts' M-tile counts
+  __shared__ int mt_incl[TR::ragged_m ? 64 * NW : 1];
   // row-scaled fc2 dgrad: the wavefronts' per-row <h, dh'> partials
   __shared__ float dp_red[RS ? (NW / 2) * 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -111,80 +125,57 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int d = args.d, f = args.f;
 
-  // ---------------------------------------------------------------- tile
-  TileInfo ti;
-  int K, M, N;
-  if constexpr (TR::ragged_m) {
-    if (!decode_ragged_m<BM, NW>(args.offsets, args.E, NT, sched, ti)) return;
-    ti.n0 *= BN;
-    K = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
-    N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
-  } else {
-    const int total = args.E * MT * NT;
-    if ((int)blockIdx.x >= total) return;
-    const int logical = xcd_remap(blockIdx.x, total);
-    ti.e = logical / (MT * NT);
-    const int rem = logical % (MT * NT);
-    ti.m0 = (rem / NT) * BM;
-    ti.n0 = (rem % NT) * BN;
-    ti.row0 = args.offsets[ti.e];
-    ti.rows = args.offsets[ti.e + 1] - ti.row0;
-    K = ti.rows;
-    N = (OP == OP_FC2_WGRAD) ? d : 2 * f;
-  }
-  ti.e = uniform(ti.e);
-  ti.row0 = uniform(ti.row0);
-  ti.rows = uniform(ti.rows);
-  ti.m0 = uniform(ti.m0);
-  ti.n0 = uniform(ti.n0);
-  M = TR::ragged_m ? ti.rows : ((OP == OP_FC2_WGRAD) ? f : d);
-  const size_t e = (size_t)ti.e;
-  const int KT = (K + BK - 1) / BK;
+  // ---------------------------------------------------------------- tiles
+  // Ragged M: M = the tile's rows, K and N fixed.  Weight gradients: M and N
+  // fixed, K = the expert's rows (0 for an empty expert, which writes zeros).
+  const int N = TR::ragged_m ? ((OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d))
+                             : ((OP == OP_FC2_WGRAD) ? d : 2 * f);
+  const int Kfix = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
+  const int Mfix = (OP == OP_FC2_WGRAD) ? f : d;
+  int total;
+  if constexpr (TR::ragged_m) total = mtile_prefix<BM, NW>(args.offsets, args.E, mt_incl, sched) * NT;
+  else total = args.E * MT * NT;
+  total = uniform(total);
+  auto decode = [&](int slot, TileInfo& ti) __attribute__((always_inline)) {
+    const int logical = xcd_remap(slot, total);
+    if constexpr (TR::ragged_m) {
+      ragged_tile(args.offsets, mt_incl, args.E, NT, BM, logical, ti);
+      ti.n0 *= BN;
+    } else {
+      ti.e = logical / (MT * NT);
+      const int rem = logical % (MT * NT);
+      ti.m0 = (rem / NT) * BM;
+      ti.n0 = (rem % NT) * BN;
+      ti.row0 = args.offsets[ti.e];
+      ti.rows = args.offsets[ti.e + 1] - ti.row0;
+    }
+    ti.e = uniform(ti.e);
+    ti.row0 = uniform(ti.row0);
+    ti.rows = uniform(ti.rows);
+    ti.m0 = uniform(ti.m0);
+    ti.n0 = uniform(ti.n0);
+  };
 
   // ---------------------------------------------------------------- operands
-  // A: K-contig rows of xp/h/dO/dab (ragged M; rows past the expert read as
-  // zero), or M-contig rows of h/xp (wgrad; K = the expert's rows, past them zero)
-  rsrc_t a_src;
-  uint32_t a_ld;
+  // Per tile: buffer resources over the rows the tile reads (rows past an
+  // expert's end or past K read as zero), the wavefront's DMA lane offsets
+  // and the stage count.
+  struct Opnd {
+    rsrc_t a_src, b_src, b_src2;
+    uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
+    int KT;
+  };
+  uint32_t a_ld, b_ld;
   {
-    const bf16_t* base;
     int ld;
-    if constexpr (OP == OP_FC1_FWD) { base = (const bf16_t*)args.xp; ld = d; }
-    else if constexpr (OP == OP_FC2_FWD) { base = (const bf16_t*)args.h; ld = f; }
-    else if constexpr (OP == OP_FC2_DGRAD) { base = (const bf16_t*)args.dO; ld = d; }
-    else if constexpr (OP == OP_FC1_DGRAD) { base = (const bf16_t*)args.dab; ld = 2 * f; }
-    else if constexpr (OP == OP_FC2_WGRAD) { base = (const bf16_t*)args.h; ld = f; }
-    else { base = (const bf16_t*)args.xp; ld = d; }
+    if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD || OP == OP_FC1_WGRAD) ld = d;
+    else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_WGRAD) ld = f;
+    else ld = 2 * f;
     a_ld = (uint32_t)ld * 2u;
-    a_src = make_rsrc(base + (size_t)ti.row0 * ld, (uint32_t)ti.rows * a_ld);
+    if constexpr (OP == OP_FC1_FWD || OP == OP_FC1_DGRAD) b_ld = (uint32_t)f * 2u;
+    else if constexpr (OP == OP_FC1_WGRAD) b_ld = (uint32_t)f * 4u;
+    else b_ld = (uint32_t)d * 2u;
   }
-  // B: weight rows (K-contig, dgrad), weight columns (N-contig, forward) or
-  // rows of dO/dab (N-contig, wgrad).  b_src2 is the second source when the
-  // tile draws from two matrices (fc1: W3 beside W1).
-  rsrc_t b_src, b_src2;
-  uint32_t b_ld;
-  if constexpr (OP == OP_FC1_FWD) {
-    b_ld = (uint32_t)f * 2u;
-    b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * b_ld);
-    b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * b_ld);
-  } else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_DGRAD) {
-    b_ld = (uint32_t)d * 2u;
-    b_src = make_rsrc((const bf16_t*)args.W2 + e * (size_t)f * d, (uint32_t)f * b_ld);
-    b_src2 = b_src;
-  } else if constexpr (OP == OP_FC1_DGRAD) {
-    b_ld = (uint32_t)f * 2u;
-    b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * b_ld);
-    b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * b_ld);
-  } else if constexpr (OP == OP_FC2_WGRAD) {
-    b_ld = (uint32_t)d * 2u;
-    b_src = make_rsrc((const bf16_t*)args.dO + (size_t)ti.row0 * d, (uint32_t)ti.rows * b_ld);
-    b_src2 = b_src;
-  } else {
-    b_ld = (uint32_t)f * 4u;
-    b_src = make_rsrc((const bf16_t*)args.dab + (size_t)ti.row0 * 2 * f, (uint32_t)ti.rows * b_ld);
-    b_src2 = b_src;
-  }
-
   // ---- DMA lane offsets (bytes, without the stage's k offset) -----------
   // K-contig operand: instruction t (0..15) covers tile rows 16t..16t+15;
   // lane -> row 16t + lane/4, stored chunk lane%4 holds logical chunk
@@ -192,7 +183,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   // MN-contig operand: instruction t covers half t>>3, k-rows 4(t&7)..+3;
   // lane -> k-row 4(t&7) + lane/16, stored 16-byte unit lane%16, i.e. 32-byte
   // unit (lane%16)/2 holding logical unit ((lane%16)/2) ^ f(k).
-  uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
   auto kc_off = [&](int t, int row_base_mn, uint32_t ld) __attribute__((always_inline)) -> uint32_t {
     const int row = 16 * t + (lane >> 2);
     const int c = (lane & 3) ^ kc_swz(row);
@@ -204,51 +194,103 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     const int unit = ((lane & 15) >> 1) ^ fk;
     return (uint32_t)k * ld + (uint32_t)(col_base + unit * 16 + (lane & 1) * 8) * 2u;
   };
-#pragma unroll
-  for (int q = 0; q < DMA_PER_WAVE; ++q) {
-    const int t = wid * DMA_PER_WAVE + q;
-    if constexpr (TR::a_kcontig) a_off[q] = kc_off(t, 0, a_ld);
-    else a_off[q] = mc_off(t, min(ti.m0 + (t >> 3) * 128, M - 128), a_ld);
-    if constexpr (TR::b_kcontig) {
-      b_off[q] = kc_off(t, ti.n0, b_ld);
-    } else if constexpr (OP == OP_FC1_FWD) {
-      b_off[q] = mc_off(t, ti.n0 / 2, b_ld);          // both halves: the tile's f-columns
-    } else {
-      b_off[q] = mc_off(t, min(ti.n0 + (t >> 3) * 128, N - 128), b_ld);
+  auto setup = [&](const TileInfo& ti, Opnd& o) __attribute__((always_inline)) {
+    const size_t e = (size_t)ti.e;
+    {
+      const bf16_t* base;
+      if constexpr (OP == OP_FC1_FWD || OP == OP_FC1_WGRAD) base = (const bf16_t*)args.xp;
+      else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_WGRAD) base = (const bf16_t*)args.h;
+      else if constexpr (OP == OP_FC2_DGRAD) base = (const bf16_t*)args.dO;
+      else base = (const bf16_t*)args.dab;
+      o.a_src = make_rsrc((const char*)base + (size_t)ti.row0 * a_ld, (uint32_t)ti.rows * a_ld);
     }
-  }
+    if constexpr (OP == OP_FC1_FWD || OP == OP_FC1_DGRAD) {
+      o.b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * (uint32_t)f * 2u);
+      o.b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * (uint32_t)f * 2u);
+    } else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_DGRAD) {
+      o.b_src = make_rsrc((const bf16_t*)args.W2 + e * (size_t)f * d, (uint32_t)f * b_ld);
+      o.b_src2 = o.b_src;
+    } else if constexpr (OP == OP_FC2_WGRAD) {
+      o.b_src = make_rsrc((const bf16_t*)args.dO + (size_t)ti.row0 * d, (uint32_t)ti.rows * b_ld);
+      o.b_src2 = o.b_src;
+    } else {
+      o.b_src = make_rsrc((const bf16_t*)args.dab + (size_t)ti.row0 * 2 * f, (uint32_t)ti.rows * b_ld);
+      o.b_src2 = o.b_src;
+    }
+    const int K = TR::ragged_m ? Kfix : ti.rows;
+    o.KT = uniform((K + BK - 1) / BK);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q) {
+      const int t = wid * DMA_PER_WAVE + q;
+      if constexpr (TR::a_kcontig) o.a_off[q] = kc_off(t, 0, a_ld);
+      else o.a_off[q] = mc_off(t, min(ti.m0 + (t >> 3) * 128, Mfix - 128), a_ld);
+      if constexpr (TR::b_kcontig) {
+        o.b_off[q] = kc_off(t, ti.n0, b_ld);
+      } else if constexpr (OP == OP_FC1_FWD) {
+        o.b_off[q] = mc_off(t, ti.n0 / 2, b_ld);        // both halves: the tile's f-columns
+      } else {
+        o.b_off[q] = mc_off(t, min(ti.n0 + (t >> 3) * 128, N - 128), b_ld);
+      }
+    }
+  };
 
   // LDS byte address of the stage ring (M0 values are this plus constants)
   const uint32_t lds_base =
       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)LDS_PTR(lds));
-  // DMA instruction q of this wavefront (q < DMA_PER_WAVE: A operand, else B) for stage kt
-  auto issue_one = [&](int kt, int q) __attribute__((always_inline)) {
-    const uint32_t st_base = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
-    const int k0 = kt * BK;
-    if (q < DMA_PER_WAVE) {
+
+  TileInfo ti, tn;
+  Opnd cur, nxt;
+  int slot = blockIdx.x;
+  if (slot >= total) return;
+  decode(slot, ti);
+  setup(ti, cur);
+  tn = ti;     // nxt always holds valid descriptors (a past-the-end load
+  nxt = cur;   // uses them with a zero-length range)
+  int phase = 0;        // ring slot of the current tile's stage 0
+  bool cross = false;   // stages past the current tile's last fetch the next tile's first three
+  // DMA instruction q of this wavefront (q < DMA_PER_WAVE: A operand, else B)
+  // for stage s of the stream, counted from the current tile's stage 0
+  // TAIL = false: the caller knows that s is a stage of the current tile.
+  auto issue_one = [&](int s, auto Q, auto TAIL) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value;
+    const uint32_t st_base = lds_base + (uint32_t)(((phase + s) & (NSTAGE - 1)) * STAGE_BYTES);
+    const bool in_cur = !decltype(TAIL)::value || s < cur.KT;
+    const int k0 = (in_cur ? s : s - cur.KT) * BK;
+    const bool live = in_cur || cross;
+    if constexpr (q < DMA_PER_WAVE) {
       const int t = wid * DMA_PER_WAVE + q;
+      rsrc_t r = pick(in_cur, cur.a_src, nxt.a_src);
+      r[2] = live ? r[2] : 0;
+      r = uniform_rsrc(r);
+      const uint32_t off = in_cur ? cur.a_off[q] : nxt.a_off[q];
       const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
-      dma16(a_src, a_off[q] + ka, st_base + (uint32_t)(t * 1024));
+      dma16(r, off + ka, st_base + (uint32_t)(t * 1024));
     } else {
       const int qq = q - DMA_PER_WAVE;
       const int t = wid * DMA_PER_WAVE + qq;
       const uint32_t dst = st_base + (uint32_t)(OPND_BYTES + t * 1024);
+      const uint32_t off = in_cur ? cur.b_off[qq] : nxt.b_off[qq];
+      rsrc_t r;
+      uint32_t voff;
       if constexpr (OP == OP_FC1_DGRAD) {
         // K = [da | db]: the first f columns multiply W1, the rest W3
         const bool first = k0 < f;
-        dma16(first ? b_src : b_src2, b_off[qq] + (uint32_t)(first ? k0 : k0 - f) * 2u, dst);
+        r = pick(in_cur, pick(first, cur.b_src, cur.b_src2), pick(first, nxt.b_src, nxt.b_src2));
+        voff = off + (uint32_t)(first ? k0 : k0 - f) * 2u;
       } else if constexpr (OP == OP_FC1_FWD) {
-        dma16((t >> 3) ? b_src2 : b_src, b_off[qq] + (uint32_t)k0 * b_ld, dst);
+        const bool second = (t >> 3) != 0;
+        r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
+        voff = off + (uint32_t)k0 * b_ld;
       } else if constexpr (TR::b_kcontig) {
-        dma16(b_src, b_off[qq] + (uint32_t)k0 * 2u, dst);
+        r = pick(in_cur, cur.b_src, nxt.b_src);
+        voff = off + (uint32_t)k0 * 2u;
       } else {
-        dma16(b_src, b_off[qq] + (uint32_t)k0 * b_ld, dst);
+        r = pick(in_cur, cur.b_src, nxt.b_src);
+        voff = off + (uint32_t)k0 * b_ld;
       }
+      r[2] = live ? r[2] : 0;
+      dma16(uniform_rsrc(r), voff, dst);
     }
-  };
-  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 2 * DMA_PER_WAVE; ++q) issue_one(kt, q);
   };
 
   // ---- fragment addresses (bytes inside a stage) -------------------------
@@ -288,13 +330,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     if constexpr (TR::b_kcontig) return lds_b128(st + bfa[j]);
     else return lds_tr_pair(st + bfa[j]);
   };
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
+    return lds + ((phase + s) & (NSTAGE - 1)) * STAGE_BYTES;
+  };
 
   // ---------------------------------------------------------------- main loop
   f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Per stage both halves walk the FM = 8 A fragments i-major against HB B
   // fragments held in registers: B fragments 0..HB-1 (b0, read during the
@@ -310,21 +351,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   // half of stage kt+1 (its B operand): issued in a burst they stall the
   // wavefront's instruction issue.
   bf16x8_t af[FM], b0[HB], b1[HB];
-  if (KT > 0) {
-    // stages 0..2 in flight; wait for stage 0, make it visible, read its fragments
-    issue_stage(0);
-    issue_stage(1);
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q) issue_one(2, q);   // stage 2's B half follows in stage 0
-    wait_vmcnt<LOADS_PER_STAGE + DMA_PER_WAVE>();
-    block_barrier();
-    static_for<0, FM>([&](auto i) __attribute__((always_inline)) { af[i.value] = read_a(lds, i.value); });
-    static_for<0, HB>([&](auto j) __attribute__((always_inline)) { b0[j.value] = read_b(lds, j.value); });
-  }
   // st and nst are distinct stage buffers (restrict lets the compiler keep
   // their reads apart).
-  auto stage_body = [&](int kt, const char* __restrict__ st,
-                        const char* __restrict__ nst) __attribute__((always_inline)) {
+  auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst,
+                        auto TAIL) __attribute__((always_inline)) {
     // B fragments HB..FN-1 for the second half: issued first, needed last
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, HB + U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
@@ -339,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       __builtin_amdgcn_sched_barrier(0);
       // second (B-operand) half of stage kt+2's refill; its buffer was freed
       // by the previous stage's barrier
-      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 2, DMA_PER_WAVE + u / DMA_STEP);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 2, IntC<DMA_PER_WAVE + u / DMA_STEP>{}, TAIL);
     });
     // stage kt+1 has landed for this wavefront; after the barrier it has for
     // all, and every wavefront is done with stage kt-1, whose buffer now
@@ -363,16 +393,81 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       // first (A-operand) half of stage kt+3's refill into the buffer stage
       // kt-1 used; one DMA instruction per step keeps the address unit from
       // stalling the issue of the MFMAs
-      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 3, u / DMA_STEP);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 3, IntC<u / DMA_STEP>{}, TAIL);
     });
   };
-  for (int kt = 0; kt < KT; ++kt)
-    stage_body(kt, lds + (kt & (NSTAGE - 1)) * STAGE_BYTES,
-               lds + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES);
-  wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
 
-  // ---------------------------------------------------------------- epilogue
-  store_tile<OP, FM, FN, WM, WN, TR::ragged_m, RS>(args, acc, ti, M, N, wm, wn, lane, dp_red);
+  bool fresh = true;  // the current tile's first stages are not yet issued
+  for (;;) {
+    const int nslot = slot + (int)gridDim.x;
+    const bool have_next = nslot < total;
+    if (have_next) {
+      decode(nslot, tn);
+      setup(tn, nxt);
+    }
+    // fc2 dgrad's epilogue reads a|b from memory and would wait for the next
+    // tile's loads in flight: it starts every tile with its own prologue
+    cross = OP != OP_FC2_DGRAD && have_next && cur.KT >= 1 && nxt.KT >= 3;
+    if (fresh) {
+      // stages 0, 1 and stage 2's A half in flight (stage 2's B half follows
+      // in stage 0); wait for stage 0 and make it visible
+      static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(0, Q, IntC<1>{}); });
+      static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(1, Q, IntC<1>{}); });
+      static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(2, Q, IntC<1>{}); });
+      wait_vmcnt<LOADS_PER_STAGE + DMA_PER_WAVE>();
+      block_barrier();
+    }
+    // (entered from the previous tile's stream, stage 0 has landed and passed
+    // that tile's last barrier)
+    {
+      const char* st0 = stage_ptr(0);
+      static_for<0, FM>([&](auto i) __attribute__((always_inline)) { af[i.value] = read_a(st0, i.value); });
+      static_for<0, HB>([&](auto j) __attribute__((always_inline)) { b0[j.value] = read_b(st0, j.value); });
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the last three stages issue the loads that may fall past the tile
+    const int kt_tail = max(cur.KT - 3, 0);
+    for (int kt = 0; kt < kt_tail; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<0>{});
+    for (int kt = kt_tail; kt < cur.KT; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<1>{});
+
+    // ---------------------------------------------------------------- epilogue
+    store_tile<OP, FM, FN, WM, WN, TR::ragged_m, RS>(args, acc, ti, TR::ragged_m ? ti.rows : Mfix, N,
+                                                      wm, wn, lane, dp_red);
+    if (!have_next) break;
+    if (cross) {
+      phase = (phase + cur.KT) & (NSTAGE - 1);
+      fresh = false;
+    } else {
+      // the past-the-end loads read nothing but still write the ring: drain
+      // them (and every LDS read) before the next tile's prologue
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      block_barrier();
+      fresh = true;
+    }
+    slot = nslot;
+    ti = tn;
+    cur = nxt;
+  }
+  wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
+}
+
+// Compute units of the current device rounded down to a multiple of 8
+// (cached per device), or -1 when the runtime cannot say.
+int persistent_blocks() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+    return -1;
+  n &= ~7;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 template <int OP, int NW>
@@ -394,6 +489,11 @@ int launch(const GemmArgs& a, hipStream_t s) {
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  // persistent blocks: one per compute unit (the tile takes a whole CU's
+  // LDS), a multiple of 8 so that every block's tiles stay on one XCD
+  const int ncu = persistent_blocks();
+  if (ncu <= 0) return MOE_ERR_HIP;
+  if (grid > ncu) grid = ncu;
   bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
   if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
     if (a.row_prob) {

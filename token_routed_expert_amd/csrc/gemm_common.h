@@ -39,6 +39,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
+// c ? x : y for buffer resources, component by component (uniform c).
+__device__ __forceinline__ rsrc_t pick(bool c, rsrc_t x, rsrc_t y) {
+  rsrc_t r;
+  r[0] = c ? x[0] : y[0];
+  r[1] = c ? x[1] : y[1];
+  r[2] = c ? x[2] : y[2];
+  r[3] = c ? x[3] : y[3];
+  return r;
+}
+
+// A resource chosen at run time between uniform ones, kept in SGPRs.
+__device__ __forceinline__ rsrc_t uniform_rsrc(rsrc_t r) {
+  rsrc_t u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // 16 bytes per lane from `r` at byte offset `voff` into LDS at byte address
 // m0 + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS address).
 // Issued through inline assembly so that the compiler does not treat it as
