@@ -29,9 +29,9 @@
 // SwiGLU forward / backward epilogues, bf16 stores).  K advances 128 per
 // stage through a 2-deep LDS ring (64 KB per stage) filled by buffer_load ...
 // lds; a K-contiguous LDS row is 128 bytes (8 chunks of 16) with chunk c of
-// row r stored at c ^ ((r >> 1) & 7), so the 16 rows of a fragment read hit
-// all 64 banks.  A fragment (32 consecutive K bytes of one row per lane) is
-// two ds_read_b128.
+// row r stored at c ^ ((r >> 1) & 7).  A fragment (32 K bytes of one row per
+// lane: chunks g and g + 4 for lane group g) is two ds_read_b128, free of
+// bank conflicts (measured).
 #include "gemm_common.h"
 
 namespace tre {
@@ -50,20 +50,15 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-__device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int c0, int sw) {
-  const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((c0 ^ sw) << 4));
-  const i32x4_t hi =
-      *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((c0 + 1) ^ sw) << 4));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // The scaled MFMA's operand layout (measured): lane group g = lane >> 4 holds
 // K values [16 g, 16 g + 16) in its bytes 0..15 and [64 + 16 g, 64 + 16 g + 16)
 // in bytes 16..31, and the scale of 32-value block g of the row comes from
-// lane group g.  So an MXFP8 fragment takes 16-byte chunks g and g + 4 of the
-// 128-byte K row (the plain MFMA of the e4m3 path accepts any K order that A
-// and B share, and takes chunks 2g, 2g + 1).
-__device__ __forceinline__ i32x8_t lds_frag_mx(const char* row_base, int g, int sw) {
+// lane group g.  So a fragment takes 16-byte chunks g and g + 4 of the
+// 128-byte K row.  The e4m3 path (one 128-value scale block per MFMA) could
+// take any K order that A and B share; it takes the same one, which is free
+// of LDS bank conflicts, where chunks 2g and 2g + 1 made half of the LDS
+// cycles conflict cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.5).
+__device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int g, int sw) {
   const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((g ^ sw) << 4));
   const i32x4_t hi =
       *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((g + 4) ^ sw) << 4));
@@ -85,7 +80,7 @@ __device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 // MX = true: MXFP8 operands.  v_mfma_scale_f32_16x16x128_f8f6f4 takes one
 // E8M0 scale per lane and operand -- that of 32-value block (lane >> 4) of the
-// lane's row (see lds_frag_mx for the matching fragment layout) -- so the
+// lane's row (see lds_frag for the matching fragment layout) -- so the
 // scales go straight into the MFMA, which accumulates in place: no promotion.
 // A lane's scale byte for fragment row r and stage kt is byte (lane >> 4) of
 // the word at r * ld + 4 kt.
@@ -321,17 +316,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       int sbb[FN];
       static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
         const int r = b_row(J.value);
-        bf[J.value] = lds_frag_mx(cur + OPND_BYTES + r * BK, lg, swz(r));
+        bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, lg, swz(r));
         sbb[J.value] = (int)((sb[J.value] >> sh8) & 0xffu);
       });
       // the next row's A fragment is read while this row's MFMAs run
-      i32x8_t af = lds_frag_mx(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
+      i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
       static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = I.value;
         i32x8_t af_next;
         if constexpr (i + 1 < FM) {
           const int r = wm * WM + 16 * (i + 1) + lm;
-          af_next = lds_frag_mx(cur + r * BK, lg, swz(r));
+          af_next = lds_frag(cur + r * BK, lg, swz(r));
         }
         const int sab = (int)((sa[i] >> sh8) & 0xffu);
         __builtin_amdgcn_sched_barrier(0);
@@ -430,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     i32x8_t bf[FN];
     static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
       const int r = b_row(J.value);
-      bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, 2 * lg, swz(r));
+      bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, lg, swz(r));
     });
     // Software pipeline over the FM fragment rows: the FN MFMAs of row i go
     // to their own product registers while the scale FMAs of row i-1 (whose
@@ -451,13 +446,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       });
     };
     f32x4_t pc[FN], pp[FN];
-    i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, 2 * lg, swz(wm * WM + lm));
+    i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
     static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = I.value;
       i32x8_t af_next;
       if constexpr (i + 1 < FM) {
         const int r = wm * WM + 16 * (i + 1) + lm;
-        af_next = lds_frag(cur + r * BK, 2 * lg, swz(r));
+        af_next = lds_frag(cur + r * BK, lg, swz(r));
       }
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, FN>([&](auto J) __attribute__((always_inline)) { pc[J.value] = mfma_fp8(bf[J.value], af); });
