@@ -29,7 +29,7 @@
 // sub-tile of 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances in stages of 32 through a 4-deep LDS ring (32 KB per
 // stage): every operand byte is moved by buffer_load ... lds (global -> LDS
 // without registers; rows past an expert's end or past K are zero-filled by
-// the buffer range check), issued three stages ahead.  LDS layouts:
+// the buffer range check), issued up to three stages ahead.  LDS layouts:
 //  * K-contiguous operands: 256 rows of 64 bytes; 16-byte chunk c of row r is
 //    stored at chunk c ^ kc_swz(r), so that a fragment read (ds_read_b128,
 //    one chunk of 16 consecutive rows) is free of bank conflicts (measured);
@@ -56,7 +56,7 @@ namespace tre {
 namespace {
 using namespace gemm;
 
-constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int OPND_BYTES = 256 * BK * 2;         // one operand of one stage (16 KB)
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // A then B
 constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 16 one-KB DMA instructions
@@ -106,6 +106,7 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // stores.  When the next tile has fewer than three stages (a weight gradient
 // of an expert with under 96 rows) those loads read nothing (a zero-length
 // buffer range) and the next tile starts its own prologue after a full wait.
+// (LOOK = 3 below: the ring depth minus one.)
 template <int OP, int NW, bool RS>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
@@ -117,13 +118,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   constexpr int DMA_STEP = 4 / DMA_PER_WAVE;       // MFMA steps per DMA instruction
   static_assert(FM == 8 && HB * 2 == FN && DMA_STEP * DMA_PER_WAVE == 4, "tile shape");
   using TR = OpTraits<OP>;
+  // LDS ring depth (measured on the Qwen3 shape: 3 stages cost 10-30 % on
+  // every product, 5 stages, possible for the weight gradients only, made
+  // them 5-10 % slower)
+  constexpr int NS = 4;
+  constexpr int LOOK = NS - 1;  // stage kt + LOOK is issued during stage kt
 
-  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
-  __shared__ int sched[NW];
-  // ragged M: inclusive prefix of the experts' M-tile counts
-  __shared__ int mt_incl[TR::ragged_m ? 64 * NW : 1];
-  // row-scaled fc2 dgrad: the wavefronts' per-row <h, dh'> partials
-  __shared__ float dp_red[RS ? (NW / 2) * 256 : 1];
+  // the stage ring, then (ragged M) the schedule scratch, the inclusive prefix
+  // of the experts' M-tile counts and (row-scaled fc2 dgrad) the wavefronts'
+  // per-row <h, dh'> partials
+  constexpr int EXTRA = TR::ragged_m ? (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + EXTRA];
+  int* const sched = (int*)(lds + NS * STAGE_BYTES);
+  int* const mt_incl = sched + NW;
+  float* const dp_red = (float*)(mt_incl + 64 * NW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   // TAIL = false: the caller knows that s is a stage of the current tile.
   auto issue_one = [&](int s, auto Q, auto TAIL) __attribute__((always_inline)) {
     constexpr int q = decltype(Q)::value;
-    const uint32_t st_base = lds_base + (uint32_t)(((phase + s) & (NSTAGE - 1)) * STAGE_BYTES);
+    const uint32_t st_base = lds_base + (uint32_t)(((uint32_t)(phase + s) % NS) * STAGE_BYTES);
     const bool in_cur = !decltype(TAIL)::value || s < cur.KT;
     const int k0 = (in_cur ? s : s - cur.KT) * BK;
     const bool live = in_cur || cross;
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     else return lds_tr_pair(st + bfa[j]);
   };
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
-    return lds + ((phase + s) & (NSTAGE - 1)) * STAGE_BYTES;
+    return lds + ((uint32_t)(phase + s) % NS) * STAGE_BYTES;
   };
 
   // ---------------------------------------------------------------- main loop
@@ -373,12 +381,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       __builtin_amdgcn_sched_barrier(0);
       // second (B-operand) half of stage kt+2's refill; its buffer was freed
       // by the previous stage's barrier
-      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 2, IntC<DMA_PER_WAVE + u / DMA_STEP>{}, TAIL);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + LOOK - 1, IntC<DMA_PER_WAVE + u / DMA_STEP>{}, TAIL);
     });
     // stage kt+1 has landed for this wavefront; after the barrier it has for
     // all, and every wavefront is done with stage kt-1, whose buffer now
     // takes stage kt+3
-    wait_vmcnt<LOADS_PER_STAGE>();
+    wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2)>();
     block_barrier();
     // next stage's B fragments 0..HB-1 first: the next first half starts with them
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
@@ -397,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       // first (A-operand) half of stage kt+3's refill into the buffer stage
       // kt-1 used; one DMA instruction per step keeps the address unit from
       // stalling the issue of the MFMAs
-      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + 3, IntC<u / DMA_STEP>{}, TAIL);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + LOOK, IntC<u / DMA_STEP>{}, TAIL);
     });
   };
 
@@ -411,14 +419,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     }
     // fc2 dgrad's epilogue reads a|b from memory and would wait for the next
     // tile's loads in flight: it starts every tile with its own prologue
-    cross = OP != OP_FC2_DGRAD && have_next && cur.KT >= 1 && nxt.KT >= 3;
+    cross = OP != OP_FC2_DGRAD && have_next && cur.KT >= 1 && nxt.KT >= LOOK;
     if (fresh) {
-      // stages 0, 1 and stage 2's A half in flight (stage 2's B half follows
-      // in stage 0); wait for stage 0 and make it visible
-      static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(0, Q, IntC<1>{}); });
-      static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(1, Q, IntC<1>{}); });
-      static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(2, Q, IntC<1>{}); });
-      wait_vmcnt<LOADS_PER_STAGE + DMA_PER_WAVE>();
+      // stages 0 .. LOOK-2 and stage LOOK-1's A half in flight (its B half
+      // follows in stage 0); wait for stage 0 and make it visible
+      static_for<0, LOOK - 1>([&](auto S) __attribute__((always_inline)) {
+        static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) {
+          issue_one(S.value, Q, IntC<1>{});
+        });
+      });
+      static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(LOOK - 1, Q, IntC<1>{}); });
+      wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE>();
       block_barrier();
     }
     // (entered from the previous tile's stream, stage 0 has landed and passed
@@ -432,8 +443,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // the last three stages issue the loads that may fall past the tile
-    const int kt_tail = max(cur.KT - 3, 0);
+    // the last LOOK stages issue the loads that may fall past the tile
+    const int kt_tail = max(cur.KT - LOOK, 0);
     for (int kt = 0; kt < kt_tail; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<0>{});
     for (int kt = kt_tail; kt < cur.KT; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<1>{});
 
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
                                                       wm, wn, lane, dp_red);
     if (!have_next) break;
     if (cross) {
-      phase = (phase + cur.KT) & (NSTAGE - 1);
+      phase = (int)((uint32_t)(phase + cur.KT) % NS);
       fresh = false;
     } else {
       // the past-the-end loads read nothing but still write the ring: drain
