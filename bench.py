@@ -520,6 +520,8 @@ def main():
             # timed through moe_layer_fwd / moe_layer_bwd: the "GEMM" figure is the whole layer's
             out["roofline"]["kernel"] = (f"{wl.dtype} layer calls (moe_layer_fwd + moe_layer_bwd, "
                                          "all steps)")
+            # permute and combine run inside the layer calls: no separate times
+            out["hbm"] = None
         # the row-scaled GEMM variants run here; the counters were taken on the plain ones
         out["roofline"]["traffic"] = None
         out["breakdown_ms"]["combine_bwd_permute"] = round(t_permb, 4)
