@@ -92,6 +92,30 @@ MARKS = ("start", "route", "permute", "aux_loss", "gemm_fwd", "combine", "combin
          "route_bwd", "gemm_bwd", "unpermute", "quantize_weights")
 
 
+def mfma_probe(iters: int = 4096):
+    """The matrix-core rate and clock this GPU sustains under MFMAs alone
+    (moe_probe_mfma), bf16 and e4m3: context for the roofline, whose peak
+    stays the published figure."""
+    import torch
+    import token_routed_expert_amd as tre
+    ticks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out = {"kernel": "8 independent MFMA chains per wavefront, 32 wavefronts per CU, no memory traffic"}
+    for dt in ("bf16", "e4m3"):
+        tre.moe_probe_mfma(dt, iters // 8, ticks, sink)     # warm-up
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        flops, khz = tre.moe_probe_mfma(dt, iters, ticks, sink)
+        stop.record()
+        torch.cuda.synchronize()
+        sec = start.elapsed_time(stop) * 1e-3
+        cyc, wall = (int(v) for v in ticks.cpu())
+        out[f"{dt}_tflops"] = round(flops / sec / 1e12, 1)
+        out[f"{dt}_frac_of_published"] = round(flops / sec / 1e12 / MFMA_PEAK_TFLOPS[dt], 4)
+        out[f"{dt}_clock_ghz"] = round(cyc / (wall / (khz * 1e3)) / 1e9, 3) if wall > 0 else None
+    return out
+
+
 def router_grad_calls(wl, sh, b, ws_aux):
     """(aux loss after the permutation, combine backward with dprob, router
     backward) as three callables, or no-ops when router_grad is off."""
@@ -413,6 +437,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA-only probe of the sustained matrix-core rate and clock")
     ap.add_argument("--router-grad", action="store_true",
                     help="also the load-balancing loss, dprob and the router backward (dlogits)")
     ap.add_argument("--memory-efficient", action="store_true",
@@ -539,6 +565,8 @@ def main():
                                    route_bwd=round(t_rbwd, 4))
         out["hbm"].update(combine_bwd_GBps=round(cb_gbs, 1),
                           combine_bwd_frac=round(cb_gbs / HBM_PEAK_GBS, 4))
+    if not args.no_mfma_probe:
+        out["mfma_probe"] = mfma_probe()
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

@@ -526,6 +526,28 @@ int moe_grouped_gemm_bwd_mx(const moe_shape* sh, const int32_t* offsets, const i
                             const moe_mx_weights* w, void* dab, void* dXp, void* dW1, void* dW3,
                             void* dW2, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_probe_mfma -- measurement helper, not a step of the layer: the dense
+ * matrix-core rate and the shader clock this GPU sustains under MFMAs alone,
+ * the ceiling against which the grouped GEMMs' rates can be read (published
+ * peaks assume the peak clock; the chip clocks lower under a sustained
+ * matrix-core load).  Launches, on `stream`, 8 blocks of 256 threads per
+ * compute unit; every wavefront runs `iters` (1 .. 2^24) rounds of 8
+ * independent MFMAs on register operands, v_mfma_f32_16x16x32_bf16 for
+ * dtype = MOE_BF16 or v_mfma_scale_f32_16x16x128_f8f6f4 on e4m3 codes for
+ * MOE_E4M3 (other dtypes: MOE_ERR_UNSUPPORTED).
+ *   ticks    device, 2 x uint64, written by the kernel: the shader-clock
+ *            cycles and the wall-clock ticks one wavefront's loop took;
+ *   sink     device, 1 float, written only in the unlikely case that the
+ *            folded results equal a sentinel (keeps the MFMAs alive);
+ *   flops    host: the launch's MFMA flop count (2 per multiply-add);
+ *   wall_khz host: the wall-clock tick rate, so clock = ticks[0] /
+ *            (ticks[1] / (wall_khz * 1e3)).
+ * The rate is flops / the launch's duration measured by the caller on
+ * `stream`.  Returns MOE_ERR_INVALID for null pointers or iters outside the
+ * range, MOE_ERR_HIP if the device cannot be queried or the launch fails. */
+int moe_probe_mfma(int dtype, int64_t iters, unsigned long long* ticks, float* sink,
+                   int64_t* flops, int64_t* wall_khz, void* stream);
+
 /* Bytes of workspace the call `kind` needs for shape sh (0 if none). */
 size_t moe_workspace_bytes(const moe_shape* sh, int kind);
 

@@ -277,3 +277,24 @@ def full_size_sampled(wl, **kw):
         assert_close(f"dW2[{e}]", to_f64(b["dW2"][e]), dW2, tol)
     for e in np.nonzero(counts == 0)[0][:4]:
         assert not b["dW1"][int(e)].any() and not b["dW2"][int(e)].any()
+
+
+# ---------------------------------------------------------------- matrix-core probe
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_mfma_probe(dtype):
+    """The probe runs, reports the launch's flop count and a plausible clock
+    (ticks of a wavefront's loop against the wall clock)."""
+    import token_routed_expert_amd as tre
+    ticks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    flops, khz = tre.moe_probe_mfma(dtype, 64, ticks, sink)
+    torch.cuda.synchronize()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    per = 16 * 16 * (32 if dtype == "bf16" else 128) * 2
+    assert flops == n_cu * 8 * 4 * 64 * 8 * per
+    cyc, wall = (int(v) for v in ticks.cpu())
+    assert cyc > 0 and wall > 0 and khz > 0
+    ghz = cyc / (wall / (khz * 1e3)) / 1e9
+    assert 0.3 < ghz < 3.5, ghz
+    with pytest.raises(tre.MoeError):
+        tre.moe_probe_mfma(dtype, 0, ticks, sink)

@@ -98,6 +98,8 @@ _PROTOS = {
                                        + [C.c_size_t, _P]),
     "moe_workspace_bytes": (C.c_size_t, [_SH, C.c_int]),
     "moe_status_str": (C.c_char_p, [C.c_int]),
+    "moe_probe_mfma": (C.c_int, [C.c_int, _I64, _P, _P, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                 _P]),
 }
 
 _lib = None

@@ -29,6 +29,11 @@ CXXFLAGS = [
 
 _BENIGN = "'-packed-fp32-ops' is not a recognized feature for this target"
 
+# Per-file additions.  probe.hip: MFMAs accumulate in VGPRs (with the default
+# accumulator-register form the compiler moves the accumulators between
+# register files on every loop trip, and the probe would time those moves).
+EXTRA_FLAGS = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -49,7 +54,9 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *CXXFLAGS, "-c", so[0], "-o", so[1]]),
+        outs = list(ex.map(lambda so: _run([HIPCC, *CXXFLAGS,
+                                            *EXTRA_FLAGS.get(os.path.basename(so[0]), []),
+                                            "-c", so[0], "-o", so[1]]),
                            zip(srcs, objs)))
     if verbose:
         for o in outs:

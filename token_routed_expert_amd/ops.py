@@ -311,3 +311,14 @@ def moe_layer_bwd(sh, buffers: dict, ws, stream=None):
     io = _io(buffers)
     _check(N.lib().moe_layer_bwd(C.byref(sh), C.byref(io), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "moe_layer_bwd")
+
+
+def moe_probe_mfma(dtype, iters, ticks, sink, stream=None):
+    """Launches the matrix-core probe (dtype "bf16" or "e4m3") on the stream;
+    `ticks` is a device uint64 tensor of 2 (int64 storage), `sink` a device
+    float tensor of 1.  Returns (flop count of the launch, wall-clock kHz)."""
+    code = {"bf16": N.MOE_BF16, "e4m3": N.MOE_E4M3}[dtype]
+    flops, khz = C.c_int64(0), C.c_int64(0)
+    _check(N.lib().moe_probe_mfma(code, int(iters), _ptr(ticks), _ptr(sink), C.byref(flops),
+                                  C.byref(khz), _stream(stream)), "moe_probe_mfma")
+    return int(flops.value), int(khz.value)
