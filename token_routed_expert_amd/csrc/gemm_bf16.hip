@@ -51,6 +51,8 @@
 #include "gemm_common.h"
 #include "schedule.h"
 
+#include <atomic>
+
 namespace tre {
 
 namespace {
@@ -495,17 +497,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
 }
 
 // Compute units of the current device rounded down to a multiple of 8
-// (cached per device), or -1 when the runtime cannot say.
+// (cached per device; concurrent first calls store the same value), or -1
+// when the runtime cannot say.
 int persistent_blocks() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
     return -1;
   n &= ~7;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
