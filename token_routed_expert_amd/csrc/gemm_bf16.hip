@@ -99,8 +99,10 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // SIMD, so one wavefront's stalls leave the matrix core to the other).
 //
 // Persistent: a block takes tiles slot = blockIdx.x, blockIdx.x + gridDim.x,
-// ... (gridDim.x is a multiple of 8, so a block's slots stay on its XCD and
-// the XCD remap of the tile numbering holds).  The K stages of a block's
+// ... (launched with one block per compute unit, gridDim.x is a multiple of
+// 8, so a block's slots stay on its XCD and the XCD remap of the tile
+// numbering holds; launched with a block per tile, as fc2 dgrad is, every
+// block takes one).  The K stages of a block's
 // tiles form one stream through the LDS ring: the loads the pipeline issues
 // past the current tile's last stage fetch the first three stages of the
 // next tile (decoded when the current one starts), so the next tile's
