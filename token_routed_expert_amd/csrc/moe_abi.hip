@@ -613,6 +613,8 @@ int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uin
   if (R % 128 != 0 || C % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (R >= (1 << 30) || C >= (1 << 30) || E > 65535 || C / 128 > 65535 || R / 128 > 65535)
     return MOE_ERR_UNSUPPORTED;
+  // the scale bytes are stored as 32-bit words
+  if ((((uintptr_t)scales) | ((uintptr_t)scales_t)) & 3) return MOE_ERR_UNSUPPORTED;
   return quant_weights_mx_launch(W, E, R, C, codes, scales, codes_t, scales_t,
                                  (hipStream_t)stream);
 }

@@ -320,14 +320,19 @@ __global__ __launch_bounds__(256) void quant_rows_mx_kernel(const T* __restrict_
 // column): codes_t [E][C][R], bytes sbt [E][C][R/32].  Thread (rg, cl) =
 // (tid / 32, tid % 32) holds rows 16 rg .. + 15 and columns 4 cl .. + 3: a row
 // block spans the 8 lanes cl / 8 = const (xor shuffles 1, 2, 4), a column
-// block the row groups rg = 2 g, 2 g + 1 (lanes l and l + 32, xor 32).
+// block the row groups rg = 2 g, 2 g + 1 (lanes l and l + 32, xor 32).  The
+// scale bytes leave as aligned 32-bit words (a row's four 32-column blocks,
+// gathered by shuffles; a column's four 32-row blocks, through LDS) rather
+// than as single bytes.
 __global__ __launch_bounds__(256) void quant_weights_mx_kernel(
     const float* __restrict__ W, int R, int C, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ sb, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ sbt) {
   __shared__ __attribute__((aligned(16))) uint8_t tt[128][144];  // [col][row], padded rows
+  __shared__ __attribute__((aligned(4))) uint8_t cs[128][4];       // column scales [col][32-row block]
   const int cb = blockIdx.x, rb = blockIdx.y, e = blockIdx.z;
   const int tid = threadIdx.x;
   const int rg = tid >> 5, cl = tid & 31, col = cl * 4;
+  const int lane = tid & 63, lbase = lane & 32;  // the row's 32 lanes start at lbase
   const size_t mat = (size_t)e * R * C;
   const float* Wt = W + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
   f32x4_t v[16];
@@ -349,7 +354,12 @@ __global__ __launch_bounds__(256) void quant_weights_mx_kernel(
     for (int q = 0; q < 4; ++q) w |= mx_code(v[i][q], inv, z) << (8 * q);
     const int r = rb * 128 + 16 * rg + i;
     *(uint32_t*)(Ct + (size_t)(16 * rg + i) * C + col) = w;
-    if ((cl & 7) == 0) sb[((size_t)e * R + r) * (C / 32) + cb * 4 + (cl >> 3)] = (uint8_t)(s + 127);
+    // the row's four scale bytes (lanes lbase + 0, 8, 16, 24) as one word
+    const uint32_t sbyte = (uint32_t)(s + 127);
+    uint32_t sw = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sw |= ((uint32_t)__shfl((int)sbyte, lbase + 8 * k, 64) & 0xffu) << (8 * k);
+    if (cl == 0) *(uint32_t*)&sb[((size_t)e * R + r) * (C / 32) + cb * 4] = sw;
   }
   // column blocks: rows 32 g .. 32 g + 31 with g = rg / 2
   uint32_t colw[4][4] = {};  // [column q][word w]: rows 16 rg + 4 w .. + 3
@@ -364,14 +374,16 @@ __global__ __launch_bounds__(256) void quant_weights_mx_kernel(
     const bool z = m == 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) colw[q][i >> 2] |= mx_code(v[i][q], inv, z) << (8 * (i & 3));
-    if ((rg & 1) == 0)
-      sbt[((size_t)e * C + (size_t)cb * 128 + col + q) * (R / 32) + rb * 4 + (rg >> 1)] =
-          (uint8_t)(s + 127);
+    if ((rg & 1) == 0) cs[col + q][rg >> 1] = (uint8_t)(s + 127);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     *(u32x4_t*)&tt[col + q][16 * rg] = u32x4_t{colw[q][0], colw[q][1], colw[q][2], colw[q][3]};
   __syncthreads();
+  // a column's four 32-row scales of this tile as one word
+  if (tid < 128)
+    *(uint32_t*)&sbt[((size_t)e * C + (size_t)cb * 128 + tid) * (R / 32) + rb * 4] =
+        *(const uint32_t*)&cs[tid][0];
   uint8_t* Tt = codes_t + mat + (size_t)cb * 128 * R + (size_t)rb * 128;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
