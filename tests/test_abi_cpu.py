@@ -207,3 +207,15 @@ def test_fp8_memory_efficient_workspace():
         sh = make_shape(64, 256, 8, 2, 256, 0, dtype)
         assert moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD_ROWSCALED) == \
             moe_workspace_bytes(sh, N.MOE_WS_LAYER_BWD) + -(-128 * 1 * 4 // 256) * 256
+
+
+def test_probe_mfma_validation():
+    """The matrix-core probe checks its arguments before it touches the device."""
+    f, khz = C.c_int64(0), C.c_int64(0)
+    lib = N.lib()
+    assert lib.moe_probe_mfma(N.MOE_BF16, 16, None, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_INVALID
+    assert lib.moe_probe_mfma(N.MOE_BF16, 16, P, P, None, C.byref(khz), None) == N.MOE_ERR_INVALID
+    assert lib.moe_probe_mfma(N.MOE_BF16, 0, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_INVALID
+    assert lib.moe_probe_mfma(N.MOE_BF16, 1 << 25, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_INVALID
+    assert lib.moe_probe_mfma(N.MOE_F32, 16, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_UNSUPPORTED
+    assert lib.moe_probe_mfma(N.MOE_MXFP8, 16, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_UNSUPPORTED
