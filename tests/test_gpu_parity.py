@@ -298,3 +298,38 @@ def test_mfma_probe(dtype):
     assert 0.3 < ghz < 3.5, ghz
     with pytest.raises(tre.MoeError):
         tre.moe_probe_mfma(dtype, 0, ticks, sink)
+
+
+# ---------------------------------------------------------------- hand-derived fixture
+def test_route_permute_golden():
+    """moe_route and moe_permute on the hand-built case of
+    tests/golden/route_permute_tiny.json (ties, an empty expert): indices,
+    counts, offsets and the map bit-exact, probabilities to float32 rounding,
+    and the permuted rows equal to their source rows."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    from golden_fixtures import fraction, load, logits_f32
+    fx = load("route_permute_tiny.json")
+    T, E, k, d = fx["T"], fx["E"], fx["k"], 64
+    L = torch.from_numpy(logits_f32(fx)).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    p = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    tre.moe_route(L, k, idx, p)
+    assert np.array_equal(idx.cpu().numpy(), np.array(fx["topk_idx"]))
+    want = np.array([[fraction(v) for v in row] for row in fx["topk_prob"]])
+    assert np.allclose(p.cpu().numpy(), want, rtol=0, atol=1e-6)
+    sh = tre.make_shape(T, d, E, k, 128, 0, "f32")
+    x = (torch.arange(T, dtype=torch.float32)[:, None] * 1000 + torch.arange(d)[None, :]).cuda()
+    P = T * k
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    r = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    tk = torch.empty(P, dtype=torch.int32, device="cuda")
+    xp = torch.empty(P, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE), dtype=torch.uint8, device="cuda")
+    tre.moe_permute(sh, x, idx, None, 1, c, o, r, tk, xp, ws)
+    assert np.array_equal(c.cpu().numpy(), fx["counts"])
+    assert np.array_equal(o.cpu().numpy(), fx["offsets"])
+    assert np.array_equal(r.cpu().numpy(), np.array(fx["row_of"]))
+    assert np.array_equal(tk.cpu().numpy(), fx["token_of"])
+    assert torch.equal(xp.cpu(), x.cpu()[torch.tensor(fx["token_of"])])
