@@ -44,8 +44,15 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// SiLU and the logistic function with gfx950's reciprocal (v_rcp_f32, about
+// 1 ulp) in place of an IEEE division: the fused SwiGLU epilogues evaluate
+// them for every output element, and the results are rounded to bf16 (or
+// compared at 1e-4 in fp32) far above that error.  Measured on the Qwen3
+// shape: fc2 dgrad 2 %, fc1 forward 0.5-1.3 % faster.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
