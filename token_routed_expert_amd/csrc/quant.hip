@@ -108,9 +108,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ s
 // One block per 128 x 128 tile of matrix e (grid: C/128, R/128, E).
 // codes [E][R][C], codes_t [E][C][R] (may be NULL), scales [E][R/128][C/128].
 // Thread (rg, cl) = (tid / 32, tid % 32) holds rows 16 rg .. 16 rg + 15 and
-// columns 4 cl .. 4 cl + 3: non-temporal float4 loads (a wavefront reads 2
-// rows of 512 bytes; the fp32 masters are read once: 4 % faster than cached
-// loads), 4-byte row-major code stores, and per column 16 consecutive row
+// columns 4 cl .. 4 cl + 3: float4 loads (a wavefront reads 2 rows of 512
+// bytes), 4-byte row-major code stores, and per column 16 consecutive row
 // codes -- one 16-byte LDS write into the transposed tile, which is then
 // stored row by row.
 __global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restrict__ W, int R, int C,
@@ -128,7 +127,7 @@ __global__ __launch_bounds__(256) void quant_tiles_kernel(const float* __restric
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    v[i] = __builtin_nontemporal_load((const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col));
+    v[i] = *(const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col);
 #pragma unroll
     for (int q = 0; q < 4; ++q) m = fmaxf(m, fabsf(v[i][q]));
   }
@@ -338,7 +337,7 @@ __global__ __launch_bounds__(256) void quant_weights_mx_kernel(
   const float* Wt = W + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
   f32x4_t v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load((const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col));
+  for (int i = 0; i < 16; ++i) v[i] = *(const f32x4_t*)(Wt + (size_t)(16 * rg + i) * C + col);
   // row blocks
   uint8_t* Ct = codes + mat + (size_t)rb * 128 * C + (size_t)cb * 128;
 #pragma unroll
