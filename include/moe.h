@@ -459,13 +459,15 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
  * MXFP8 expert GEMMs
  * ------------------
  * The pages run the Blackwell results in MXFP8 (French summary, section 2 E;
- * Spanish summary, section 2.4) and name it without a definition; the format
- * is the OCP Microscaling one.  Every block of 32 consecutive values along a
- * product's contraction axis has one scale 2^s, stored as the E8M0 byte
- * s + 127, with s the smallest integer such that max|v| <= 448 * 2^s (the
- * scale rounded up, so nothing saturates; s clamped to [-127, 127]; an
+ * Spanish summary, section 2.4) and name it without a definition; the
+ * storage is the OCP Microscaling one.  Every block of 32 consecutive values
+ * along a product's contraction axis has one scale 2^s, stored as the E8M0
+ * byte s + 127, with s the smallest integer such that max|v| <= 448 * 2^s
+ * (the scale rounded up, so nothing saturates; s clamped to [-127, 127]; an
  * all-zero block has s = 0 and +0 codes); codes are E4M3FN(v * 2^-s), round
- * to nearest even.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0
+ * to nearest even.  This scale rule departs from the OCP MX v1.0 reference
+ * conversion (s = floor(log2 max|v|) - 8 with elements above 448 clamped),
+ * which can clip a block's largest element by up to 12.5 %.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0
  * scale per lane, which is one 32-value block of one row, so the scales go
  * straight into the matrix instruction.  Scale bytes are stored row-major next
  * to the codes they scale:

@@ -5,14 +5,20 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 The pages name MXFP8 as the FP8 recipe of the Blackwell runs, beside the
 blockwise recipe on Hopper ("Scalable Training of Mixture-of-Experts Models
 with Megatron Core", gist.science French technical summary, section 2 E;
-Spanish summary, section 2.4), without a definition.  The format is the OCP
-Microscaling one: blocks of 32 consecutive values along the contraction axis
-share an 8-bit exponent-only scale 2^s (E8M0 byte s + 127), elements are OCP
-E4M3FN.  Reading used for the scale and the codes of a block of fp32 values:
+Spanish summary, section 2.4), without a definition.  The storage follows
+the OCP Microscaling format: blocks of 32 consecutive values along the
+contraction axis share an 8-bit exponent-only scale 2^s (E8M0 byte s + 127),
+elements are OCP E4M3FN.  Reading used for the scale and the codes of a block
+of fp32 values:
 
 * amax = max |v|; s is the smallest integer with amax <= 448 * 2^s (the
   scale rounded up to a power of two, so no element saturates), clamped to
-  [-127, 127]; an all-zero block has s = 0 and every code +0;
+  [-127, 127]; an all-zero block has s = 0 and every code +0.  This departs
+  from the OCP MX v1.0 reference conversion, which takes s = floor(log2 amax)
+  - 8 and clamps elements above 448: with that rule a block whose largest
+  magnitude lies in (448, 512) * 2^s loses up to 12.5 % on it, where the
+  rounded-up scale keeps every element within half an e4m3 step, at the
+  cost of one binade of resolution for blocks with amax in (1.75, 2) * 2^E;
 * code(v) = E4M3(v * 2^-s), round to nearest, ties to even (the product is
   exact in fp32 except where it falls below 2^-126, where every code is 0);
   the sign is kept, so -0 and tiny negatives give 0x80;
@@ -23,8 +29,8 @@ Block layouts: rows of activations and gradients (xp, h, dO, [da db]) in 1 x
 blocks along its rows (the operand of the data-gradient products) and once
 in 32 x 1 blocks along its columns, stored transposed (the operand of the
 forward products); weight-gradient operands in 32-row blocks per column,
-restarting at every expert's first row, stored transposed in the padded
-token-block layout (expert e's rows start at column 128 * blk[e]).
+restarting at every expert's first row (codes keep the operand's [P][C]
+shape; one scale per block and column).
 
 Every GEMM of dequantised operands is a plain fp64 product (the hardware's
 block-scaled MFMA multiplies exact block sums by 2^(s_A + s_B)).
@@ -105,50 +111,42 @@ def dequant_mx_weights(codes, sbytes):
 
 
 def quant_mx_token_blocks(X, offsets):
-    """Weight-gradient operand X [P][C]: per column, 32-row blocks of each
-    expert's rows (restarting at the expert's first row).  Returns codes_t
-    [C][128 cap] in the padded token-block layout (cap = number of 128-row
-    blocks, expert e from block blk[e] on) and scale bytes [cap][C][4], byte
-    g of (b, c) for rows 32 g .. 32 g + 31 of block b; padding codes are 0 and
-    padding blocks have s = 0."""
+    """Weight-gradient operand X [P][C] (rows grouped by expert as `offsets`
+    gives them): in every column, each expert's rows are cut into blocks of
+    32 consecutive rows starting at the expert's first row (the last block
+    short) and every block gets its own scale.
+
+    Returns codes [P][C] (row r stays row r) and scale bytes [NB][C], where
+    NB = sum_e ceil(m_e / 32) and block b of expert e is row
+    token_block_offsets(offsets, 32)[e] + b.  A short block is quantised as
+    its rows alone (absent rows contribute nothing to its amax)."""
     X = np.asarray(X, dtype=np.float32)
     P, C = X.shape
-    blk = token_block_offsets(offsets, 128)
-    cap = int(blk[-1])
-    codes_t = np.zeros((C, 128 * cap), dtype=np.uint8)
-    sb_t = np.full((C, 4 * cap), 127, dtype=np.uint8)       # [C][32-row block]
+    b32 = token_block_offsets(offsets, MX_BLOCK)
+    codes = np.zeros((P, C), dtype=np.uint8)
+    sb = np.full((int(b32[-1]), C), 127, dtype=np.uint8)
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        m = r1 - r0
-        if m == 0:
-            continue
-        n32 = (m + MX_BLOCK - 1) // MX_BLOCK
-        seg = np.zeros((n32 * MX_BLOCK, C), dtype=np.float32)   # zero rows pad the last block
-        seg[:m] = X[r0:r1]
-        codes, sb = _mx_groups(seg.T.reshape(C, n32, MX_BLOCK))
-        c0 = 128 * int(blk[e])
-        codes_t[:, c0:c0 + m] = codes.reshape(C, n32 * MX_BLOCK)[:, :m]
-        sb_t[:, 4 * int(blk[e]):4 * int(blk[e]) + n32] = sb
-    return codes_t, np.ascontiguousarray(sb_t.reshape(C, cap, 4).transpose(1, 0, 2))
+        for b, s in enumerate(range(r0, r1, MX_BLOCK)):
+            t = min(s + MX_BLOCK, r1)
+            seg = np.zeros((C, MX_BLOCK), dtype=np.float32)    # absent rows are zero
+            seg[:, :t - s] = X[s:t].T
+            c_blk, s_blk = _mx_groups(seg)                     # one block per column
+            codes[s:t] = c_blk[:, :t - s].T
+            sb[int(b32[e]) + b] = s_blk
+    return codes, sb
 
 
-def dequant_mx_token_blocks(codes_t, sb_t, offsets):
-    """Values [P][C] of the token-block operand (scale bytes [cap][C][4])."""
-    blk = token_block_offsets(offsets, 128)
-    C = codes_t.shape[0]
-    sb_t = np.asarray(sb_t).transpose(1, 0, 2).reshape(C, -1)  # [C][32-row block]
-    P = int(offsets[-1])
-    out = np.zeros((P, C))
-    vals = e4m3_decode(codes_t)
-    sv = _scale_values(sb_t)
+def dequant_mx_token_blocks(codes, sb, offsets):
+    """Values [P][C] of the token-block operand (codes [P][C], bytes [NB][C])."""
+    vals = e4m3_decode(codes)
+    out = np.zeros_like(vals)
+    b32 = token_block_offsets(offsets, MX_BLOCK)
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        m = r1 - r0
-        if m == 0:
-            continue
-        c0 = 128 * int(blk[e])
-        i = np.arange(m)
-        out[r0:r1] = (vals[:, c0 + i] * sv[:, 4 * int(blk[e]) + i // MX_BLOCK]).T
+        for b, s in enumerate(range(r0, r1, MX_BLOCK)):
+            t = min(s + MX_BLOCK, r1)
+            out[s:t] = vals[s:t] * _scale_values(sb[int(b32[e]) + b])[None, :]
     return out
 
 

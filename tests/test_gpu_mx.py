@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import device_layout
 import oracle
 from moe_workloads import VARIANTS, Workload, make_inputs, to_f64
 
@@ -101,8 +102,9 @@ def test_quantize_token_blocks_mx_bit_exact(gather):
     rq, rs = oracle.quant_mx_token_blocks(vals, off)
     NB = int(oracle.token_block_offsets(off)[-1])
     assert np.array_equal(blk.cpu().numpy(), oracle.token_block_offsets(off))
-    assert np.array_equal(u8(codes_t)[:, :128 * NB], rq)
-    assert np.array_equal(u8(sbt)[:NB], rs)
+    # the device's padded, transposed layout taken apart (indexing only)
+    assert np.array_equal(device_layout.token_block_codes(u8(codes_t)[:, :128 * NB], off), rq)
+    assert np.array_equal(device_layout.mx_token_block_scales(u8(sbt)[:NB], off), rs)
 
 
 def test_permute_mx_bit_exact():

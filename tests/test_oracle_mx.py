@@ -115,34 +115,34 @@ def small_offsets():
 
 
 def test_token_block_layout():
+    """Each 32-row block of each expert, per column, is quantised alone:
+    compare with quant_mx_rows on the block's values, built here by slicing."""
     off = small_offsets()
     P, C = int(off[-1]), 64
     X = RNG.standard_normal((P, C)).astype(np.float32)
-    qt, sbw = quant_mx_token_blocks(X, off)
-    blk = token_block_offsets(off, 128)
-    cap = int(blk[-1])
-    assert qt.shape == (C, 128 * cap) and sbw.shape == (cap, C, 4)
-    sbt = sbw.transpose(1, 0, 2).reshape(C, 4 * cap)         # [C][32-row block]
+    X[100:132, 5] = 0.0                                      # an all-zero block (expert 2's first)
+    q, sb = quant_mx_token_blocks(X, off)
+    b32 = token_block_offsets(off, 32)
+    assert q.shape == (P, C) and sb.shape == (int(b32[-1]), C)
+    assert list(b32) == [0, 4, 4, 8, 10, 11]                 # ceil(m_e / 32) = 4, 0, 4, 2, 1
     for e in range(len(off) - 1):
         r0, r1 = int(off[e]), int(off[e + 1])
-        c0 = 128 * int(blk[e])
-        nb = (r1 - r0 + 127) // 128
-        for g in range(4 * nb):
-            rows = slice(r0 + 32 * g, min(r0 + 32 * g + 32, r1))
-            n = max(0, rows.stop - rows.start)
-            for c in (0, 17, 63):
-                if n == 0:
-                    assert sbt[c, 4 * int(blk[e]) + g] == 127
-                    assert (qt[c, c0 + 32 * g:c0 + 32 * g + 32] == 0).all()
-                    continue
+        for g, s in enumerate(range(r0, r1, 32)):
+            t = min(s + 32, r1)
+            for c in (0, 5, 17, 63):
                 seg = np.zeros(32, np.float32)
-                seg[:n] = X[rows, c]
+                seg[:t - s] = X[s:t, c]
                 c1, s1 = quant_mx_rows(seg[None, :])
-                assert sbt[c, 4 * int(blk[e]) + g] == s1[0, 0]
-                assert np.array_equal(qt[c, c0 + 32 * g:c0 + 32 * g + n], c1[0, :n])
-                assert (qt[c, c0 + 32 * g + n:c0 + 32 * g + 32] == 0).all()
-    D = dequant_mx_token_blocks(qt, sbw, off)
+                assert sb[int(b32[e]) + g, c] == s1[0, 0]
+                assert np.array_equal(q[s:t, c], c1[0, :t - s])
+    assert sb[4, 5] == 127 and not q[100:132, 5].any()       # zero block: s = 0, +0 codes
+    D = dequant_mx_token_blocks(q, sb, off)
     assert np.abs(D - X).max() <= np.abs(X).max() * 2.0 ** -4
+    # blocks restart at each expert: expert 3 (rows 228..260) has blocks
+    # 228..259 and 260, not the fixed-stride blocks 224..255 and 256..287
+    assert off[3] == 228 and off[4] == 261
+    alt_q, alt_s = quant_mx_rows(np.ascontiguousarray(X[224:256].T))
+    assert not (np.array_equal(sb[8], alt_s[:, 0]) and np.array_equal(q[228:256], alt_q.T[4:]))
 
 
 def grid_token_operand(P, C, off, rng):
