@@ -260,6 +260,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
   });
   if constexpr (RS && OP == OP_FC2_DGRAD) {
     constexpr int WAVES_N = 256 / WN;
+    // the partials were written with plain LDS stores, and other wavefronts
+    // read them: they must have completed before the (fence-free) barrier
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     block_barrier();
     const int t = (int)threadIdx.x;
     if (t < 256 && t < ti.rows) {
