@@ -30,7 +30,10 @@
  *    row, so permuted buffers always have exactly P rows -- the worst case is
  *    known on the host; cf. the hyper.ai article on Hybrid-EP, which reserves
  *    buffers for the worst case).  Limits: 1 <= k <= E <= 256, T >= 1,
- *    P < 2^31.  The bf16 expert GEMMs need d and f to be multiples of 128.
+ *    P < 2^31.  The bf16 expert GEMMs need d and f to be multiples of 128,
+ *    and P * max(d, 2f) * 2 and d * f * 2 below 2^32 bytes (the shared
+ *    expert: T in place of P, f_shared in place of f); outside that they
+ *    return MOE_ERR_UNSUPPORTED.
  *  - Expert weights: W1, W3 are [E][d][f], W2 is [E][f][d]; expert e maps a
  *    row x to o = (silu(x W1_e) * (x W3_e)) W2_e with silu(z) = z / (1+e^-z).
  *  - Dtypes: MOE_F32 (every tensor fp32), MOE_BF16 (x, weights, outputs and
@@ -86,13 +89,17 @@ typedef enum {
 /*
  * moe_route -- top-k routing (Spanish summary, section 2.1: a router assigns
  * each token to its k best experts).
- *   logits    fp32 [T][E], finite values (behaviour on NaN is unspecified).
+ *   logits    fp32 [T][E].
  *   topk_idx  out int32 [T][k]: the k largest logits of the token in
  *             descending order; equal logits (IEEE equality, -0 == +0) are
- *             ordered by lower expert index first.
+ *             ordered by lower expert index first.  A NaN logit ranks below
+ *             every number (-inf included), NaNs among themselves by index,
+ *             so every token always gets k distinct experts in [0, E).
  *   topk_prob out fp32 [T][k]: softmax over the k selected logits,
- *             p_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), summed in j order.
- * Errors: MOE_ERR_INVALID for null pointers, T < 1, k < 1, k > E, E > 256.
+ *             p_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), summed in j order
+ *             (NaN for every pick of a token whose picks include a NaN).
+ * Errors: MOE_ERR_INVALID for null pointers, T < 1, k < 1 or k > E;
+ * MOE_ERR_UNSUPPORTED for E > 256 or T * k >= 2^31.
  */
 int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
               int32_t* topk_idx, float* topk_prob, void* stream);
@@ -107,12 +114,15 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
  *       row_of   out int32 [T][k] destination row of assignment (t, j);
  *       token_of out int32 [P]   source token of each row;
  *     rows of one expert ascend by token index (a stable counting sort), so
- *     the map is unique.  Needs ws_bytes >= moe_workspace_bytes(sh,
- *     MOE_WS_PERMUTE).
+ *     the map is unique.  An index outside [0, E) gets no row: its row_of
+ *     entry is -1 and it is not counted (offsets[E] is then below P and the
+ *     rows from offsets[E] on are not written).  Needs ws_bytes >=
+ *     moe_workspace_bytes(sh, MOE_WS_PERMUTE).
  *   build_map = 0: uses the caller's row_of; counts, offsets, token_of, ws
  *     may be NULL.
- *   src [T][d] and dst [P][d] are in sh->dtype.  row_scale NULL: dst rows are
- *   bit copies of src rows.  row_scale fp32 [T][k] non-NULL: dst[row_of[t][j]]
+ *   src [T][d] and dst [P][d] are in sh->dtype.  Assignments whose row_of
+ *   entry lies outside [0, P) are skipped (here and in every call that reads
+ *   row_of).  row_scale NULL: dst rows are bit copies of src rows.  row_scale fp32 [T][k] non-NULL: dst[row_of[t][j]]
  *   = round(row_scale[t][j] * src[t]) computed in fp32 (the backward of the
  *   weighted combine, dO = p * dY).
  */

@@ -32,8 +32,11 @@ def route(logits: np.ndarray, k: int):
     Per token t the experts are fully sorted by the key (-logit, expert index)
     with a stable sort, so equal logits (IEEE equality, -0 == +0) keep the
     lower expert index first; the first k form idx[t].  Selection compares the
-    stored fp32 logits.  Then, with m the largest selected logit,
-    p[t, j] = exp(l_j - m) / sum_i exp(l_i - m), all in fp64.
+    stored fp32 logits.  A NaN logit sorts after every number (-inf included;
+    NaNs among themselves by index), which is NumPy's ordering of NaN, so the
+    k picks are always k distinct experts.  Then, with m the largest selected
+    logit, p[t, j] = exp(l_j - m) / sum_i exp(l_i - m), all in fp64 (NaN for
+    every pick of a token that has a NaN among its picks).
 
     Returns idx int32 [T][k] (descending logit, lower index first on ties)
     and p float64 [T][k].

@@ -48,6 +48,100 @@ def test_route_bit_exact(E, k, tied):
     assert np.abs(prob.cpu().numpy() - rp).max() <= PROB_TOL
 
 
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 8), (128, 8), (256, 4)])
+def test_route_nan_logits_give_valid_experts(E, k):
+    """NaN logits rank below every number: indices bit-exact against the
+    oracle, always k distinct experts in [0, E); the map built from them is
+    the oracle's."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    T = 700
+    g = torch.Generator().manual_seed(E + k)
+    L = torch.randn(T, E, generator=g)
+    L[0] = float("nan")                                    # all NaN
+    L[1, ::2] = float("nan")                               # half NaN
+    L[2, :] = float("-inf")
+    L[2, 1::3] = float("nan")                              # -inf and NaN mixed
+    L[5::11, 0] = float("nan")
+    L[7::13, E - 1] = float("nan")
+    L[9::17, : max(1, E - k + 1)] = float("nan")           # at most k - 1 numbers left
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    prob = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    tre.moe_route(L.cuda(), k, idx, prob)
+    ridx, rp = oracle.route(L.numpy(), k)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, ridx)
+    assert (gi >= 0).all() and (gi < E).all()
+    assert all(len(set(r)) == k for r in gi)
+    gp = prob.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(gp), np.isnan(rp))
+    fin = ~np.isnan(rp)
+    assert np.abs(gp[fin] - rp[fin]).max() <= PROB_TOL
+    sh = tre.make_shape(T, 64, E, k, 128, 0, "bf16")
+    counts, offsets, row_of, token_of = oracle.permute_map(ridx, E)
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    r = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    tk = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    x = torch.randn(T, 64, generator=g).to(torch.bfloat16).cuda()
+    xp = torch.empty(T * k, 64, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE), dtype=torch.uint8, device="cuda")
+    tre.moe_permute(sh, x, idx, None, 1, c, o, r, tk, xp, ws)
+    assert np.array_equal(c.cpu().numpy(), counts) and np.array_equal(r.cpu().numpy(), row_of)
+    assert np.array_equal(tk.cpu().numpy(), token_of)
+
+
+def test_permute_skips_indices_outside_the_experts():
+    """An index outside [0, E) gets row_of = -1 and no row; counts and rows
+    are those of the valid assignments in the canonical order; the row moves
+    and the combine skip the assignment (rows from offsets[E] on stay as they
+    were)."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    T, E, k, d = 300, 16, 4, 128
+    rng = np.random.default_rng(4)
+    idx_np = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.random((T, k)) < 0.1
+    idx_np[bad] = rng.choice(np.array([-1, E, E + 7, 1 << 30, -(1 << 30)], dtype=np.int32), bad.sum())
+    valid = (idx_np >= 0) & (idx_np < E)
+    flat, vflat = idx_np.reshape(-1), valid.reshape(-1)
+    pos = np.nonzero(vflat)[0]
+    order = pos[np.argsort(flat[pos], kind="stable")]       # token-major, then by expert
+    nv = len(pos)
+    ref_row = np.full(T * k, -1, np.int64)
+    ref_row[order] = np.arange(nv)
+    ref_counts = np.bincount(flat[pos], minlength=E)
+    ref_tok = order // k
+    sh = tre.make_shape(T, d, E, k, 128, 0, "bf16")
+    x = torch.randn(T, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    r = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    tk = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    xp = torch.full((T * k, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(tre.moe_workspace_bytes(sh, N.MOE_WS_PERMUTE), dtype=torch.uint8, device="cuda")
+    tre.moe_permute(sh, x.cuda(), torch.from_numpy(idx_np).cuda(), None, 1, c, o, r, tk, xp, ws)
+    assert np.array_equal(c.cpu().numpy(), ref_counts)
+    assert int(o.cpu()[E]) == nv
+    assert np.array_equal(r.cpu().numpy().reshape(-1), ref_row)
+    assert np.array_equal(tk.cpu().numpy()[:nv], ref_tok) and (tk.cpu().numpy()[nv:] == -7).all()
+    xpn = xp.cpu()
+    assert torch.equal(xpn[:nv], x[torch.from_numpy(ref_tok)]) and (xpn[nv:] == 3.0).all()
+    p = torch.rand(T, k, generator=torch.Generator().manual_seed(3))
+    dO = torch.full((T * k, d), 5.0, dtype=torch.bfloat16, device="cuda")
+    tre.moe_permute(sh, x.cuda(), None, p.cuda(), 0, None, None, r, None, dO, None)
+    assert (dO.cpu()[nv:] == 5.0).all()
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    tre.moe_unpermute(sh, xp, r, p.cuda(), None, y)
+    xf = to_f64(x)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            if valid[t, j]:
+                ref[t] += float(p[t, j]) * xf[t]
+    assert_close("combine", to_f64(y), ref, TOL["bf16"] / 4)
+
+
 # ---------------------------------------------------------------- permute / combine
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,E,k,d", [(1, 4, 2, 64), (257, 8, 2, 128), (1000, 128, 8, 256),

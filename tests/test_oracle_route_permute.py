@@ -39,6 +39,43 @@ def test_route_matches_k_round_argmax(T, E, k, tied):
         assert np.allclose(p[t], [v / sum(ex) for v in ex], rtol=0, atol=1e-15)
 
 
+def brute_topk_nan_last(row, k):
+    """k rounds of a pure-Python scan in which a NaN ranks below every
+    number (-inf included) and equal keys keep the lower index."""
+    def key(e):
+        v = row[e]
+        return (0, 0.0) if v != v else (1, v)
+    taken, out = set(), []
+    for _ in range(k):
+        best = None
+        for e in range(len(row)):
+            if e not in taken and (best is None or key(e) > key(best)):
+                best = e
+        taken.add(best)
+        out.append(best)
+    return out
+
+
+def test_route_nan_ranks_last():
+    nan, inf = float("nan"), float("inf")
+    L = np.array([[nan, 1.0, nan, -inf, 0.5, nan],
+                  [nan, nan, nan, nan, nan, nan],
+                  [-inf, nan, -inf, 2.0, nan, -inf],
+                  [0.0, -0.0, nan, 3.0, -inf, 1.0]], dtype=np.float32)
+    for k in (1, 3, 4, 6):
+        idx, p = oracle.route(L, k)
+        for t in range(L.shape[0]):
+            assert list(idx[t]) == brute_topk_nan_last([float(v) for v in L[t]], k)
+            assert len(set(idx[t])) == k and (idx[t] >= 0).all() and (idx[t] < 6).all()
+            picked = L[t, idx[t]]
+            if np.isnan(picked).any():
+                assert np.isnan(p[t]).all()
+            else:
+                assert np.isfinite(p[t]).all() or np.isinf(picked[0])
+    idx, p = oracle.route(L, 3)
+    assert list(idx[0]) == [1, 4, 3] and list(idx[1]) == [0, 1, 2] and list(idx[2]) == [3, 0, 2]
+
+
 def test_route_all_equal_logits():
     for k in (1, 2, 3, 8):
         L = np.full((4, 8), 0.75, dtype=np.float32)

@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
   const unsigned long long lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
-    if ((unsigned)e >= (unsigned)E) continue;
+    if ((unsigned)e >= (unsigned)E) {  // no row for an index outside [0, E)
+      row_of[(size_t)t * k + j] = -1;
+      continue;
+    }
     int before = __popcll(mask[w][e] & lower);
     for (int ww = 0; ww < w; ++ww) before += __popcll(mask[ww][e]);
     const int row = blk[(size_t)e * NB + blockIdx.x] + before;
@@ -149,6 +152,12 @@ __device__ __forceinline__ u32x4_t store_vec<bf16_t>(const float* in) {
                     pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7])};
 }
 
+// Rows outside [0, P) (P = T * k, the grid's token count times k; the map
+// marks an assignment without a row with -1) are skipped by every row move.
+__device__ __forceinline__ bool row_ok(int row, int k) {
+  return (unsigned)row < (unsigned)(gridDim.x * k);
+}
+
 // One block per token; C = 16-byte chunks per row.
 template <typename T, bool SCALED>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __restrict__ src,
@@ -161,11 +170,13 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4_t* __rest
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     const u32x4_t v = __builtin_nontemporal_load(&src[(size_t)t * C + c]);
     if (!SCALED) {
-      for (int j = 0; j < k; ++j) __builtin_nontemporal_store(v, &dst[(size_t)rows[j] * C + c]);
+      for (int j = 0; j < k; ++j)
+        if (row_ok(rows[j], k)) __builtin_nontemporal_store(v, &dst[(size_t)rows[j] * C + c]);
     } else {
       float x[N], y[N];
       load_vec<T>(v, x);
       for (int j = 0; j < k; ++j) {
+        if (!row_ok(rows[j], k)) continue;
         const float p = scale[(size_t)t * k + j];
 #pragma unroll
         for (int i = 0; i < N; ++i) y[i] = p * x[i];
@@ -189,6 +200,7 @@ __global__ __launch_bounds__(512) void gather_rows_kernel(const u32x4_t* __restr
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
+      if (!row_ok(rows[j], k)) continue;
       float v[N];
       load_vec<T>(__builtin_nontemporal_load(&src[(size_t)rows[j] * C + c]), v);
       if (WEIGHTED) {
@@ -222,11 +234,13 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(const u32x4_t* __rest
   const int32_t* rows = row_of + (size_t)t * k;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     const u32x4_t v = __builtin_nontemporal_load(&codes[(size_t)t * C + c]);
-    for (int j = 0; j < k; ++j) __builtin_nontemporal_store(v, &dst_codes[(size_t)rows[j] * C + c]);
+    for (int j = 0; j < k; ++j)
+      if (row_ok(rows[j], k)) __builtin_nontemporal_store(v, &dst_codes[(size_t)rows[j] * C + c]);
   }
   for (int c = threadIdx.x; c < KB; c += blockDim.x) {
     const float v = scales[(size_t)t * KB + c];
-    for (int j = 0; j < k; ++j) dst_scales[(size_t)rows[j] * KB + c] = v;
+    for (int j = 0; j < k; ++j)
+      if (row_ok(rows[j], k)) dst_scales[(size_t)rows[j] * KB + c] = v;
   }
 }
 

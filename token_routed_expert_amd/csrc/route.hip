@@ -9,8 +9,10 @@
 // a lane-local best, then a butterfly (xor-shuffle) reduction inside the
 // group; the winner's owner marks it taken.  The order key is (logit desc,
 // expert asc), so equal logits go to the lower expert index; +0 and -0 are
-// equal under the float comparison.  The result is the same as a full stable
-// sort of the row, independent of lane order.
+// equal under the float comparison.  A NaN logit ranks below every number
+// (-inf included), NaNs among themselves by index, so every token always gets
+// k distinct experts in [0, E) whatever its logits hold.  The result is the
+// same as a full stable sort of the row, independent of lane order.
 #include "common.h"
 #include "internal.h"
 
@@ -18,7 +20,10 @@ namespace tre {
 
 namespace {
 
+// (v, e) ranks before (bv, be): larger logit, then lower index; NaN last.
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+  if (v != v) return bv != bv && e < be;  // NaN only beats a NaN of higher index
+  if (bv != bv) return true;              // any number beats NaN
   return v > bv || (v == bv && e < be);
 }
 
@@ -48,7 +53,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   int sel_e = 0;
   float first = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
+    // the sentinel (NaN, INT_MAX) loses to every candidate, NaN logits included
+    float bv = __builtin_nanf("");
     int be = 0x7fffffff;
 #pragma unroll
     for (int v = 0; v < V; ++v)

@@ -92,10 +92,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restr
       if (jj < nj) {
         const int row = row_of[(size_t)t * k + j0 + jj];
         const float p = prob[(size_t)t * k + j0 + jj];
+        // an assignment without a row (outside [0, T k)) moves nothing; its dprob is 0
+        const bool live = (unsigned)row < (unsigned)(gridDim.x * k);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
           const int c = tid + q * 256;
-          if (c < C) {
+          if (live && c < C) {
             float ov[N], y[N];
             vec8<T>(__builtin_nontemporal_load(&o[(size_t)row * C + c]), ov);
 #pragma unroll
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void row_probs_kernel(const int32_t* __restric
                                                         const float* __restrict__ prob, int n,
                                                         float* __restrict__ row_prob) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) row_prob[row_of[i]] = prob[i];
+  if (i < n && (unsigned)row_of[i] < (unsigned)n) row_prob[row_of[i]] = prob[i];
 }
 
 // out[i] = sum_nt part[r * NT + nt] with r = row_of[i] (or r = i without a map)
@@ -302,9 +304,10 @@ __global__ __launch_bounds__(256) void dp_rows_kernel(const float* __restrict__ 
                                                       float* __restrict__ out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const size_t r = row_of ? (size_t)row_of[i] : (size_t)i;
+  const int r = row_of ? row_of[i] : i;
   float s = 0.0f;
-  for (int nt = 0; nt < NT; ++nt) s += part[r * NT + nt];
+  if ((unsigned)r < (unsigned)n)  // an assignment without a row gets 0
+    for (int nt = 0; nt < NT; ++nt) s += part[(size_t)r * NT + nt];
   out[i] = s;
 }
 
