@@ -102,6 +102,36 @@ def test_gemm_validation():
     assert lib.moe_unpermute(C.byref(bad), P, P, None, None, P, None) == N.MOE_ERR_UNSUPPORTED
 
 
+def test_gemm_32bit_ranges():
+    """bf16 expert GEMMs refuse shapes whose per-expert byte ranges reach 2^32
+    (P * max(d, 2f) * 2 or d * f * 2) before looking at any pointer."""
+    lib = N.lib()
+    big_rows = make_shape(1 << 19, 512, 8, 8, 128, 0, "bf16")      # P * d * 2 = 2^32
+    ok_rows = make_shape(1 << 19, 256, 8, 8, 128, 0, "bf16")       # P * 2f * 2 = 2^31
+    big_ab = make_shape(1 << 19, 128, 8, 8, 256, 0, "bf16")        # P * 2f * 2 = 2^32
+    big_w = make_shape(4, 65536, 8, 2, 32768, 0, "bf16")           # d * f * 2 = 2^32
+    for sh, expect in ((big_rows, N.MOE_ERR_UNSUPPORTED), (big_ab, N.MOE_ERR_UNSUPPORTED),
+                       (big_w, N.MOE_ERR_UNSUPPORTED), (ok_rows, N.MOE_ERR_INVALID)):
+        assert lib.moe_grouped_gemm_fwd(C.byref(sh), None, P, P, P, P, P, P, P, None, 0,
+                                        None) == expect
+        assert lib.moe_grouped_gemm_bwd(C.byref(sh), None, P, P, P, P, P, P, P, P, P, P, P, P, None,
+                                        0, None) == expect
+        assert lib.moe_grouped_gemm_fwd_rowscaled(C.byref(sh), None, P, P, P, P, P, P, P, P,
+                                                  None) == expect
+        io = N.moe_layer_io()
+        assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 20, None) == expect
+        assert lib.moe_layer_bwd(C.byref(sh), C.byref(io), P, 1 << 20, None) == expect
+    # the shared expert runs over all T tokens: T * 2 f_s * 2 = 2^33, while the
+    # routed experts' P * max(d, 2f) * 2 = 2^25 is fine
+    sh = make_shape(1 << 16, 128, 4, 1, 128, 1 << 15, "bf16")
+    io = N.moe_layer_io()
+    assert lib.moe_layer_fwd(C.byref(sh), C.byref(io), P, 1 << 20, None) == N.MOE_ERR_UNSUPPORTED
+    # fp32 layers address with 64-bit offsets: no such limit
+    sh = make_shape(1 << 19, 512, 8, 8, 128, 0, "f32")
+    assert lib.moe_grouped_gemm_fwd(C.byref(sh), None, P, P, P, P, P, P, P, None, 0,
+                                    None) == N.MOE_ERR_INVALID
+
+
 def test_layer_validation():
     lib = N.lib()
     sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")

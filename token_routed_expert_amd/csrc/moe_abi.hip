@@ -39,8 +39,19 @@ int check_shape(const moe_shape* sh) {
   return MOE_OK;
 }
 
-int check_gemm_dims(const moe_shape* sh, int64_t f) {
+// Expert GEMM dimensions for `rows` permuted rows (P, or T for the shared
+// expert) and FFN width f.  The bf16 kernels address their operands through
+// 32-bit buffer ranges and offsets: a weight-gradient tile spans all rows of
+// one expert (up to `rows`) of xp / dO ([.][d]) or dab ([.][2f]), and a
+// forward or data-gradient tile one expert's d x f weight matrix.  Shapes
+// where those byte counts reach 2^32 are refused rather than read wrapped.
+int check_gemm_dims(const moe_shape* sh, int64_t rows, int64_t f) {
   if (sh->dtype != MOE_F32 && (sh->d % 128 != 0 || f % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (sh->dtype == MOE_BF16) {
+    const int64_t lim = (int64_t)1 << 32;
+    if (rows * std::max(sh->d, 2 * f) * 2 >= lim || sh->d * f * 2 >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -369,7 +380,7 @@ int moe_grouped_gemm_fwd(const moe_shape* sh, const int32_t* offsets, const void
   (void)ws_bytes;
   int st = check_shape(sh);
   if (st) return st;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (is_fp8(sh)) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_fwd_e4m3 / _mx
   if (!offsets || !xp || !W1 || !W3 || !W2 || !ab || !h || !o) return MOE_ERR_INVALID;
   GemmArgs a = expert_args(sh, offsets);
@@ -386,7 +397,7 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   (void)ws_bytes;
   int st = check_shape(sh);
   if (st) return st;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (is_fp8(sh)) return MOE_ERR_UNSUPPORTED;  // moe_grouped_gemm_bwd_e4m3 / _mx
   if (!offsets || !xp || !ab || !h || !dO || !W1 || !W3 || !W2 || !dab || !dXp || !dW1 || !dW3 ||
       !dW2)
@@ -411,7 +422,7 @@ int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
                                    void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!offsets || !xp || !W1 || !W3 || !W2 || !row_prob || !ab || !h || !o) return MOE_ERR_INVALID;
   GemmArgs a = expert_args(sh, offsets);
@@ -428,7 +439,7 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
                                    void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!offsets || !xp || !ab || !h || !dO || !W1 || !W3 || !W2 || !row_prob || !dab || !dXp ||
       !dW1 || !dW3 || !dW2)
@@ -550,7 +561,7 @@ int moe_grouped_gemm_fwd_e4m3(const moe_shape* sh, const int32_t* offsets, const
   int st = check_shape(sh);
   if (st) return st;
   if (sh->dtype != MOE_E4M3) return MOE_ERR_INVALID;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!offsets || !xpq || !xps || !weights_ok(w) || !ab || !h || !o) return MOE_ERR_INVALID;
   return gemm_fwd8(sh, offsets, xpq, xps, wq8_of(w), ab, h, o, ws, ws_bytes, stream, false);
 }
@@ -561,7 +572,7 @@ int moe_grouped_gemm_fwd_mx(const moe_shape* sh, const int32_t* offsets, const u
   int st = check_shape(sh);
   if (st) return st;
   if (sh->dtype != MOE_MXFP8) return MOE_ERR_INVALID;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!offsets || !xpq || !xps || !weights_ok(w) || !ab || !h || !o) return MOE_ERR_INVALID;
   return gemm_fwd8(sh, offsets, xpq, xps, wq8_of(w), ab, h, o, ws, ws_bytes, stream, true);
 }
@@ -574,7 +585,7 @@ int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
   int st = check_shape(sh);
   if (st) return st;
   if (sh->dtype != MOE_E4M3) return MOE_ERR_INVALID;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!offsets || !token_of || !x || !ab || !h || !dO || !weights_ok(w) || !dab || !dXp || !dW1 ||
       !dW3 || !dW2)
     return MOE_ERR_INVALID;
@@ -589,7 +600,7 @@ int moe_grouped_gemm_bwd_mx(const moe_shape* sh, const int32_t* offsets, const i
   int st = check_shape(sh);
   if (st) return st;
   if (sh->dtype != MOE_MXFP8) return MOE_ERR_INVALID;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!offsets || !token_of || !x || !ab || !h || !dO || !weights_ok(w) || !dab || !dXp || !dW1 ||
       !dW3 || !dW2)
     return MOE_ERR_INVALID;
@@ -649,8 +660,8 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if (st) return st;
   if (is_fp8(sh)) return layer_fwd_e4m3(sh, io, ws, ws_bytes, stream);
   if (io && io->memory_efficient) return layer_fwd_rowscaled(sh, io, ws, ws_bytes, stream);
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io || !io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
       !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xp ||
       !io->ab || !io->h || !io->o || !io->y)
@@ -691,8 +702,8 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if (st) return st;
   if (is_fp8(sh)) return layer_bwd_e4m3(sh, io, ws, ws_bytes, stream);
   if (io && io->memory_efficient) return layer_bwd_rowscaled(sh, io, ws, ws_bytes, stream);
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io || !io->dY || !io->W1 || !io->W3 || !io->W2 || !io->topk_prob || !io->offsets ||
       !io->row_of || !io->xp || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX ||
       !io->dW1 || !io->dW3 || !io->dW2)
@@ -734,7 +745,7 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
                    void* stream) {
   int st;
   const bool mx = sh->dtype == MOE_MXFP8;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!io || !(mx ? weights_ok(io->wmx) : weights_ok(io->wq))) return MOE_ERR_INVALID;
   if (!io->logits || !io->x || !io->topk_idx || !io->topk_prob ||
       !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xq || !io->xs ||
@@ -769,7 +780,7 @@ int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
                    void* stream) {
   int st;
   const bool mx = sh->dtype == MOE_MXFP8;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (!io || !(mx ? weights_ok(io->wmx) : weights_ok(io->wq))) return MOE_ERR_INVALID;
   if (!io->dY || !io->x || !io->topk_prob || !io->offsets ||
       !io->row_of || !io->token_of || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp ||
@@ -835,8 +846,8 @@ int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
                         void* stream) {
   int st;
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
       !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xp ||
       !io->ab || !io->h || !io->o || !io->y || !io->row_prob)
@@ -876,8 +887,8 @@ int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
                         void* stream) {
   int st;
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if ((st = check_gemm_dims(sh, sh->f))) return st;
-  if (sh->f_shared && (st = check_gemm_dims(sh, sh->f_shared))) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
+  if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io->dY || !io->W1 || !io->W3 || !io->W2 || !io->offsets || !io->row_of || !io->xp ||
       !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX || !io->dW1 || !io->dW3 ||
       !io->dW2 || !io->row_prob)
