@@ -15,8 +15,10 @@ Prints one JSON line.  `value` is the layer's algorithmic GEMM TFLOP/s over
 the whole step (18*d*f per routed row, plus the shared expert).  `roofline`
 is for the grouped-GEMM kernel (all its launches in a step): algorithmic
 flop / their summed duration, measured with HIP events on the launch stream.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+Every step is timed on its own with HIP events (median and min reported);
+a 512 MiB write between steps, outside the events, leaves nothing of the
+previous step in L2 or the MALL.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload (fp32 and fp64 runs of the same code).
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "e4m3": 5000.0, "mxfp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
 METRIC = "MoE layer fwd+bwd TFLOPS/GPU & % MFMA peak; permute/combine HBM GB/s"
 
 
@@ -368,21 +372,17 @@ def e4m3_expert_fwd_bwd(oracle, X, dO, W1, W3, W2):
     oracle.wgrad_e4m3(X, dab, one)
 
 
-def cpu_baseline(wl, inp, budget_s: float):
-    """The fp64 oracle, unchanged, on a bounded sample: routing and the
-    permutation map of all T tokens, then the SwiGLU forward and backward of
-    whole experts in index order until `budget_s` seconds of expert compute."""
+def _oracle_sample(wl, inp, budget_s: float, dtype):
+    """Routing and the permutation map of all T tokens, then the SwiGLU
+    forward and backward of whole experts in index order until `budget_s`
+    seconds of expert compute, with the oracle's functions on `dtype` arrays
+    (np.float64: the correctness oracle; np.float32: the same code in fp32;
+    fp8 workloads: the oracle's e4m3 / MXFP8 chain, fp64 only)."""
     import numpy as np
     import torch
 
     import oracle
     from moe_workloads import to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     L = inp["logits"].cpu().numpy()
     t0 = time.perf_counter()
     idx, p = oracle.route(L, wl.k)
@@ -406,7 +406,8 @@ def cpu_baseline(wl, inp, budget_s: float):
             (mx_expert_fwd_bwd if wl.dtype == "mxfp8" else e4m3_expert_fwd_bwd)(oracle, X, dO, *Wm)
             t_exp += time.perf_counter() - t0
         else:
-            W1, W3, W2 = (to_f64(inp[n][e]) for n in ("W1", "W3", "W2"))
+            X, dO = X.astype(dtype), dO.astype(dtype)
+            W1, W3, W2 = (to_f64(inp[n][e]).astype(dtype) for n in ("W1", "W3", "W2"))
             t0 = time.perf_counter()
             a, b, h, o = oracle.swiglu_fwd(X, W1, W3, W2)
             oracle.swiglu_bwd(X, a, b, h, dO, W1, W3, W2)
@@ -416,17 +417,44 @@ def cpu_baseline(wl, inp, budget_s: float):
         rows_done += r1 - r0
         if t_exp >= budget_s:
             break
-    return {
-        "value": round(flops / t_exp / 1e12, 6) if t_exp > 0 else None,
+    return (round(flops / t_exp / 1e12, 6) if t_exp > 0 else None), t_route, n_exp, rows_done, t_exp
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The oracle, unchanged, on a bounded sample of the workload (see
+    _oracle_sample): for bf16 / fp32 workloads the same code on fp32 arrays
+    (the reported value) and on fp64 arrays (the correctness oracle as the
+    tests run it); for fp8 workloads the fp64 e4m3 / MXFP8 chain."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    fp8 = wl.dtype in ("e4m3", "mxfp8")
+    runs = [("fp64", np.float64)] if fp8 else [("fp32", np.float32), ("fp64", np.float64)]
+    res = {}
+    for name, dt in runs:
+        res[name] = _oracle_sample(wl, inp, budget_s / len(runs), dt)
+    head = runs[0][0]
+    val, t_route, n_exp, rows, t_exp = res[head]
+    out = {
+        "value": val,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle{f' ({wl.dtype} chain: quantise, dequantise, fp64 products)' if wl.dtype in ('e4m3', 'mxfp8') else ''}: "
+        "sample": (f"{head} NumPy oracle{f' ({wl.dtype} chain: quantise, dequantise, fp64 products)' if fp8 else ''}: "
                    f"route + permutation map of all {wl.T} tokens "
                    f"({t_route:.2f} s), then SwiGLU fwd+bwd of experts 0..{n_exp - 1} "
-                   f"({rows_done} of {wl.P} routed rows) in {t_exp:.1f} s; host has "
+                   f"({rows} of {wl.P} routed rows) in {t_exp:.1f} s; host has "
                    f"{len(os.sched_getaffinity(0))} usable cores"),
     }
+    if "fp64" in res and head != "fp64":
+        v64, _, n64, r64, t64 = res["fp64"]
+        out["fp64"] = {"value": v64, "unit": "TFLOP/s",
+                       "sample": f"the same code on fp64 arrays: experts 0..{n64 - 1} ({r64} rows) in {t64:.1f} s"}
+    return out
 
 
 def main():
@@ -447,6 +475,8 @@ def main():
                     help="with --memory-efficient: recompute p*h in the backward instead of keeping it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run two 1 GiB device copies first (for hardware-counter runs)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time the steps back to back, without the 512 MiB write between them")
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py: this library is one GPU's share of the layer; --gpus {args.gpus} is not "
@@ -476,7 +506,13 @@ def main():
 
     ev = [marks() for _ in range(args.steps)]
     warm = marks()
-    for _ in range(args.warmup):
+    # a write larger than the 256 MB last-level cache between timed steps, so
+    # that no step reads what the previous one left in L2 / MALL; it runs
+    # outside each step's events
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        if flush is not None:
+            flush.fill_(i & 0x7f)
         step(warm)
     torch.cuda.synchronize()
     log(f"bench: warmup done ({args.warmup} steps)")
@@ -484,20 +520,28 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0x7f)
         step(ev[i])
     stop.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    log(f"bench: timed {args.steps} steps, {ms_step:.3f} ms/step")
+    per_step = sorted(e[MARKS[0]].elapsed_time(e[MARKS[-1]]) for e in ev)
+    ms_step = statistics.median(per_step)
+    ms_wall = start.elapsed_time(stop) / args.steps          # incl. the flushes
+    log(f"bench: timed {args.steps} steps, median {ms_step:.3f} ms/step, min {per_step[0]:.3f}, "
+        f"{ms_wall:.3f} ms per step incl. the flush")
 
     def seg(i):
-        return sum(e[MARKS[i]].elapsed_time(e[MARKS[i + 1]]) for e in ev) / args.steps
+        return statistics.median(e[MARKS[i]].elapsed_time(e[MARKS[i + 1]]) for e in ev)
 
     (t_route, t_perm, t_aux, t_gf, t_comb, t_permb, t_rbwd, t_gb, t_unp,
      t_wq) = (seg(i) for i in range(len(MARKS) - 1))
     s = 4 if wl.dtype == "f32" else 2
     flops = wl.flops_fwd_bwd()
-    gemm_ms = t_gf + t_gb
+    # the grouped-GEMM launches of one step (forward and backward segments),
+    # median over the timed steps
+    gemm_ms = statistics.median(e["aux_loss"].elapsed_time(e["gemm_fwd"]) +
+                                e["route_bwd"].elapsed_time(e["gemm_bwd"]) for e in ev)
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     move_bytes = (wl.T * wl.d + wl.P * wl.d) * s          # bf16 / fp32 rows in and out
@@ -538,7 +582,14 @@ def main():
                          "quantize_weights": round(t_wq, 4)},
         "hbm": {"permute_GBps": round(perm_gbs, 1), "combine_GBps": round(comb_gbs, 1),
                 "permute_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
-                "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS},
+                "combine_frac": round(comb_gbs / HBM_PEAK_GBS, 4), "peak_GBps": HBM_PEAK_GBS,
+                "permute_us_per_call": round(t_perm * 1e3, 1),
+                "combine_us_per_call": round(t_comb * 1e3, 1)},
+        "timing": {"per_step": "HIP events around each step; median over the timed steps",
+                   "median_ms": round(ms_step, 4), "min_ms": round(per_step[0], 4),
+                   "mean_ms": round(statistics.fmean(per_step), 4),
+                   "wall_ms_per_step_incl_flush": round(ms_wall, 4),
+                   "flush_between_steps_bytes": 0 if args.no_flush else FLUSH_BYTES},
     }
     if args.memory_efficient:
         out["config"]["memory_efficient"] = "recompute_h" if me == 2 else True
