@@ -132,6 +132,26 @@ int moe_permute(const moe_shape* sh, const void* src, const int32_t* topk_idx,
                 void* stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  With build_map = 1
+ * the map's per-(expert, 256-token block) counts, E * ceil(T / 256) int32
+ * (aligned up to 256 bytes), go to a 1 MiB array that the library keeps in
+ * device memory, one per GPU, for the life of the process (e.g. E = 256
+ * experts allow T <= 262144 tokens); larger maps return MOE_ERR_WORKSPACE
+ * before anything is enqueued.  All calls on one GPU share that array: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Nothing in it needs to start at zero.  The first
+ * call on a device looks up the array's device address (MOE_ERR_HIP if the
+ * runtime cannot); no call allocates or frees memory.  Arguments, results
+ * and errors otherwise as moe_permute.
+ */
+int moe_permute_noalloc(const moe_shape* sh, const void* src, const int32_t* topk_idx,
+                        const float* row_scale, int build_map, int32_t* counts,
+                        int32_t* offsets, int32_t* row_of, int32_t* token_of, void* dst,
+                        void* stream);
+
+/*
  * moe_unpermute -- combine on one GPU (Spanish summary, section 2.1):
  *   dst[t] = round( sum_{j=0..k-1} w[t][j] * src[row_of[t][j]] + add[t] )
  * with the sum in fp32 in j order, w = topk_prob (fp32 [T][k]) or 1 when

@@ -132,6 +132,23 @@ def test_gemm_32bit_ranges():
                                     None) == N.MOE_ERR_INVALID
 
 
+def test_permute_noalloc_validation():
+    """The allocation-free map refuses maps larger than its 1 MiB array before
+    any HIP call, and validates its arguments as moe_permute does."""
+    lib = N.lib()
+    sh = make_shape(1025 * 256, 64, 256, 2, 128, 0, "bf16")        # 256 * 1025 * 4 B > 1 MiB
+    assert lib.moe_permute_noalloc(C.byref(sh), P, P, None, 1, P, P, P, P, P, None) == \
+        N.MOE_ERR_WORKSPACE
+    sh = make_shape(64, 256, 8, 2, 128, 0, "bf16")
+    assert lib.moe_permute_noalloc(C.byref(sh), None, P, None, 1, P, P, P, P, P, None) == \
+        N.MOE_ERR_INVALID
+    assert lib.moe_permute_noalloc(C.byref(sh), P, None, None, 1, P, P, P, P, P, None) == \
+        N.MOE_ERR_INVALID
+    sh = make_shape(4, 100, 8, 2, 128, 0, "bf16")                  # 16-byte rows
+    assert lib.moe_permute_noalloc(C.byref(sh), P, P, None, 1, P, P, P, P, P, None) == \
+        N.MOE_ERR_UNSUPPORTED
+
+
 def test_layer_validation():
     lib = N.lib()
     sh = make_shape(64, 256, 8, 2, 256, 0, "bf16")

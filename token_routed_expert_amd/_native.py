@@ -61,6 +61,7 @@ _SH = C.POINTER(moe_shape)
 _PROTOS = {
     "moe_route": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "moe_permute": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_permute_noalloc": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P]),
     "moe_unpermute": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_fwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_grouped_gemm_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,

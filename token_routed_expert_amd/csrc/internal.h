@@ -14,6 +14,10 @@ int route_launch(const float* logits, int T, int E, int k, int32_t* idx, float* 
 
 // permute.hip
 size_t permute_ws_bytes(int64_t T, int64_t E);
+// the file-scope scratch of the allocation-free map: its size, and its device
+// address on the current device (looked up once per device)
+size_t permute_scratch_bytes();
+int permute_scratch(void** ptr);
 int permute_map_launch(const int32_t* idx, int T, int E, int k, int32_t* counts,
                        int32_t* offsets, int32_t* row_of, int32_t* token_of, void* ws,
                        hipStream_t s);

@@ -364,6 +364,26 @@ int moe_permute(const moe_shape* sh, const void* src, const int32_t* topk_idx,
                              elem_bytes(sh), dst, s);
 }
 
+int moe_permute_noalloc(const moe_shape* sh, const void* src, const int32_t* topk_idx,
+                        const float* row_scale, int build_map, int32_t* counts, int32_t* offsets,
+                        int32_t* row_of, int32_t* token_of, void* dst, void* stream) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (!src || !dst || !row_of) return MOE_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  if (build_map) {
+    if (!topk_idx || !counts || !offsets || !token_of) return MOE_ERR_INVALID;
+    if (permute_ws_bytes(sh->T, sh->E) > permute_scratch_bytes()) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = permute_scratch(&ws))) return st;
+    st = permute_map_launch(topk_idx, (int)sh->T, (int)sh->E, (int)sh->k, counts, offsets, row_of,
+                            token_of, ws, s);
+    if (st) return st;
+  }
+  return permute_rows_launch(src, row_of, row_scale, (int)sh->T, (int)sh->k, (int)sh->d,
+                             elem_bytes(sh), dst, s);
+}
+
 int moe_unpermute(const moe_shape* sh, const void* src, const int32_t* row_of,
                   const float* topk_prob, const void* add, void* dst, void* stream) {
   int st = check_shape(sh);

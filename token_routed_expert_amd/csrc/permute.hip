@@ -22,6 +22,15 @@
 #include "common.h"
 #include "internal.h"
 
+#include <atomic>
+
+// Scratch of the allocation-free permutation map (moe_permute_noalloc): the
+// per-(expert, token block) counts live here instead of in a caller
+// workspace.  Every GPU holds its own copy until the process ends; calls on
+// one GPU share it, so calls that overlap on one GPU race.  The map kernels
+// overwrite every count they read, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[1 << 20];
+
 namespace tre {
 
 namespace {
@@ -288,6 +297,25 @@ int gather_typed(const void* src, const int32_t* row_of, const float* prob, cons
 }
 
 }  // namespace
+
+size_t permute_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress once
+// per device (with that device current), kept per device; host code passes
+// this address to the kernels, never the array's host-side name.
+int permute_scratch(void** ptr) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    addr[dev].store(p, std::memory_order_release);  // concurrent first calls store the same value
+  }
+  *ptr = p;
+  return MOE_OK;
+}
 
 size_t permute_ws_bytes(int64_t T, int64_t E) {
   const int64_t NB = (T + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK;

@@ -76,6 +76,15 @@ def moe_permute(sh, src, topk_idx, row_scale, build_map, counts, offsets, row_of
            "moe_permute")
 
 
+def moe_permute_noalloc(sh, src, topk_idx, row_scale, build_map, counts, offsets, row_of,
+                        token_of, dst, stream=None):
+    _check(N.lib().moe_permute_noalloc(C.byref(sh), _ptr(src), _ptr(topk_idx, I32),
+                                       _ptr(row_scale, F32), int(build_map), _ptr(counts, I32),
+                                       _ptr(offsets, I32), _ptr(row_of, I32), _ptr(token_of, I32),
+                                       _ptr(dst), _stream(stream)),
+           "moe_permute_noalloc")
+
+
 def moe_unpermute(sh, src, row_of, topk_prob, add, dst, stream=None):
     _check(N.lib().moe_unpermute(C.byref(sh), _ptr(src), _ptr(row_of, I32), _ptr(topk_prob, F32),
                                  _ptr(add), _ptr(dst), _stream(stream)), "moe_unpermute")
