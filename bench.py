@@ -138,14 +138,15 @@ def router_grad_calls(wl, sh, b, ws_aux):
     return aux, comb_bwd, route_bwd
 
 
-def build_step(wl, inp, router_grad=False, memory_efficient=False):
+def build_step(wl, inp, router_grad=False, memory_efficient=False, fused=False):
     import torch
     import token_routed_expert_amd as tre
     from token_routed_expert_amd import _native as N
     from token_routed_expert_amd.buffers import layer_buffers
 
     sh, b, wsf, wsb = layer_buffers(wl.T, wl.d, wl.E, wl.k, wl.f, wl.f_shared, wl.dtype, "cuda", inp,
-                                    router_grad=router_grad, memory_efficient=memory_efficient)
+                                    router_grad=router_grad, memory_efficient=memory_efficient,
+                                    fused_permute=fused)
     rg = None
     if router_grad:
         base = tre.moe_workspace_bytes(sh, N.MOE_WS_LAYER_FWD)
@@ -163,19 +164,38 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
 
     if memory_efficient:
         return build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg, memory_efficient)
+    # the fused permutation builds the map alone; fc1 reads x through token_of
+    xp = None if fused else b["xp"]
+
+    def gemm_fwd():
+        if fused:
+            tre.moe_grouped_gemm_fwd_gather(sh, b["offsets"], b["token_of"], b["x"], b["W1"],
+                                            b["W3"], b["W2"], b["ab"], b["h"], b["o"])
+        else:
+            tre.moe_grouped_gemm_fwd(sh, b["offsets"], xp, b["W1"], b["W3"], b["W2"], b["ab"],
+                                     b["h"], b["o"])
+
+    def gemm_bwd():
+        if fused:
+            tre.moe_grouped_gemm_bwd_gather(sh, b["offsets"], b["token_of"], b["x"], b["ab"],
+                                            b["h"], b["dO"], b["W1"], b["W3"], b["W2"], b["dab"],
+                                            b["dXp"], b["dW1"], b["dW3"], b["dW2"])
+        else:
+            tre.moe_grouped_gemm_bwd(sh, b["offsets"], xp, b["ab"], b["h"], b["dO"], b["W1"],
+                                     b["W3"], b["W2"], b["dab"], b["dXp"], b["dW1"], b["dW3"],
+                                     b["dW2"])
 
     def step(ev):
         ev["start"].record()
         tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
         ev["route"].record()
-        tre.moe_permute(sh, b["x"], b["topk_idx"], None, 1, b["counts"], b["offsets"], b["row_of"],
-                        b["token_of"], b["xp"], wsf)
+        tre.moe_permute(sh, None if fused else b["x"], b["topk_idx"], None, 1, b["counts"],
+                        b["offsets"], b["row_of"], b["token_of"], xp, wsf)
         ev["permute"].record()
         if rg:
             rg[0]()
         ev["aux_loss"].record()
-        tre.moe_grouped_gemm_fwd(sh, b["offsets"], b["xp"], b["W1"], b["W3"], b["W2"], b["ab"],
-                                 b["h"], b["o"])
+        gemm_fwd()
         if shared:
             tre.moe_grouped_gemm_fwd(shared[0], shared[1], b["x"], b["Ws1"], b["Ws3"], b["Ws2"],
                                      b["s_ab"], b["s_h"], b["ys"])
@@ -191,8 +211,7 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False):
         if rg:
             rg[2]()
         ev["route_bwd"].record()
-        tre.moe_grouped_gemm_bwd(sh, b["offsets"], b["xp"], b["ab"], b["h"], b["dO"], b["W1"],
-                                 b["W3"], b["W2"], b["dab"], b["dXp"], b["dW1"], b["dW3"], b["dW2"])
+        gemm_bwd()
         if shared:
             tre.moe_grouped_gemm_bwd(shared[0], shared[1], b["x"], b["s_ab"], b["s_h"], b["dY"],
                                      b["Ws1"], b["Ws3"], b["Ws2"], b["s_dab"], b["dXs"], b["dWs1"],
@@ -475,6 +494,8 @@ def main():
                     help="with --memory-efficient: recompute p*h in the backward instead of keeping it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run two 1 GiB device copies first (for hardware-counter runs)")
+    ap.add_argument("--fused-permute", action="store_true",
+                    help="bf16 / fp32: the permutation fused into fc1's operand loads (no xp)")
     ap.add_argument("--no-flush", action="store_true",
                     help="time the steps back to back, without the 512 MiB write between them")
     args = ap.parse_args()
@@ -499,7 +520,10 @@ def main():
         log("bench.py: --memory-efficient needs a bf16, e4m3 or mxfp8 workload")
         sys.exit(2)
     me = (2 if args.recompute_h else 1) if args.memory_efficient else 0
-    step = build_step(wl, inp, args.router_grad, me)
+    if args.fused_permute and (wl.dtype not in ("bf16", "f32") or args.memory_efficient):
+        log("bench.py: --fused-permute needs a bf16 or fp32 workload without --memory-efficient")
+        sys.exit(2)
+    step = build_step(wl, inp, args.router_grad, me, args.fused_permute)
 
     def marks():
         return {m: torch.cuda.Event(enable_timing=True) for m in MARKS}
@@ -591,6 +615,11 @@ def main():
                    "wall_ms_per_step_incl_flush": round(ms_wall, 4),
                    "flush_between_steps_bytes": 0 if args.no_flush else FLUSH_BYTES},
     }
+    if args.fused_permute:
+        # the permute segment builds the map alone (no rows move): no GB/s figure
+        out["config"]["fused_permute"] = True
+        out["hbm"].update(permute_GBps=None, permute_frac=None,
+                          permute_note="map only: fc1 reads x rows through token_of")
     if args.memory_efficient:
         out["config"]["memory_efficient"] = "recompute_h" if me == 2 else True
         if wl.dtype in ("e4m3", "mxfp8"):

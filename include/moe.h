@@ -120,6 +120,8 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
  *     moe_workspace_bytes(sh, MOE_WS_PERMUTE).
  *   build_map = 0: uses the caller's row_of; counts, offsets, token_of, ws
  *     may be NULL.
+ *   dst NULL (build_map = 1 only): the map alone, no rows moved (src may be
+ *     NULL); the experts then read x through token_of (the *_gather calls).
  *   src [T][d] and dst [P][d] are in sh->dtype.  Assignments whose row_of
  *   entry lies outside [0, P) are skipped (here and in every call that reads
  *   row_of).  row_scale NULL: dst rows are bit copies of src rows.  row_scale fp32 [T][k] non-NULL: dst[row_of[t][j]]
@@ -195,6 +197,27 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
                          void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_gemm_fwd_gather / moe_grouped_gemm_bwd_gather -- the same
+ * products with the permutation fused into the expert GEMMs' operand loads
+ * (the pages' dispatchers eliminate permutation steps: German technical
+ * summary, section 2 C, and the hyper.ai article on Hybrid-EP): row r of the
+ * permuted input is row token_of[r] of x [T][d] (token_of from moe_permute's
+ * map), read by fc1 forward and by the fc1 weight gradient, so no permuted
+ * copy xp is written or read.  Results equal moe_grouped_gemm_fwd / _bwd on
+ * xp = x[token_of] bit for bit.  bf16 and fp32; MOE_ERR_UNSUPPORTED when
+ * T * d * element bytes >= 2^31 - 4096.
+ */
+int moe_grouped_gemm_fwd_gather(const moe_shape* sh, const int32_t* offsets,
+                                const int32_t* token_of, const void* x, const void* W1,
+                                const void* W3, const void* W2, void* ab, void* h, void* o,
+                                void* ws, size_t ws_bytes, void* stream);
+int moe_grouped_gemm_bwd_gather(const moe_shape* sh, const int32_t* offsets,
+                                const int32_t* token_of, const void* x, const void* ab,
+                                const void* h, const void* dO, const void* W1, const void* W3,
+                                const void* W2, void* dab, void* dXp, void* dW1, void* dW3,
+                                void* dW2, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Buffers of a whole layer.  Inputs are read-only; "saved" buffers are
  * written by moe_layer_fwd and read by moe_layer_bwd; the rest are outputs.
  * Shared-expert pointers are ignored when f_shared == 0.
@@ -249,6 +272,12 @@ typedef struct {
      may be NULL); xq, xpq hold codes as for e4m3 and xs, xps hold E8M0 scale
      bytes, [T][d/32] and [P][d/32] (the same byte count as the e4m3 scales) */
   const struct moe_mx_weights* wmx;
+  /* fused permutation (bf16 and fp32 layers): when fused_permute != 0 the
+     forward builds the map alone and the experts' fc1 forward and fc1 weight
+     gradient read row token_of[r] of x directly (moe_grouped_gemm_fwd_gather
+     / moe_grouped_gemm_bwd_gather), so xp is neither written nor read and
+     may be NULL; needs T * d * element bytes below 2^31 - 4096 */
+  int32_t fused_permute;
 } moe_layer_io;
 
 /*

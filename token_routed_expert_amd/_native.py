@@ -40,7 +40,8 @@ _IO_FIELDS_ROUTER = ["aux_loss", "dprob", "dlogits"]
 class moe_layer_io(C.Structure):
     _fields_ = ([(n, C.c_void_p) for n in _IO_FIELDS + _IO_FIELDS_E4M3 + _IO_FIELDS_ROUTER]
                 + [("aux_alpha", C.c_float), ("row_prob", C.c_void_p),
-                   ("memory_efficient", C.c_int32), ("wmx", C.c_void_p)])
+                   ("memory_efficient", C.c_int32), ("wmx", C.c_void_p),
+                   ("fused_permute", C.c_int32)])
 
 
 IO_FIELDS = tuple(_IO_FIELDS + _IO_FIELDS_E4M3[1:] + _IO_FIELDS_ROUTER + ["row_prob"])
@@ -66,6 +67,9 @@ _PROTOS = {
     "moe_grouped_gemm_fwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_grouped_gemm_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, C.c_size_t, _P]),
+    "moe_grouped_gemm_fwd_gather": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              C.c_size_t, _P]),
+    "moe_grouped_gemm_bwd_gather": (C.c_int, [_SH] + [_P] * 15 + [C.c_size_t, _P]),
     "moe_layer_fwd": (C.c_int, [_SH, C.POINTER(moe_layer_io), _P, C.c_size_t, _P]),
     "moe_layer_bwd": (C.c_int, [_SH, C.POINTER(moe_layer_io), _P, C.c_size_t, _P]),
     "moe_quantize_rows": (C.c_int, [_P, C.c_int32, _I64, _I64, _P, _P, _P]),

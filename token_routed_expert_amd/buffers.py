@@ -9,7 +9,8 @@ from .ops import (E4M3Weights, MXWeights, make_shape, moe_quantize_weights,
 
 
 def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs=None,
-                  router_grad=False, aux_alpha=0.01, memory_efficient=False):
+                  router_grad=False, aux_alpha=0.01, memory_efficient=False,
+                  fused_permute=False):
     """Every buffer moe_layer_fwd/bwd touch, as a dict keyed like moe_layer_io.
 
     `inputs` (logits, x, W1, W3, W2, Ws1, Ws3, Ws2, dY) are used as given.
@@ -17,6 +18,7 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     router gradient (aux_loss, dprob, dlogits).
     memory_efficient: probabilities applied before W2 (row_prob [P]);
     2 also recomputes h in the backward.
+    fused_permute: the experts read x through token_of; no xp buffer.
     Returns (shape, buffers, ws_fwd, ws_bwd).
     """
     sh = make_shape(T, d, E, k, f, f_shared, dtype)
@@ -47,6 +49,9 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
                  xpq=z(P, d, dtype=u8), xps=z(P, d // 32, dtype=u8))
         if "W1" in b and b["W1"].dtype == torch.float32:
             b["wmx"] = quantized_weights_mx(b["W1"], b["W3"], b["W2"])
+    if fused_permute:
+        b.pop("xp", None)
+        b["fused_permute"] = 1
     if f_shared:
         b.update(s_ab=z(T, 2 * f_shared), s_h=z(T, f_shared), ys=z(T, d), s_dab=z(T, 2 * f_shared),
                  dXs=z(T, d), dWs1=z(d, f_shared), dWs3=z(d, f_shared), dWs2=z(f_shared, d))

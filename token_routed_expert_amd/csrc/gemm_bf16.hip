@@ -62,6 +62,9 @@ constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int OPND_BYTES = 256 * BK * 2;         // one operand of one stage (16 KB)
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // A then B
 constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 16 one-KB DMA instructions
+// a buffer offset past every operand's range: the load returns zeros (the
+// gathered operand's range, T * d * 2 bytes, stays below 2^31)
+constexpr uint32_t kPastRange = 0x80000000u;
 
 template <int OP>
 struct OpTraits {
@@ -111,7 +114,18 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // of an expert with under 96 rows) those loads read nothing (a zero-length
 // buffer range) and the next tile starts its own prologue after a full wait.
 // (LOOK = 3 below: the ring depth minus one.)
-template <int OP, int NW, bool RS>
+//
+// GATHER (fc1 forward and fc1 weight gradient): the permuted input xp is not
+// read; row r of it is row token_of[r] of x (args.gather, args.gx), fetched by
+// the same DMA (the permutation fused into the operand loader).  fc1 forward
+// takes the rows' offsets once per tile.  In the fc1 weight gradient the rows
+// run along K, so every stage needs new ones: the wavefront's two A DMA
+// instructions cover the same four k-rows (both 128-column halves), and four
+// stages ahead each wavefront DMAs the token ids of those rows into one of
+// four LDS slots of its own (one more load per stage in the wait counts); right
+// after the stage's barrier, when none of its LDS reads is pending, it turns
+// them into the lane offsets of the A loads it issues next.
+template <int OP, int NW, bool RS, bool GATHER = false>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // wavefront sub-tile
@@ -127,11 +141,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   // them 5-10 % slower)
   constexpr int NS = 4;
   constexpr int LOOK = NS - 1;  // stage kt + LOOK is issued during stage kt
+  // gathered weight gradient: token ids of stage kt + TLOOK are loaded in stage kt
+  constexpr bool GW = GATHER && OP == OP_FC1_WGRAD;
+  constexpr int TLOOK = LOOK + 1;
+  constexpr int VM_STAGE = LOADS_PER_STAGE + (GW ? 1 : 0);  // vector-memory loads per stage
 
   // the stage ring, then (ragged M) the schedule scratch, the inclusive prefix
   // of the experts' M-tile counts and (row-scaled fc2 dgrad) the wavefronts'
   // per-row <h, dh'> partials
-  constexpr int EXTRA = TR::ragged_m ? (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4 : 0;
+  // (gathered weight gradient: four 256-byte token slots per wavefront)
+  constexpr int TSLOTS = 4;
+  constexpr int EXTRA = TR::ragged_m ? (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4
+                                     : (GW ? NW * TSLOTS * 256 : 0);
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + EXTRA];
   int* const sched = (int*)(lds + NS * STAGE_BYTES);
   int* const mt_incl = sched + NW;
@@ -180,6 +201,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     rsrc_t a_src, b_src, b_src2;
     uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
     int KT;
+    int row0, rows;  // the tile's permuted rows (gathered operands)
   };
   uint32_t a_ld, b_ld;
   {
@@ -210,6 +232,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     const int unit = ((lane & 15) >> 1) ^ fk;
     return (uint32_t)k * ld + (uint32_t)(col_base + unit * 16 + (lane & 1) * 8) * 2u;
   };
+  // A DMA instruction q of this wavefront: t = wid * 2 + q, except in the
+  // gathered weight gradient, where t = wid + 8 q (half q, k-rows 4 wid..+3)
+  auto a_instr = [&](int q) __attribute__((always_inline)) -> int {
+    if constexpr (GW) return wid + 8 * q;
+    else return wid * DMA_PER_WAVE + q;
+  };
   auto setup = [&](const TileInfo& ti, Opnd& o) __attribute__((always_inline)) {
     const size_t e = (size_t)ti.e;
     {
@@ -218,8 +246,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       else if constexpr (OP == OP_FC2_FWD || OP == OP_FC2_WGRAD) base = (const bf16_t*)args.h;
       else if constexpr (OP == OP_FC2_DGRAD) base = (const bf16_t*)args.dO;
       else base = (const bf16_t*)args.dab;
-      o.a_src = make_rsrc((const char*)base + (size_t)ti.row0 * a_ld, (uint32_t)ti.rows * a_ld);
+      if constexpr (GATHER) o.a_src = make_rsrc(args.gx, (uint32_t)args.gT * a_ld);  // all of x
+      else o.a_src = make_rsrc((const char*)base + (size_t)ti.row0 * a_ld, (uint32_t)ti.rows * a_ld);
     }
+    o.row0 = ti.row0;
+    o.rows = ti.rows;
     if constexpr (OP == OP_FC1_FWD || OP == OP_FC1_DGRAD) {
       o.b_src = make_rsrc((const bf16_t*)args.W1 + e * (size_t)d * f, (uint32_t)d * (uint32_t)f * 2u);
       o.b_src2 = make_rsrc((const bf16_t*)args.W3 + e * (size_t)d * f, (uint32_t)d * (uint32_t)f * 2u);
@@ -238,7 +269,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) {
       const int t = wid * DMA_PER_WAVE + q;
-      if constexpr (TR::a_kcontig) o.a_off[q] = kc_off(t, 0, a_ld);
+      if constexpr (GATHER && OP == OP_FC1_FWD) {
+        // row `row` of the tile is x row token_of[row0 + row]; rows past the
+        // expert's end read as zero (an offset past the buffer's range)
+        const int row = 16 * t + (lane >> 2);
+        const int c = (lane & 3) ^ kc_swz(row);
+        o.a_off[q] = row < ti.rows
+                         ? (uint32_t)args.gather[ti.row0 + row] * a_ld + (uint32_t)c * 16u
+                         : kPastRange;
+      } else if constexpr (GW) {
+        // the column part only: the k-row's token comes per stage
+        const int ta = a_instr(q);
+        o.a_off[q] = mc_off(ta, min(ti.m0 + (ta >> 3) * 128, Mfix - 128), 0u);
+      } else if constexpr (TR::a_kcontig) o.a_off[q] = kc_off(t, 0, a_ld);
       else o.a_off[q] = mc_off(t, min(ti.m0 + (t >> 3) * 128, Mfix - 128), a_ld);
       if constexpr (TR::b_kcontig) {
         o.b_off[q] = kc_off(t, ti.n0, b_ld);
@@ -264,6 +307,41 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   nxt = cur;   // uses them with a zero-length range)
   int phase = 0;        // ring slot of the current tile's stage 0
   bool cross = false;   // stages past the current tile's last fetch the next tile's first three
+  // gathered weight gradient: token slot of the current tile's stage 0, the
+  // token-id source, the slots' LDS address, and the lane offsets of the A
+  // loads of the stage issued next
+  int tphase = 0;
+  const rsrc_t tok_src = GW ? make_rsrc(args.gather, (uint32_t)args.P * 4u) : rsrc_t{0, 0, 0, 0};
+  const uint32_t tok_base = lds_base + (uint32_t)(NS * STAGE_BYTES);
+  uint32_t gofs[DMA_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < DMA_PER_WAVE; ++q) gofs[q] = kPastRange;
+  // token ids of the four k-rows of this wavefront in stage s (lanes 0..3
+  // load them; the other lanes' loads land unused) into the stage's slot
+  auto issue_tok = [&](int s) __attribute__((always_inline)) {
+    const bool in_cur = s < cur.KT;
+    const int ks = (in_cur ? s : s - cur.KT) * BK + 4 * wid;
+    const int base = (in_cur ? cur.row0 : nxt.row0) + ks;
+    const uint32_t idx = (uint32_t)min(max(base + lane, 0), args.P - 1);
+    rsrc_t r = tok_src;
+    r[2] = (in_cur || cross) ? r[2] : 0;
+    dma4(uniform_rsrc(r), idx * 4u,
+         tok_base + (uint32_t)((wid * TSLOTS + ((tphase + s) & (TSLOTS - 1))) * 256));
+  };
+  // A offsets of stage s from its token ids (landed for this wavefront): x row
+  // token * d for the lane's k-row, past the range for k-rows past the tile's
+  auto gather_offsets = [&](int s) __attribute__((always_inline)) {
+    const bool in_cur = s < cur.KT;
+    const int ks = (in_cur ? s : s - cur.KT) * BK + 4 * wid;
+    const int lim = (in_cur ? cur.rows : nxt.rows) - ks;  // valid k-rows of the four
+    const int tok = *(const __attribute__((address_space(3))) int*)(
+        lds + NS * STAGE_BYTES + (wid * TSLOTS + ((tphase + s) & (TSLOTS - 1))) * 256 +
+        (lane >> 4) * 4);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      gofs[q] = (lane >> 4) < lim ? (uint32_t)tok * a_ld + (in_cur ? cur.a_off[q] : nxt.a_off[q])
+                                  : kPastRange;
+  };
   // DMA instruction q of this wavefront (q < DMA_PER_WAVE: A operand, else B)
   // for stage s of the stream, counted from the current tile's stage 0
   // TAIL = false: the caller knows that s is a stage of the current tile.
@@ -274,13 +352,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     const int k0 = (in_cur ? s : s - cur.KT) * BK;
     const bool live = in_cur || cross;
     if constexpr (q < DMA_PER_WAVE) {
-      const int t = wid * DMA_PER_WAVE + q;
+      const int t = a_instr(q);
       rsrc_t r = pick(in_cur, cur.a_src, nxt.a_src);
       r[2] = live ? r[2] : 0;
       r = uniform_rsrc(r);
-      const uint32_t off = in_cur ? cur.a_off[q] : nxt.a_off[q];
-      const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
-      dma16(r, off + ka, st_base + (uint32_t)(t * 1024));
+      if constexpr (GW) {
+        dma16(r, gofs[q], st_base + (uint32_t)(t * 1024));  // offsets of stage s (gather_offsets)
+      } else {
+        const uint32_t off = in_cur ? cur.a_off[q] : nxt.a_off[q];
+        const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
+        dma16(r, off + ka, st_base + (uint32_t)(t * 1024));
+      }
     } else {
       const int qq = q - DMA_PER_WAVE;
       const int t = wid * DMA_PER_WAVE + qq;
@@ -377,6 +459,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst,
                         auto TAIL, auto SKIP) __attribute__((always_inline)) {
     constexpr bool skip = decltype(SKIP)::value;
+    // gathered weight gradient: the token ids of stage kt + 4, ahead of this
+    // stage's B loads (the wait below counts it)
+    if constexpr (GW) issue_tok(kt + TLOOK);
     // B fragments HB..FN-1 for the second half: issued first, needed last
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, HB + U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
@@ -398,8 +483,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     // stage kt+1 has landed for this wavefront; after the barrier it has for
     // all, and every wavefront is done with stage kt-1, whose buffer now
     // takes stage kt+3
-    wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2)>();
+    wait_vmcnt<VM_STAGE * (LOOK - 2)>();
     block_barrier();
+    // the token ids of stage kt + 3 have landed (issued before stage kt + 1's
+    // B loads); no LDS read of this wavefront is pending here
+    if constexpr (GW) gather_offsets(kt + LOOK);
     // next stage's B fragments 0..HB-1 first: the next first half starts with them
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
@@ -434,14 +522,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     // fc2 dgrad's epilogue reads a|b from memory and would wait for the next
     // tile's loads in flight: it starts every tile with its own prologue
     cross = OP != OP_FC2_DGRAD && have_next && cur.KT >= 1 && nxt.KT >= LOOK;
+    // gathered weight gradient: the next tile's first TLOOK token loads are
+    // issued in this tile's last TLOOK stages
+    if constexpr (GW) cross = cross && cur.KT >= TLOOK;
     if (fresh) {
+      // gathered weight gradient: token ids of stages 0 .. TLOOK-1 first;
+      // those of stages 0 .. LOOK-1 land before their A loads are issued
+      if constexpr (GW) {
+        static_for<0, TLOOK>([&](auto S) __attribute__((always_inline)) { issue_tok(S.value); });
+        wait_vmcnt<TLOOK - LOOK>();
+      }
       // stages 0 .. LOOK-2 and stage LOOK-1's A half in flight (its B half
       // follows in stage 0); wait for stage 0 and make it visible
       static_for<0, LOOK - 1>([&](auto S) __attribute__((always_inline)) {
+        if constexpr (GW) gather_offsets(S.value);
         static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) {
           issue_one(S.value, Q, IntC<1>{});
         });
       });
+      if constexpr (GW) gather_offsets(LOOK - 1);
       static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(LOOK - 1, Q, IntC<1>{}); });
       wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE>();
       block_barrier();
@@ -482,6 +581,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     if (!have_next) break;
     if (cross) {
       phase = (int)((uint32_t)(phase + cur.KT) % NS);
+      tphase = (tphase + cur.KT) & (TSLOTS - 1);
       fresh = false;
     } else {
       // the past-the-end loads read nothing but still write the ring: drain
@@ -547,14 +647,23 @@ int launch(const GemmArgs& a, hipStream_t s) {
     if (ncu <= 0) return MOE_ERR_HIP;
     if (grid > ncu) grid = ncu;
   }
-  bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
-  if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
-    if (a.row_prob) {
-      gemm_bf16_kernel<OP, NW, true><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
-      scaled = true;
-    }
+  // row-scaled variants (only fc1 forward and fc2 dgrad change) and the
+  // gathered fc1 operand (fc1 forward and fc1 weight gradient)
+  const unsigned g = (unsigned)grid;
+  if constexpr (OP == OP_FC1_FWD) {
+    if (a.gather && a.row_prob) gemm_bf16_kernel<OP, NW, true, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
+    else if (a.gather) gemm_bf16_kernel<OP, NW, false, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
+    else if (a.row_prob) gemm_bf16_kernel<OP, NW, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
+    else gemm_bf16_kernel<OP, NW, false><<<g, NW * 64, 0, s>>>(a, NT, MT);
+  } else if constexpr (OP == OP_FC2_DGRAD) {
+    if (a.row_prob) gemm_bf16_kernel<OP, NW, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
+    else gemm_bf16_kernel<OP, NW, false><<<g, NW * 64, 0, s>>>(a, NT, MT);
+  } else if constexpr (OP == OP_FC1_WGRAD) {
+    if (a.gather) gemm_bf16_kernel<OP, NW, false, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
+    else gemm_bf16_kernel<OP, NW, false><<<g, NW * 64, 0, s>>>(a, NT, MT);
+  } else {
+    gemm_bf16_kernel<OP, NW, false><<<g, NW * 64, 0, s>>>(a, NT, MT);
   }
-  if (!scaled) gemm_bf16_kernel<OP, NW, false><<<(unsigned)grid, NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -71,6 +71,15 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t m0) {
                : "memory");
 }
 
+// 4 bytes per lane from `r` at byte offset `voff` into LDS at byte address
+// m0 + 4 * lane (buffer_load_dword ... lds), ordered like dma16.
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0)
+               : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding load); the empty asm statements keep the
 // compiler from moving memory accesses across it.

@@ -63,7 +63,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args, int NT, in
     if constexpr (ragged) {
       if (m >= M) return 0.f;
       const size_t r = (size_t)(ti.row0 + m);
-      if constexpr (OP == OP_FC1_FWD) return xp[r * d + k];
+      if constexpr (OP == OP_FC1_FWD) {
+        if (args.gather) return ((const float*)args.gx)[(size_t)args.gather[r] * d + k];
+        return xp[r * d + k];
+      }
       if constexpr (OP == OP_FC2_FWD) return h[r * f + k];
       if constexpr (OP == OP_FC2_DGRAD) return dO[r * d + k];
       return dab[r * 2 * f + k];
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args, int NT, in
       if (mm >= M) return 0.f;
       const size_t r = (size_t)(ti.row0 + k);
       if constexpr (OP == OP_FC2_WGRAD) return h[r * f + mm];
+      if (args.gather) return ((const float*)args.gx)[(size_t)args.gather[r] * d + mm];
       return xp[r * d + mm];
     }
   };

@@ -100,6 +100,12 @@ struct GemmArgs {
   const uint8_t* a_sx;
   const uint8_t* b_sx;
   const uint8_t* b_sx2;
+  // fused permutation (bf16 and fp32 fc1 forward and fc1 weight gradient):
+  // when `gather` (token_of [P]) is set, row r of the permuted input is row
+  // gather[r] of gx [gT][d], and xp is not read
+  const int32_t* gather;
+  const void* gx;
+  int gT;
 };
 
 // gemm_bf16.hip: MFMA kernels, bf16 in/out, fp32 accumulation

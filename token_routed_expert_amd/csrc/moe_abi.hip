@@ -177,6 +177,30 @@ GemmArgs expert_args(const moe_shape* sh, const int32_t* offsets) {
   return a;
 }
 
+// Where the experts' input rows come from: the permuted copy xp, or (fused
+// permutation) row token_of[r] of x, read by fc1 forward and fc1 wgrad.
+struct RowSrc {
+  const void* xp;
+  const int32_t* token_of;
+  const void* x;
+};
+void set_rows(GemmArgs& a, const moe_shape* sh, const RowSrc& r) {
+  a.xp = r.xp;
+  a.gather = r.token_of;
+  a.gx = r.x;
+  a.gT = (int)sh->T;
+}
+RowSrc rows_of(const moe_layer_io* io) {
+  return io->fused_permute ? RowSrc{nullptr, io->token_of, io->x} : RowSrc{io->xp, nullptr, nullptr};
+}
+// Gathered rows: bf16 or fp32, and x's byte range below 2^31 (the bf16
+// kernels give rows past an expert's end an offset past that range).
+int check_gather(const moe_shape* sh) {
+  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (sh->T * sh->d * elem_bytes(sh) >= ((int64_t)1 << 31) - 4096) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // The shared expert is a one-group grouped GEMM over all T token rows.
 GemmArgs shared_args(const moe_shape* sh, const int32_t* offsets2) {
   GemmArgs a = {};
@@ -219,6 +243,14 @@ size_t dp_part_bytes(const moe_shape* sh) {
   return align_up((size_t)(sh->T * sh->k) * (size_t)((sh->f + 255) / 256) * sizeof(float), 256);
 }
 int layer_combine_bwd(const moe_shape* sh, const moe_layer_io* io, void* stream);
+int fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const RowSrc& rows, const void* W1,
+                  const void* W3, const void* W2, const float* row_prob, void* ab, void* h, void* o,
+                  void* stream);
+int bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const RowSrc& rows, const void* ab,
+                  void* h, int32_t recompute_h, const void* dO, const void* W1, const void* W3,
+                  const void* W2, const float* row_prob, void* dab, void* dXp, void* dW1,
+                  void* dW3, void* dW2, const int32_t* row_of, float* dprob, void* ws,
+                  void* stream);
 
 // Expert forward of the fp8 products (e4m3 or MXFP8); arguments checked by the caller.
 // row_prob != NULL: the memory-efficient form, h = p silu(a) b.
@@ -351,7 +383,9 @@ int moe_permute(const moe_shape* sh, const void* src, const int32_t* topk_idx,
                 void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (!src || !dst || !row_of) return MOE_ERR_INVALID;
+  // dst NULL with build_map: the map alone (the fused permutation's experts
+  // read x through token_of)
+  if (!row_of || (!dst && !build_map) || (dst && !src)) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
   if (build_map) {
     if (!topk_idx || !counts || !offsets || !token_of) return MOE_ERR_INVALID;
@@ -360,6 +394,7 @@ int moe_permute(const moe_shape* sh, const void* src, const int32_t* topk_idx,
                             token_of, ws, s);
     if (st) return st;
   }
+  if (!dst) return MOE_OK;
   return permute_rows_launch(src, row_of, row_scale, (int)sh->T, (int)sh->k, (int)sh->d,
                              elem_bytes(sh), dst, s);
 }
@@ -369,7 +404,7 @@ int moe_permute_noalloc(const moe_shape* sh, const void* src, const int32_t* top
                         int32_t* row_of, int32_t* token_of, void* dst, void* stream) {
   int st = check_shape(sh);
   if (st) return st;
-  if (!src || !dst || !row_of) return MOE_ERR_INVALID;
+  if (!row_of || (!dst && !build_map) || (dst && !src)) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
   if (build_map) {
     if (!topk_idx || !counts || !offsets || !token_of) return MOE_ERR_INVALID;
@@ -380,6 +415,7 @@ int moe_permute_noalloc(const moe_shape* sh, const void* src, const int32_t* top
                             token_of, ws, s);
     if (st) return st;
   }
+  if (!dst) return MOE_OK;
   return permute_rows_launch(src, row_of, row_scale, (int)sh->T, (int)sh->k, (int)sh->d,
                              elem_bytes(sh), dst, s);
 }
@@ -428,6 +464,43 @@ int moe_grouped_gemm_bwd(const moe_shape* sh, const int32_t* offsets, const void
   return bwd_sequence(sh, a, (hipStream_t)stream);
 }
 
+int moe_grouped_gemm_fwd_gather(const moe_shape* sh, const int32_t* offsets,
+                                const int32_t* token_of, const void* x, const void* W1,
+                                const void* W3, const void* W2, void* ab, void* h, void* o,
+                                void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f)) || (st = check_gather(sh))) return st;
+  if (!offsets || !token_of || !x || !W1 || !W3 || !W2 || !ab || !h || !o) return MOE_ERR_INVALID;
+  GemmArgs a = expert_args(sh, offsets);
+  set_rows(a, sh, RowSrc{nullptr, token_of, x});
+  a.W1 = W1; a.W3 = W3; a.W2 = W2;
+  a.ab_out = ab; a.h_out = h; a.h = h; a.o_out = o;
+  return fwd_sequence(sh, a, (hipStream_t)stream);
+}
+
+int moe_grouped_gemm_bwd_gather(const moe_shape* sh, const int32_t* offsets,
+                                const int32_t* token_of, const void* x, const void* ab,
+                                const void* h, const void* dO, const void* W1, const void* W3,
+                                const void* W2, void* dab, void* dXp, void* dW1, void* dW3,
+                                void* dW2, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f)) || (st = check_gather(sh))) return st;
+  if (!offsets || !token_of || !x || !ab || !h || !dO || !W1 || !W3 || !W2 || !dab || !dXp ||
+      !dW1 || !dW3 || !dW2)
+    return MOE_ERR_INVALID;
+  GemmArgs a = expert_args(sh, offsets);
+  set_rows(a, sh, RowSrc{nullptr, token_of, x});
+  a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
+  a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
+  return bwd_sequence(sh, a, (hipStream_t)stream);
+}
+
 int moe_row_probs(const moe_shape* sh, const int32_t* row_of, const float* topk_prob,
                   float* row_prob, void* stream) {
   int st = check_shape(sh);
@@ -445,10 +518,8 @@ int moe_grouped_gemm_fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
   if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!offsets || !xp || !W1 || !W3 || !W2 || !row_prob || !ab || !h || !o) return MOE_ERR_INVALID;
-  GemmArgs a = expert_args(sh, offsets);
-  a.xp = xp; a.W1 = W1; a.W3 = W3; a.W2 = W2; a.row_prob = row_prob;
-  a.ab_out = ab; a.h_out = h; a.h = h; a.o_out = o;
-  return fwd_sequence(sh, a, (hipStream_t)stream);
+  return fwd_rowscaled(sh, offsets, RowSrc{xp, nullptr, nullptr}, W1, W3, W2, row_prob, ab, h, o,
+                       stream);
 }
 
 int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const void* xp,
@@ -465,8 +536,34 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
       !dW1 || !dW3 || !dW2)
     return MOE_ERR_INVALID;
   if (!ws || ws_bytes < dp_part_bytes(sh)) return MOE_ERR_WORKSPACE;
+  return bwd_rowscaled(sh, offsets, RowSrc{xp, nullptr, nullptr}, ab, h, recompute_h, dO, W1, W3,
+                       W2, row_prob, dab, dXp, dW1, dW3, dW2, row_of, dprob, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Row-scaled expert forward and backward (bf16; arguments checked by the caller).
+int fwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const RowSrc& rows, const void* W1,
+                  const void* W3, const void* W2, const float* row_prob, void* ab, void* h, void* o,
+                  void* stream) {
   GemmArgs a = expert_args(sh, offsets);
-  a.xp = xp; a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
+  set_rows(a, sh, rows);
+  a.W1 = W1; a.W3 = W3; a.W2 = W2; a.row_prob = row_prob;
+  a.ab_out = ab; a.h_out = h; a.h = h; a.o_out = o;
+  return fwd_sequence(sh, a, (hipStream_t)stream);
+}
+
+int bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, const RowSrc& rows, const void* ab,
+                  void* h, int32_t recompute_h, const void* dO, const void* W1, const void* W3,
+                  const void* W2, const float* row_prob, void* dab, void* dXp, void* dW1,
+                  void* dW3, void* dW2, const int32_t* row_of, float* dprob, void* ws,
+                  void* stream) {
+  int st;
+  GemmArgs a = expert_args(sh, offsets);
+  set_rows(a, sh, rows);
+  a.ab = ab; a.h = h; a.dO = dO; a.W1 = W1; a.W3 = W3; a.W2 = W2;
   a.dab_out = dab; a.dXp_out = dXp; a.dW1 = dW1; a.dW3 = dW3; a.dW2 = dW2;
   a.row_prob = row_prob;
   a.dp_part = (float*)ws;
@@ -484,6 +581,10 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
   return dp_rows_launch((const float*)ws, (int)((sh->f + 255) / 256), row_of,
                         (int)(sh->T * sh->k), dprob, s);
 }
+
+}  // namespace
+
+extern "C" {
 
 int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* counts,
                  float alpha, float* loss, void* ws, size_t ws_bytes, void* stream) {
@@ -683,9 +784,10 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io || !io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
-      !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xp ||
-      !io->ab || !io->h || !io->o || !io->y)
+      !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of ||
+      (!io->xp && !io->fused_permute) || !io->ab || !io->h || !io->o || !io->y)
     return MOE_ERR_INVALID;
+  if (io->fused_permute && (st = check_gather(sh))) return st;
   if (sh->f_shared &&
       (!io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h || !io->ys))
     return MOE_ERR_INVALID;
@@ -695,13 +797,18 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
 
   if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
     return st;
+  // fused permutation: the map alone; fc1 reads x through token_of
   if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
-                        io->token_of, io->xp, ws, pws, stream)))
+                        io->token_of, io->fused_permute ? nullptr : io->xp, ws, pws, stream)))
     return st;
   if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
-  if ((st = moe_grouped_gemm_fwd(sh, io->offsets, io->xp, io->W1, io->W3, io->W2, io->ab, io->h,
-                                 io->o, nullptr, 0, stream)))
-    return st;
+  {
+    GemmArgs a = expert_args(sh, io->offsets);
+    set_rows(a, sh, rows_of(io));
+    a.W1 = io->W1; a.W3 = io->W3; a.W2 = io->W2;
+    a.ab_out = io->ab; a.h_out = io->h; a.h = io->h; a.o_out = io->o;
+    if ((st = fwd_sequence(sh, a, s))) return st;
+  }
   const void* add = nullptr;
   if (sh->f_shared) {
     int32_t* off2 = (int32_t*)((char*)ws + pws);
@@ -725,9 +832,11 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io || !io->dY || !io->W1 || !io->W3 || !io->W2 || !io->topk_prob || !io->offsets ||
-      !io->row_of || !io->xp || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX ||
+      !io->row_of || !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX ||
       !io->dW1 || !io->dW3 || !io->dW2)
     return MOE_ERR_INVALID;
+  if (io->fused_permute ? (!io->token_of || !io->x) : !io->xp) return MOE_ERR_INVALID;
+  if (io->fused_permute && (st = check_gather(sh))) return st;
   if (sh->f_shared && (!io->x || !io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h ||
                        !io->s_dab || !io->dXs || !io->dWs1 || !io->dWs3 || !io->dWs2))
     return MOE_ERR_INVALID;
@@ -736,10 +845,13 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
 
   // dO[row_of[t][j]] = p[t][j] * dY[t] (+ dprob and the router gradient when asked for)
   if ((st = layer_combine_bwd(sh, io, stream))) return st;
-  if ((st = moe_grouped_gemm_bwd(sh, io->offsets, io->xp, io->ab, io->h, io->dO, io->W1, io->W3,
-                                 io->W2, io->dab, io->dXp, io->dW1, io->dW3, io->dW2, nullptr, 0,
-                                 stream)))
-    return st;
+  {
+    GemmArgs a = expert_args(sh, io->offsets);
+    set_rows(a, sh, rows_of(io));
+    a.ab = io->ab; a.h = io->h; a.dO = io->dO; a.W1 = io->W1; a.W3 = io->W3; a.W2 = io->W2;
+    a.dab_out = io->dab; a.dXp_out = io->dXp; a.dW1 = io->dW1; a.dW3 = io->dW3; a.dW2 = io->dW2;
+    if ((st = bwd_sequence(sh, a, s))) return st;
+  }
   const void* add = nullptr;
   if (sh->f_shared) {
     int32_t* off2 = (int32_t*)ws;
@@ -869,9 +981,10 @@ int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
   if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
   if (!io->logits || !io->x || !io->W1 || !io->W3 || !io->W2 || !io->topk_idx ||
-      !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of || !io->xp ||
-      !io->ab || !io->h || !io->o || !io->y || !io->row_prob)
+      !io->topk_prob || !io->counts || !io->offsets || !io->row_of || !io->token_of ||
+      (!io->xp && !io->fused_permute) || !io->ab || !io->h || !io->o || !io->y || !io->row_prob)
     return MOE_ERR_INVALID;
+  if (io->fused_permute && (st = check_gather(sh))) return st;
   if (sh->f_shared &&
       (!io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h || !io->ys))
     return MOE_ERR_INVALID;
@@ -881,12 +994,12 @@ int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
   if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
     return st;
   if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
-                        io->token_of, io->xp, ws, pws, stream)))
+                        io->token_of, io->fused_permute ? nullptr : io->xp, ws, pws, stream)))
     return st;
   if ((st = layer_aux_loss(sh, io, ws, ws_bytes, stream))) return st;
   if ((st = moe_row_probs(sh, io->row_of, io->topk_prob, io->row_prob, stream))) return st;
-  if ((st = moe_grouped_gemm_fwd_rowscaled(sh, io->offsets, io->xp, io->W1, io->W3, io->W2,
-                                           io->row_prob, io->ab, io->h, io->o, stream)))
+  if ((st = fwd_rowscaled(sh, io->offsets, rows_of(io), io->W1, io->W3, io->W2, io->row_prob,
+                          io->ab, io->h, io->o, stream)))
     return st;
   const void* add = nullptr;
   if (sh->f_shared) {
@@ -909,10 +1022,12 @@ int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
   if (sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if ((st = check_gemm_dims(sh, sh->T * sh->k, sh->f))) return st;
   if (sh->f_shared && (st = check_gemm_dims(sh, sh->T, sh->f_shared))) return st;
-  if (!io->dY || !io->W1 || !io->W3 || !io->W2 || !io->offsets || !io->row_of || !io->xp ||
+  if (!io->dY || !io->W1 || !io->W3 || !io->W2 || !io->offsets || !io->row_of ||
       !io->ab || !io->h || !io->dO || !io->dab || !io->dXp || !io->dX || !io->dW1 || !io->dW3 ||
       !io->dW2 || !io->row_prob)
     return MOE_ERR_INVALID;
+  if (io->fused_permute ? (!io->token_of || !io->x) : !io->xp) return MOE_ERR_INVALID;
+  if (io->fused_permute && (st = check_gather(sh))) return st;
   if (sh->f_shared && (!io->x || !io->Ws1 || !io->Ws3 || !io->Ws2 || !io->s_ab || !io->s_h ||
                        !io->s_dab || !io->dXs || !io->dWs1 || !io->dWs3 || !io->dWs2))
     return MOE_ERR_INVALID;
@@ -927,12 +1042,10 @@ int layer_bwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
                         io->dO, nullptr, 0, stream)))
     return st;
   // dprob[t][j] too when the router gradient is asked for
-  if ((st = moe_grouped_gemm_bwd_rowscaled(sh, io->offsets, io->xp, io->ab, io->h,
-                                           io->memory_efficient == 2, io->dO, io->W1, io->W3,
-                                           io->W2, io->row_prob, io->dab, io->dXp, io->dW1,
-                                           io->dW3, io->dW2, io->row_of,
-                                           io->dlogits ? io->dprob : nullptr, dp_part, part,
-                                           stream)))
+  if ((st = bwd_rowscaled(sh, io->offsets, rows_of(io), io->ab, io->h, io->memory_efficient == 2,
+                          io->dO, io->W1, io->W3, io->W2, io->row_prob, io->dab, io->dXp,
+                          io->dW1, io->dW3, io->dW2, io->row_of,
+                          io->dlogits ? io->dprob : nullptr, dp_part, stream)))
     return st;
   const void* add = nullptr;
   if (sh->f_shared) {

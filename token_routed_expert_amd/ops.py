@@ -104,6 +104,25 @@ def moe_grouped_gemm_bwd(sh, offsets, xp, ab, h, dO, W1, W3, W2, dab, dXp, dW1, 
                                         None, 0, _stream(stream)), "moe_grouped_gemm_bwd")
 
 
+def moe_grouped_gemm_fwd_gather(sh, offsets, token_of, x, W1, W3, W2, ab, h, o, stream=None):
+    """moe_grouped_gemm_fwd with fc1 reading row token_of[r] of x (no xp)."""
+    _check(N.lib().moe_grouped_gemm_fwd_gather(C.byref(sh), _ptr(offsets, I32), _ptr(token_of, I32),
+                                               _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(ab),
+                                               _ptr(h), _ptr(o), None, 0, _stream(stream)),
+           "moe_grouped_gemm_fwd_gather")
+
+
+def moe_grouped_gemm_bwd_gather(sh, offsets, token_of, x, ab, h, dO, W1, W3, W2, dab, dXp, dW1,
+                                dW3, dW2, stream=None):
+    """moe_grouped_gemm_bwd with the fc1 weight gradient reading row
+    token_of[r] of x (no xp)."""
+    _check(N.lib().moe_grouped_gemm_bwd_gather(C.byref(sh), _ptr(offsets, I32), _ptr(token_of, I32),
+                                               _ptr(x), _ptr(ab), _ptr(h), _ptr(dO), _ptr(W1),
+                                               _ptr(W3), _ptr(W2), _ptr(dab), _ptr(dXp), _ptr(dW1),
+                                               _ptr(dW3), _ptr(dW2), None, 0, _stream(stream)),
+           "moe_grouped_gemm_bwd_gather")
+
+
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
@@ -255,6 +274,7 @@ def _io(buffers: dict) -> N.moe_layer_io:
         io.wmx = C.cast(C.pointer(wmx.struct), C.c_void_p).value
     io.aux_alpha = float(buffers.get("aux_alpha", 0.0))
     io.memory_efficient = int(buffers.get("memory_efficient", 0))
+    io.fused_permute = int(buffers.get("fused_permute", 0))
     return io
 
 
