@@ -120,11 +120,12 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(const char* p) {
 // the same DMA (the permutation fused into the operand loader).  fc1 forward
 // takes the rows' offsets once per tile.  In the fc1 weight gradient the rows
 // run along K, so every stage needs new ones: the wavefront's two A DMA
-// instructions cover the same four k-rows (both 128-column halves), and four
+// instructions cover the same four k-rows (both 128-column halves), and five
 // stages ahead each wavefront DMAs the token ids of those rows into one of
-// four LDS slots of its own (one more load per stage in the wait counts); right
-// after the stage's barrier, when none of its LDS reads is pending, it turns
-// them into the lane offsets of the A loads it issues next.
+// eight LDS slots of its own (one more load per stage in the wait counts).  It
+// reads the ids of stage kt + 3 at the top of stage kt, where they have
+// landed, and turns them into the lane offsets of that stage's A loads after
+// the stage's barrier, so the read's latency hides under the MFMAs between.
 template <int OP, int NW, bool RS, bool GATHER = false>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
@@ -143,14 +144,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   constexpr int LOOK = NS - 1;  // stage kt + LOOK is issued during stage kt
   // gathered weight gradient: token ids of stage kt + TLOOK are loaded in stage kt
   constexpr bool GW = GATHER && OP == OP_FC1_WGRAD;
-  constexpr int TLOOK = LOOK + 1;
+  constexpr int TLOOK = LOOK + 2;
   constexpr int VM_STAGE = LOADS_PER_STAGE + (GW ? 1 : 0);  // vector-memory loads per stage
 
   // the stage ring, then (ragged M) the schedule scratch, the inclusive prefix
   // of the experts' M-tile counts and (row-scaled fc2 dgrad) the wavefronts'
   // per-row <h, dh'> partials
-  // (gathered weight gradient: four 256-byte token slots per wavefront)
-  constexpr int TSLOTS = 4;
+  // (gathered weight gradient: eight 256-byte token slots per wavefront)
+  constexpr int TSLOTS = 8;
   constexpr int EXTRA = TR::ragged_m ? (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4
                                      : (GW ? NW * TSLOTS * 256 : 0);
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + EXTRA];
@@ -330,13 +331,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   };
   // A offsets of stage s from its token ids (landed for this wavefront): x row
   // token * d for the lane's k-row, past the range for k-rows past the tile's
-  auto gather_offsets = [&](int s) __attribute__((always_inline)) {
+  auto read_tok = [&](int s) __attribute__((always_inline)) -> int {
+    return *(const __attribute__((address_space(3))) int*)(
+        lds + NS * STAGE_BYTES + (wid * TSLOTS + ((tphase + s) & (TSLOTS - 1))) * 256 +
+        (lane >> 4) * 4);
+  };
+  auto gather_offsets = [&](int s, int tok) __attribute__((always_inline)) {
     const bool in_cur = s < cur.KT;
     const int ks = (in_cur ? s : s - cur.KT) * BK + 4 * wid;
     const int lim = (in_cur ? cur.rows : nxt.rows) - ks;  // valid k-rows of the four
-    const int tok = *(const __attribute__((address_space(3))) int*)(
-        lds + NS * STAGE_BYTES + (wid * TSLOTS + ((tphase + s) & (TSLOTS - 1))) * 256 +
-        (lane >> 4) * 4);
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q)
       gofs[q] = (lane >> 4) < lim ? (uint32_t)tok * a_ld + (in_cur ? cur.a_off[q] : nxt.a_off[q])
@@ -459,9 +462,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst,
                         auto TAIL, auto SKIP) __attribute__((always_inline)) {
     constexpr bool skip = decltype(SKIP)::value;
-    // gathered weight gradient: the token ids of stage kt + 4, ahead of this
-    // stage's B loads (the wait below counts it)
-    if constexpr (GW) issue_tok(kt + TLOOK);
+    // gathered weight gradient: the ids of stage kt + 3 (landed: issued
+    // before stage kt's B loads) are read first; those of stage kt + 5 are
+    // loaded ahead of this stage's B loads (the wait below counts them)
+    int tok = 0;
+    if constexpr (GW) {
+      tok = read_tok(kt + LOOK);
+      issue_tok(kt + TLOOK);
+    }
     // B fragments HB..FN-1 for the second half: issued first, needed last
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b1[U.value] = read_b(st, HB + U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
@@ -485,9 +493,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     // takes stage kt+3
     wait_vmcnt<VM_STAGE * (LOOK - 2)>();
     block_barrier();
-    // the token ids of stage kt + 3 have landed (issued before stage kt + 1's
-    // B loads); no LDS read of this wavefront is pending here
-    if constexpr (GW) gather_offsets(kt + LOOK);
+    // the A offsets of stage kt + 3, issued in the second half
+    if constexpr (GW) gather_offsets(kt + LOOK, tok);
     // next stage's B fragments 0..HB-1 first: the next first half starts with them
     static_for<0, HB>([&](auto U) __attribute__((always_inline)) { b0[U.value] = read_b(nst, U.value); });
     static_for<0, 4>([&](auto U) __attribute__((always_inline)) {
@@ -535,12 +542,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       // stages 0 .. LOOK-2 and stage LOOK-1's A half in flight (its B half
       // follows in stage 0); wait for stage 0 and make it visible
       static_for<0, LOOK - 1>([&](auto S) __attribute__((always_inline)) {
-        if constexpr (GW) gather_offsets(S.value);
+        if constexpr (GW) gather_offsets(S.value, read_tok(S.value));
         static_for<0, 2 * DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) {
           issue_one(S.value, Q, IntC<1>{});
         });
       });
-      if constexpr (GW) gather_offsets(LOOK - 1);
+      if constexpr (GW) gather_offsets(LOOK - 1, read_tok(LOOK - 1));
       static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(LOOK - 1, Q, IntC<1>{}); });
       wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE>();
       block_barrier();
