@@ -122,11 +122,16 @@ def mfma_probe(iters: int = 4096):
 
 def router_grad_calls(wl, sh, b, ws_aux):
     """(aux loss after the permutation, combine backward with dprob, router
-    backward) as three callables, or no-ops when router_grad is off."""
+    backward, routing) as four callables: the routing is moe_route_aux, which
+    also writes the loss's column sums, and the loss is then formed from them
+    and the counts."""
     import token_routed_expert_amd as tre
 
+    def route():
+        tre.moe_route_aux(b["logits"], wl.k, b["topk_idx"], b["topk_prob"], ws_aux)
+
     def aux():
-        tre.moe_aux_loss(b["logits"], wl.k, b["counts"], b["aux_alpha"], b["aux_loss"], ws_aux)
+        tre.moe_aux_loss_final(ws_aux, wl.T, wl.E, wl.k, b["counts"], b["aux_alpha"], b["aux_loss"])
 
     def comb_bwd():
         tre.moe_combine_bwd(sh, b["dY"], b["o"], b["row_of"], b["topk_prob"], b["dO"], b["dprob"])
@@ -135,7 +140,7 @@ def router_grad_calls(wl, sh, b, ws_aux):
         tre.moe_route_bwd(b["logits"], wl.k, b["topk_idx"], b["topk_prob"], b["dprob"], b["counts"],
                           b["aux_alpha"], 1.0, b["dlogits"])
 
-    return aux, comb_bwd, route_bwd
+    return aux, comb_bwd, route_bwd, route
 
 
 def build_step(wl, inp, router_grad=False, memory_efficient=False, fused=False):
@@ -187,7 +192,10 @@ def build_step(wl, inp, router_grad=False, memory_efficient=False, fused=False):
 
     def step(ev):
         ev["start"].record()
-        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        if rg:
+            rg[3]()
+        else:
+            tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
         ev["route"].record()
         tre.moe_permute(sh, None if fused else b["x"], b["topk_idx"], None, 1, b["counts"],
                         b["offsets"], b["row_of"], b["token_of"], xp, wsf)
@@ -259,7 +267,10 @@ def build_step_rowscaled(wl, sh, b, wsf, wsb, shared, rg, memory_efficient):
 
     def step(ev):
         ev["start"].record()
-        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        if rg:
+            rg[3]()
+        else:
+            tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
         ev["route"].record()
         tre.moe_permute(sh, b["x"], b["topk_idx"], None, 1, b["counts"], b["offsets"], b["row_of"],
                         b["token_of"], b["xp"], wsf)
@@ -321,7 +332,10 @@ def build_step_e4m3(wl, inp, sh, b, wsf, wsb, rg=None):
 
     def step(ev):
         ev["start"].record()
-        tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
+        if rg:
+            rg[3]()
+        else:
+            tre.moe_route(b["logits"], wl.k, b["topk_idx"], b["topk_prob"])
         ev["route"].record()
         quant_rows(b["x"], b["xq"], b["xs"])
         permute8(sh, b["xq"], b["xs"], b["topk_idx"], 1, b["counts"], b["offsets"],

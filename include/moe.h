@@ -287,9 +287,9 @@ typedef struct {
  * moe_unpermute in sequence on one stream.  For MOE_E4M3: moe_route,
  * moe_quantize_rows of x into xq/xs, moe_permute_e4m3 into xpq/xps,
  * moe_grouped_gemm_fwd_e4m3, moe_unpermute (MOE_MXFP8: the _mx calls, weights
- * io->wmx).  With io->aux_loss set, also
- * moe_aux_loss (alpha = io->aux_alpha) after the permutation; ws_bytes then
- * needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient:
+ * io->wmx).  With io->aux_loss set, the routing is moe_route_aux and
+ * moe_aux_loss_final (alpha = io->aux_alpha) follows the permutation;
+ * ws_bytes then needs MOE_WS_AUX_LOSS more bytes.  With io->memory_efficient:
  * moe_row_probs into io->row_prob, the row-scaled expert forward (bf16:
  * moe_grouped_gemm_fwd_rowscaled; e4m3 / MXFP8: fc1's epilogue scales h by p
  * before h is quantised) and an unweighted moe_unpermute.
@@ -439,6 +439,22 @@ int moe_grouped_gemm_bwd_e4m3(const moe_shape* sh, const int32_t* offsets,
  */
 int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int32_t* counts,
                  float alpha, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_aux / moe_aux_loss_final -- moe_route fused with the first half
+ * of moe_aux_loss (the pages fuse routing with the auxiliary-loss
+ * computation: German technical summary, section 2 D).  moe_route_aux writes
+ * topk_idx and topk_prob bit-identical to moe_route and, into ws (ws_bytes >=
+ * moe_workspace_bytes(sh with this T and E, MOE_WS_AUX_LOSS)), the softmax
+ * column sums of each 32-token block; once the permutation has produced the
+ * counts, moe_aux_loss_final (the same ws, T, E, k) writes *loss, bit-
+ * identical to moe_aux_loss on the same logits and counts.  One kernel fewer
+ * than moe_route followed by moe_aux_loss.  Errors as moe_aux_loss.
+ */
+int moe_route_aux(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* topk_idx,
+                  float* topk_prob, void* ws, size_t ws_bytes, void* stream);
+int moe_aux_loss_final(const void* ws, int64_t T, int64_t E, int64_t k, const int32_t* counts,
+                       float alpha, float* loss, void* stream);
 
 /*
  * moe_combine_bwd -- the backward of the weighted combine with the

@@ -178,6 +178,43 @@ def test_aux_loss(T, E, k, skew):
         assert abs(got - 0.01) <= 1e-8        # one expert: f = P = 1, L = alpha
 
 
+@pytest.mark.parametrize("T,E,k,skew", [(1, 12, 1, False), (63, 8, 2, False), (65, 8, 2, True),
+                                        (8200, 128, 8, True), (4097, 256, 8, False),
+                                        (300, 1, 1, False), (1000, 200, 6, False),
+                                        (777, 33, 7, True), (129, 64, 64, False)])
+def test_route_aux_fused(T, E, k, skew):
+    """moe_route_aux: indices and probabilities bit-identical to moe_route;
+    moe_aux_loss_final after it bit-identical to moe_aux_loss, and within
+    the loss tolerance of the oracle."""
+    import token_routed_expert_amd as tre
+    from token_routed_expert_amd import _native as N
+    L, Lg, idx, prob, counts, _, _ = routed(T, E, k, seed=T + 3 * E, skew=skew and E > 10 + k)
+    if T > 100:
+        Lg[5, :] = float("nan")                     # a NaN row routes as moe_route does
+        Lg[7, ::3] = float("nan")
+        tre.moe_route(Lg, k, idx, prob)
+    sh = tre.make_shape(T, 128, E, k, 128, 0, "bf16")
+    wsb = max(256, tre.moe_workspace_bytes(sh, N.MOE_WS_AUX_LOSS))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    idx2 = torch.full_like(idx, -9)
+    prob2 = torch.full_like(prob, 5.0)
+    tre.moe_route_aux(Lg, k, idx2, prob2, ws)
+    assert torch.equal(idx2, idx)
+    assert torch.equal(prob2.view(torch.int32), prob.view(torch.int32))
+    if T > 100:
+        Lg = L.cuda()                               # the loss on finite logits
+        tre.moe_route_aux(Lg, k, idx2, prob2, ws)
+    c = torch.from_numpy(counts.astype(np.int32)).cuda()
+    loss = torch.full((1,), float("nan"), device="cuda")
+    tre.moe_aux_loss_final(ws, T, E, k, c, 0.01, loss)
+    ws2 = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    loss2 = torch.full((1,), float("nan"), device="cuda")
+    tre.moe_aux_loss(Lg, k, c, 0.01, loss2, ws2)
+    assert torch.equal(loss.view(torch.int32), loss2.view(torch.int32)), (float(loss), float(loss2))
+    ref, _ = oracle.aux_loss(L.numpy(), counts, k, 0.01)
+    assert abs(float(loss) - ref) <= LOSS_TOL * abs(ref), (float(loss), ref)
+
+
 def test_aux_loss_uniform_router():
     """Equal logits: P_e = 1/E and sum_e f_e = 1, so L = alpha exactly."""
     T, E, k = 1000, 64, 4

@@ -9,7 +9,7 @@ from .ops import (E4M3Weights, MXWeights, MoeError, make_shape, moe_aux_loss, mo
                   moe_permute_mx, moe_grouped_gemm_fwd_mx, moe_grouped_gemm_bwd_mx,
                   moe_row_probs, moe_grouped_gemm_fwd_rowscaled, moe_grouped_gemm_bwd_rowscaled,
                   moe_grouped_gemm_bwd, moe_route_bwd, moe_grouped_gemm_fwd_gather,
-                  moe_grouped_gemm_bwd_gather,
+                  moe_grouped_gemm_bwd_gather, moe_route_aux, moe_aux_loss_final,
                   moe_grouped_gemm_bwd_e4m3, moe_grouped_gemm_fwd, moe_grouped_gemm_fwd_e4m3,
                   moe_layer_bwd, moe_layer_fwd, moe_permute, moe_permute_e4m3, moe_permute_noalloc,
                   moe_quantize_rows, moe_quantize_token_blocks, moe_quantize_weights, moe_route,
@@ -26,4 +26,5 @@ __all__ = ["MoeError", "make_shape", "moe_route", "moe_permute", "moe_unpermute"
            "moe_quantize_weights_mx", "moe_quantize_token_blocks_mx", "moe_permute_mx",
            "moe_grouped_gemm_fwd_mx", "moe_grouped_gemm_bwd_mx", "moe_probe_mfma",
            "moe_permute_noalloc", "moe_grouped_gemm_fwd_gather",
-           "moe_grouped_gemm_bwd_gather", "_native"]
+           "moe_grouped_gemm_bwd_gather", "moe_route_aux",
+           "moe_aux_loss_final", "_native"]

@@ -94,6 +94,8 @@ _PROTOS = {
                                           C.POINTER(moe_mx_weights), _P, _P, _P, _P, _P, _P,
                                           C.c_size_t, _P]),
     "moe_aux_loss": (C.c_int, [_P, _I64, _I64, _I64, _P, C.c_float, _P, _P, C.c_size_t, _P]),
+    "moe_route_aux": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, C.c_size_t, _P]),
+    "moe_aux_loss_final": (C.c_int, [_P, _I64, _I64, _I64, _P, C.c_float, _P, _P]),
     "moe_combine_bwd": (C.c_int, [_SH, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, C.c_float, C.c_float, _P,
                                 _P]),

@@ -11,6 +11,10 @@ namespace tre {
 // route.hip
 int route_launch(const float* logits, int T, int E, int k, int32_t* idx, float* prob,
                  hipStream_t s);
+// routing plus the load-balancing loss's per-32-token softmax column sums
+// (partial [ceil(T/32)][E], the layout aux_final_launch reads)
+int route_aux_launch(const float* logits, int T, int E, int k, int32_t* idx, float* prob,
+                     float* partial, hipStream_t s);
 
 // permute.hip
 size_t permute_ws_bytes(int64_t T, int64_t E);
@@ -42,6 +46,9 @@ int dp_rows_launch(const float* part, int NT, const int32_t* row_of, int n, floa
                    hipStream_t s);
 int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* counts, float alpha,
                     float* loss, void* ws, hipStream_t s);
+// the loss from the column-sum partials and the counts
+int aux_final_launch(const float* partial, int T, int E, int k, const int32_t* counts,
+                     float alpha, float* loss, hipStream_t s);
 
 // Grouped-GEMM problem: which of the six expert products to run.
 enum GemmOp {

@@ -233,6 +233,8 @@ int layer_bwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
                    void* stream);
 int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream);
+int layer_route(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                void* stream);
 bool aux_ws_ok(const moe_shape* sh, const moe_layer_io* io, size_t ws_bytes);
 int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                         void* stream);
@@ -597,6 +599,27 @@ int moe_aux_loss(const float* logits, int64_t T, int64_t E, int64_t k, const int
                          (hipStream_t)stream);
 }
 
+int moe_route_aux(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* topk_idx,
+                  float* topk_prob, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !topk_idx || !topk_prob) return MOE_ERR_INVALID;
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T >= (1 << 30)) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < aux_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return route_aux_launch(logits, (int)T, (int)E, (int)k, topk_idx, topk_prob, (float*)ws,
+                          (hipStream_t)stream);
+}
+
+int moe_aux_loss_final(const void* ws, int64_t T, int64_t E, int64_t k, const int32_t* counts,
+                       float alpha, float* loss, void* stream) {
+  if (!ws || !counts || !loss) return MOE_ERR_INVALID;
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T >= (1 << 30)) return MOE_ERR_UNSUPPORTED;
+  return aux_final_launch((const float*)ws, (int)T, (int)E, (int)k, counts, alpha, loss,
+                          (hipStream_t)stream);
+}
+
 int moe_combine_bwd(const moe_shape* sh, const void* dY, const void* o, const int32_t* row_of,
                     const float* topk_prob, void* dO, float* dprob, void* stream) {
   int st = check_shape(sh);
@@ -795,8 +818,7 @@ int moe_layer_fwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
   if (!ws || ws_bytes < pws + 256 || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
 
-  if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
-    return st;
+  if ((st = layer_route(sh, io, ws, ws_bytes, stream))) return st;
   // fused permutation: the map alone; fc1 reads x through token_of
   if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
                         io->token_of, io->fused_permute ? nullptr : io->xp, ws, pws, stream)))
@@ -888,8 +910,7 @@ int layer_fwd_e4m3(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t
   const size_t pws = permute_ws_bytes(sh->T, sh->E);
   const size_t gws = fwd8_ws_bytes(sh);
   if (!ws || ws_bytes < pws + gws || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
-  if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
-    return st;
+  if ((st = layer_route(sh, io, ws, ws_bytes, stream))) return st;
   if ((st = (mx ? moe_quantize_rows_mx(io->x, MOE_BF16, sh->T, sh->d, io->xq,
                                        (uint8_t*)io->xs, stream)
                  : moe_quantize_rows(io->x, MOE_BF16, sh->T, sh->d, io->xq, io->xs, stream))))
@@ -962,15 +983,28 @@ bool aux_ws_ok(const moe_shape* sh, const moe_layer_io* io, size_t ws_bytes) {
          ws_bytes >= moe_workspace_bytes(sh, MOE_WS_LAYER_FWD) + aux_ws_bytes(sh->T, sh->E);
 }
 
-// aux loss after the permutation's counts, when io->aux_loss is set
+// Routing of a layer; when io->aux_loss is set, fused with the loss's
+// softmax column sums, which go to the aux region of the forward workspace
+// (after the MOE_WS_LAYER_FWD bytes, untouched by the permutation).
+int layer_route(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!io->aux_loss)
+    return moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream);
+  const size_t base = moe_workspace_bytes(sh, MOE_WS_LAYER_FWD);
+  const size_t need = aux_ws_bytes(sh->T, sh->E);
+  if (ws_bytes < base + need) return MOE_ERR_WORKSPACE;
+  return moe_route_aux(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob,
+                       (char*)ws + base, need, stream);
+}
+
+// aux loss from those column sums and the permutation's counts
 int layer_aux_loss(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t ws_bytes,
                    void* stream) {
   if (!io->aux_loss) return MOE_OK;
   const size_t base = moe_workspace_bytes(sh, MOE_WS_LAYER_FWD);
-  const size_t need = aux_ws_bytes(sh->T, sh->E);
-  if (ws_bytes < base + need) return MOE_ERR_WORKSPACE;
-  return moe_aux_loss(io->logits, sh->T, sh->E, sh->k, io->counts, io->aux_alpha, io->aux_loss,
-                      (char*)ws + base, need, stream);
+  if (ws_bytes < base + aux_ws_bytes(sh->T, sh->E)) return MOE_ERR_WORKSPACE;
+  return moe_aux_loss_final((char*)ws + base, sh->T, sh->E, sh->k, io->counts, io->aux_alpha,
+                            io->aux_loss, stream);
 }
 
 // Memory-efficient layer (probabilities applied before W2), bf16 only.
@@ -991,8 +1025,7 @@ int layer_fwd_rowscaled(const moe_shape* sh, const moe_layer_io* io, void* ws, s
   const size_t pws = permute_ws_bytes(sh->T, sh->E);
   if (!ws || ws_bytes < pws + 256 || !aux_ws_ok(sh, io, ws_bytes)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = moe_route(io->logits, sh->T, sh->E, sh->k, io->topk_idx, io->topk_prob, stream)))
-    return st;
+  if ((st = layer_route(sh, io, ws, ws_bytes, stream))) return st;
   if ((st = moe_permute(sh, io->x, io->topk_idx, nullptr, 1, io->counts, io->offsets, io->row_of,
                         io->token_of, io->fused_permute ? nullptr : io->xp, ws, pws, stream)))
     return st;

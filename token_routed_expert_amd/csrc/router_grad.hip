@@ -372,16 +372,22 @@ size_t aux_ws_bytes(int64_t T, int64_t E) {
   return align_up((size_t)((T + AUX_TOK - 1) / AUX_TOK) * (size_t)E * sizeof(float), 256);
 }
 
+int aux_final_launch(const float* partial, int T, int E, int k, const int32_t* counts,
+                     float alpha, float* loss, hipStream_t s) {
+  const int NB = (T + AUX_TOK - 1) / AUX_TOK;
+  const float scale = (float)((double)alpha * E / ((double)T * T * k));
+  aux_final_kernel<<<1, 1024, 0, s>>>(partial, NB, E, counts, scale, loss);
+  TRE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 int aux_loss_launch(const float* logits, int T, int E, int k, const int32_t* counts, float alpha,
                     float* loss, void* ws, hipStream_t s) {
   const int NB = (T + AUX_TOK - 1) / AUX_TOK;
   float* partial = (float*)ws;
   aux_partial_kernel<<<NB, 256, 0, s>>>(logits, T, E, partial);
   TRE_LAUNCH_CHECK();
-  const float scale = (float)((double)alpha * E / ((double)T * T * k));
-  aux_final_kernel<<<1, 1024, 0, s>>>(partial, NB, E, counts, scale, loss);
-  TRE_LAUNCH_CHECK();
-  return MOE_OK;
+  return aux_final_launch(partial, T, E, k, counts, alpha, loss, s);
 }
 
 }  // namespace tre

@@ -313,6 +313,21 @@ def moe_aux_loss(logits, k, counts, alpha, loss, ws, stream=None):
            "moe_aux_loss")
 
 
+def moe_route_aux(logits, k, topk_idx, topk_prob, ws, stream=None):
+    """moe_route plus the load-balancing loss's column sums (into ws)."""
+    T, E = logits.shape
+    _check(N.lib().moe_route_aux(_ptr(logits, F32), T, E, k, _ptr(topk_idx, I32),
+                                 _ptr(topk_prob, F32), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_route_aux")
+
+
+def moe_aux_loss_final(ws, T, E, k, counts, alpha, loss, stream=None):
+    """The load-balancing loss from moe_route_aux's column sums and the counts."""
+    _check(N.lib().moe_aux_loss_final(_ptr(ws), int(T), int(E), int(k), _ptr(counts, I32),
+                                      float(alpha), _ptr(loss, F32), _stream(stream)),
+           "moe_aux_loss_final")
+
+
 def moe_combine_bwd(sh, dY, o, row_of, topk_prob, dO, dprob, stream=None):
     """dO = p * dY permuted, and dprob[t][j] = <dY[t], o[row_of[t][j]]>."""
     _check(N.lib().moe_combine_bwd(C.byref(sh), _ptr(dY), _ptr(o), _ptr(row_of, I32),
