@@ -313,10 +313,14 @@ def test_layer_full_size_sampled(wl):
     full_size_sampled(wl)
 
 
-def full_size_sampled(wl, **kw):
+def full_size_sampled(wl, n_tokens=32, **kw):
     """The layer at full size (kw: layer_buffers options) against the oracle:
-    routing and permutation in full, y and dX on sampled tokens, dW on
-    sampled experts."""
+    routing and permutation in full; for five experts (the first non-empty,
+    the median, the hottest, the smallest non-empty and the highest-index one
+    with rows) every product on sampled rows of theirs (first, last and six
+    more: ab, h, o, dab, dXp from each row's own oracle chain) and their
+    weight gradients; y and dX on n_tokens tokens (the first, the last, tokens
+    of the hottest and of the highest-index expert, the rest random)."""
     announce(f"{wl.name}: inputs")
     inp = make_inputs(wl, seed=0, device="cuda")
     announce(f"{wl.name}: layer fwd+bwd {kw}")
@@ -330,47 +334,73 @@ def full_size_sampled(wl, **kw):
     if wl.skew:
         assert (counts == 0).sum() >= 10
     tol = TOL[wl.dtype]
+    me = kw.get("memory_efficient", 0)          # h and o then hold p-scaled rows
     W = {n: inp[n] for n in ("W1", "W3", "W2")}
     shared = None
     if wl.f_shared:
         shared = tuple(to_f64(inp[n]) for n in ("Ws1", "Ws3", "Ws2"))
-    rng = np.random.default_rng(0)
-    tokens = [0, wl.T - 1] + list(rng.choice(wl.T, 2, replace=False))
     cache = {}
 
     def expert(e):
         if e not in cache:
-            if len(cache) > 12:
-                cache.clear()
+            if len(cache) >= 16:
+                cache.pop(next(iter(cache)))
             cache[e] = tuple(to_f64(W[n][e]) for n in ("W1", "W3", "W2"))
         return cache[e]
 
-    x_h = inp["x"]
-    dY_h = inp["dY"]
-    announce(f"{wl.name}: oracle on sampled tokens {tokens}")
-    for t in tokens:
-        Ws = [expert(int(e)) for e in idx[t]]
-        W1s = {int(e): w[0] for e, w in zip(idx[t], Ws)}
-        W3s = {int(e): w[1] for e, w in zip(idx[t], Ws)}
-        W2s = {int(e): w[2] for e, w in zip(idx[t], Ws)}
-        y_t, dX_t = oracle.token_fwd_bwd(to_f64(x_h[t]), to_f64(dY_h[t]), idx[t], p[t], W1s, W3s,
-                                         W2s, shared)
-        assert_close(f"y[{t}]", to_f64(b["y"][t])[None], y_t[None], tol)
-        assert_close(f"dX[{t}]", to_f64(b["dX"][t])[None], dX_t[None], tol)
-    announce(f"{wl.name}: oracle weight gradients of sampled experts")
+    x_h, dY_h = inp["x"], inp["dY"]
+    p_rows = p.reshape(-1)[np.argsort(row_of.reshape(-1))]          # probability of each row
     nonempty = np.nonzero(counts)[0]
-    for e in [int(nonempty[0]), int(nonempty[len(nonempty) // 2]), int(np.argmax(counts))]:
-        rows = slice(int(offsets[e]), int(offsets[e + 1]))
-        toks = token_of[rows]
-        pe = p.reshape(-1)[np.argsort(row_of.reshape(-1))][rows]
-        dO_e = pe[:, None] * to_f64(dY_h[torch.from_numpy(toks).cuda()])
-        dW1, dW3, dW2 = oracle.expert_wgrad(to_f64(x_h[torch.from_numpy(toks).cuda()]), dO_e,
-                                            *expert(e))
+    hot, last = int(np.argmax(counts)), int(nonempty[-1])
+    small = int(nonempty[np.argmin(counts[nonempty])])
+    if counts[wl.E - 1] > 0:
+        assert last == wl.E - 1
+    experts = list(dict.fromkeys([int(nonempty[0]), int(nonempty[len(nonempty) // 2]), hot, small,
+                                  last]))
+    rng = np.random.default_rng(0)
+    f = wl.f
+    for e in experts:
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        announce(f"{wl.name}: expert {e} ({r1 - r0} rows): sampled rows and weight gradients")
+        rows = np.array(sorted({r0, r1 - 1} | set(rng.choice(np.arange(r0, r1), min(6, r1 - r0),
+                                                              replace=False).tolist())))
+        sel = torch.from_numpy(rows).cuda()
+        toks = torch.from_numpy(token_of[rows]).cuda()
+        X = to_f64(x_h[toks])
+        dO = p_rows[rows, None] * to_f64(dY_h[toks])
+        W1, W3, W2 = expert(e)
+        a, bb, h, o = oracle.swiglu_fwd(X, W1, W3, W2)
+        dXr, _, _, _, da, db = oracle.swiglu_bwd(X, a, bb, h, dO, W1, W3, W2)
+        pr = p_rows[rows, None] if me else 1.0
+        assert_close(f"ab[{e}]", to_f64(b["ab"][sel]), np.concatenate([a, bb], 1), tol)
+        assert_close(f"h[{e}]", to_f64(b["h"][sel]), pr * h, tol)
+        assert_close(f"o[{e}]", to_f64(b["o"][sel]), pr * o, tol)
+        assert_close(f"dab[{e}]", to_f64(b["dab"][sel]), np.concatenate([da, db], 1), tol)
+        assert_close(f"dXp[{e}]", to_f64(b["dXp"][sel]), dXr, tol)
+        allr = torch.from_numpy(token_of[r0:r1]).cuda()
+        dO_e = p_rows[r0:r1, None] * to_f64(dY_h[allr])
+        dW1, dW3, dW2 = oracle.expert_wgrad(to_f64(x_h[allr]), dO_e, W1, W3, W2)
         assert_close(f"dW1[{e}]", to_f64(b["dW1"][e]), dW1, tol)
         assert_close(f"dW3[{e}]", to_f64(b["dW3"][e]), dW3, tol)
         assert_close(f"dW2[{e}]", to_f64(b["dW2"][e]), dW2, tol)
     for e in np.nonzero(counts == 0)[0][:4]:
         assert not b["dW1"][int(e)].any() and not b["dW2"][int(e)].any()
+    # tokens: first, last, some of the hottest and of the highest-index expert, random
+    picks = [0, wl.T - 1]
+    for e in (hot, last):
+        seg = token_of[int(offsets[e]):int(offsets[e + 1])]
+        picks += [int(t) for t in rng.choice(seg, min(4, len(seg)), replace=False)]
+    picks += [int(t) for t in rng.choice(wl.T, n_tokens, replace=False)]
+    tokens = list(dict.fromkeys(picks))[:max(n_tokens, 10)]
+    announce(f"{wl.name}: oracle y and dX on {len(tokens)} tokens")
+    for t in tokens:
+        Ws = {int(e): expert(int(e)) for e in idx[t]}
+        y_t, dX_t = oracle.token_fwd_bwd(to_f64(x_h[t]), to_f64(dY_h[t]), idx[t], p[t],
+                                         {e: w[0] for e, w in Ws.items()},
+                                         {e: w[1] for e, w in Ws.items()},
+                                         {e: w[2] for e, w in Ws.items()}, shared)
+        assert_close(f"y[{t}]", to_f64(b["y"][t])[None], y_t[None], tol)
+        assert_close(f"dX[{t}]", to_f64(b["dX"][t])[None], dX_t[None], tol)
 
 
 # ---------------------------------------------------------------- matrix-core probe
