@@ -78,6 +78,18 @@ __device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t o
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// A value loaded a stage ahead is complete once the stage's explicit
+// s_waitcnt vmcnt(0) has passed, but the compiler's wait insertion merges the
+// loop's entry and back edge and still counts it as pending: it then puts a
+// vmcnt(0) in front of the first use -- in the middle of the next stage's
+// MFMAs, where it also waits for that stage's freshly issued DMA loads.  Passing
+// the value through an empty asm at the top of the stage, while nothing is
+// outstanding, ends that chain.
+template <typename T>
+__device__ __forceinline__ void settle(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // MX = true: MXFP8 operands.  v_mfma_scale_f32_16x16x128_f8f6f4 takes one
 // E8M0 scale per lane and operand -- that of 32-value block (lane >> 4) of the
 // lane's row (see lds_frag for the matching fragment layout) -- so the
@@ -200,22 +212,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     sca_src = make_rsrc(as + (size_t)kb0 * Mt + ti.m0, (uint32_t)((K / BK) * Mt - ti.m0) * 4u);
     scb_src = make_rsrc(bs + (size_t)kb0 * N + ti.n0, (uint32_t)((K / BK) * N - ti.n0) * 4u);
   }
-  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+  // DMA instruction p (0 .. 2 DMA_PER_WAVE - 1) of this wavefront for stage
+  // kt: A instruction p, then B instruction p - DMA_PER_WAVE (weight
+  // gradients: the scale rows with the first).
+  auto issue_part = [&](int kt, int p) __attribute__((always_inline)) {
     const uint32_t st = lds_base + (uint32_t)((kt & (NSTAGE - 1)) * STAGE_BYTES);
     const uint32_t ka = (uint32_t)kt * BK;
     if constexpr (WGRAD) {
-      const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
-      const uint32_t sc = sc_base + (uint32_t)((kt & (NSTAGE - 1)) * 2048);
-      if (wid == 0) dma16(sca_src, (uint32_t)kt * (uint32_t)Mt * 4u + (uint32_t)lane * 16u, sc);
-      if (wid == 1) dma16(scb_src, (uint32_t)kt * (uint32_t)N * 4u + (uint32_t)lane * 16u, sc + 1024);
+      if (p == 0) {
+        const int Mt = (OP == OP_FC2_WGRAD) ? f : d;
+        const uint32_t sc = sc_base + (uint32_t)((kt & (NSTAGE - 1)) * 2048);
+        if (wid == 0) dma16(sca_src, (uint32_t)kt * (uint32_t)Mt * 4u + (uint32_t)lane * 16u, sc);
+        if (wid == 1) dma16(scb_src, (uint32_t)kt * (uint32_t)N * 4u + (uint32_t)lane * 16u, sc + 1024);
+      }
     }
-#pragma unroll
-    for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int tt = wid * DMA_PER_WAVE + t;
-      dma16(a_src, a_off[t] + ka, st + tt * 1024);
-    }
-#pragma unroll
-    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    if (p < DMA_PER_WAVE) {
+      const int tt = wid * DMA_PER_WAVE + p;
+      dma16(a_src, a_off[p] + ka, st + tt * 1024);
+    } else {
+      const int t = p - DMA_PER_WAVE;
       const int tt = wid * DMA_PER_WAVE + t;
       const uint32_t m0 = st + OPND_BYTES + tt * 1024;
       if constexpr (OP == OP_FC1_FWD) {
@@ -227,6 +242,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         dma16(b_src, b_off[t] + ka, m0);
       }
     }
+  };
+  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+    static_for<0, 2 * DMA_PER_WAVE>([&](auto P) __attribute__((always_inline)) { issue_part(kt, P.value); });
   };
 
   const int lm = lane & 15, lg = lane >> 4;
@@ -301,7 +319,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     const int sh8 = 8 * lg;
     for (int kt = 0; kt < KT; ++kt) {
       const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
-      if (kt + 1 < KT) {
+      const bool more = kt + 1 < KT;
+      if constexpr (RAGGED) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) settle(sa[i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) settle(sb[j]);
+      }
+      if (more) {
         load_scales(kt + 1, sa_n, sb_n);
         issue_stage(kt + 1);
       }
@@ -404,10 +429,30 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   wait_vmcnt<0>();
   block_barrier();
 
+  // ragged ops: the weight scales of the current and the next stage (loaded a
+  // stage ahead like the A scales, so no load of this stage waits mid-stage)
+  float wsc0 = 0.f, wsc1 = 0.f, wsc0_n = 0.f, wsc1_n = 0.f;
+  if constexpr (RAGGED) {
+    if (KT > 0) {
+      wsc0 = weight_scale(0, 0);
+      wsc1 = (OP == OP_FC1_FWD) ? weight_scale(0, 1) : wsc0;
+    }
+  }
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = lds + (kt & (NSTAGE - 1)) * STAGE_BYTES;
-    if (kt + 1 < KT) {
-      if constexpr (RAGGED) load_sa(kt + 1, sa_n);
+    const bool more = kt + 1 < KT;
+    if constexpr (RAGGED) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) settle(sa[i]);
+      settle(wsc0);
+      settle(wsc1);
+    }
+    if (more) {
+      if constexpr (RAGGED) {
+        load_sa(kt + 1, sa_n);
+        wsc0_n = weight_scale(kt + 1, 0);
+        wsc1_n = (OP == OP_FC1_FWD) ? weight_scale(kt + 1, 1) : wsc0_n;
+      }
       issue_stage(kt + 1);
     }
     if constexpr (WGRAD) {
@@ -416,11 +461,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       for (int i = 0; i < FM; ++i) sa[i] = sct[wm * WM + 16 * i + lm];
 #pragma unroll
       for (int j = 0; j < FN; ++j) sb[j] = *(const f32x4_t*)&sct[256 + wn * WN + 16 * j + 4 * lg];
-    }
-    float wsc0 = 0.f, wsc1 = 0.f;
-    if constexpr (RAGGED) {
-      wsc0 = weight_scale(kt, 0);
-      wsc1 = (OP == OP_FC1_FWD) ? weight_scale(kt, 1) : wsc0;
     }
     i32x8_t bf[FN];
     static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
@@ -466,6 +506,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     wait_vmcnt<0>();
     block_barrier();
     if constexpr (RAGGED) {
+      wsc0 = wsc0_n;
+      wsc1 = wsc1_n;
 #pragma unroll
       for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
     }
