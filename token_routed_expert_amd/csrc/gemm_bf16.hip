@@ -155,6 +155,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   constexpr int EXTRA = TR::ragged_m ? (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4
                                      : (GW ? NW * TSLOTS * 256 : 0);
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + EXTRA];
+  // the expert offsets, copied once: decoding a tile then reads LDS, whose
+  // wait (lgkmcnt) leaves the DMA loads in flight, where a global read's
+  // vmcnt(0) at the top of every tile drained the prefetched stages and the
+  // previous tile's epilogue stores
+  __shared__ int offs[257];
   int* const sched = (int*)(lds + NS * STAGE_BYTES);
   int* const mt_incl = sched + NW;
   float* const dp_red = (float*)(mt_incl + 64 * NW);
@@ -171,21 +176,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   const int Kfix = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
   const int Mfix = (OP == OP_FC2_WGRAD) ? f : d;
   int total;
-  if constexpr (TR::ragged_m) total = mtile_prefix<BM, NW>(args.offsets, args.E, mt_incl, sched) * NT;
+  for (int i = tid; i <= args.E; i += NW * 64) offs[i] = args.offsets[i];
+  __syncthreads();
+  if constexpr (TR::ragged_m) total = mtile_prefix<BM, NW>(offs, args.E, mt_incl, sched) * NT;
   else total = args.E * MT * NT;
   total = uniform(total);
   auto decode = [&](int slot, TileInfo& ti) __attribute__((always_inline)) {
     const int logical = xcd_remap(slot, total);
     if constexpr (TR::ragged_m) {
-      ragged_tile(args.offsets, mt_incl, args.E, NT, BM, logical, ti);
+      ragged_tile(offs, mt_incl, args.E, NT, BM, logical, ti);
       ti.n0 *= BN;
     } else {
       ti.e = logical / (MT * NT);
       const int rem = logical % (MT * NT);
       ti.m0 = (rem / NT) * BM;
       ti.n0 = (rem % NT) * BN;
-      ti.row0 = args.offsets[ti.e];
-      ti.rows = args.offsets[ti.e + 1] - ti.row0;
+      ti.row0 = offs[ti.e];
+      ti.rows = offs[ti.e + 1] - ti.row0;
     }
     ti.e = uniform(ti.e);
     ti.row0 = uniform(ti.row0);
