@@ -150,7 +150,12 @@ __device__ __forceinline__ void pair_f32(f32x4_t& x, f32x4_t& y) {
 // in order, then xor shuffles over the 4 lanes of a row, then the WAVES_N
 // wavefronts of a row in order through `red`, [WAVES_N][256] floats of LDS;
 // every wavefront of the block must call store_tile).
-template <int OP, int FM, int FN, int WM, int WN, bool RAGGED, bool RS = false>
+//
+// LINES (plain-store products, FN == 4: a wavefront covers 64 columns, one
+// 128-byte line of a bf16 row): lanes l and l + 8 of each row of 16 lanes
+// trade pair halves (one DPP rotate per dword), so that each store
+// instruction writes whole lines of 8 rows instead of half lines of 16 rows.
+template <int OP, int FM, int FN, int WM, int WN, bool RAGGED, bool RS = false, bool LINES = false>
 __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (&acc)[FM][FN],
                                            const TileInfo& ti, int M, int N, int wm, int wn,
                                            int lane, float* red = nullptr) {
@@ -194,6 +199,43 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const f32x4_t (
           *(u32x4_t*)(ab + fcol) = av;
           *(u32x4_t*)(ab + f + fcol) = bv;
           *(u32x4_t*)((bf16_t*)args.h_out + row * (size_t)f + fcol) = hv;
+        }
+      });
+    } else if constexpr (LINES) {
+      static_assert(FN == 4 && !RS && OP != OP_FC2_DGRAD, "whole-line stores: plain products, 64 columns");
+      // lane l < 8 keeps pair 0 (columns 0..31) of row l and receives pair 0
+      // of row l + 8; lane l >= 8 keeps pair 1 (columns 32..63) of row l and
+      // receives pair 1 of row l - 8.  Instruction H then writes rows 8H..8H+7.
+      const bool hi = lm >= 8;
+      const u32x4_t v0 = pair_bf16(acc[i][0], acc[i][1]);
+      const u32x4_t v1 = pair_bf16(acc[i][2], acc[i][3]);
+      u32x4_t w0, w1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t snd = hi ? v0[q] : v1[q];
+        // row_ror:8 inside each row of 16 lanes: lane l reads lane l ^ 8
+        const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xF, 0xF, false);
+        w0[q] = hi ? rcv : v0[q];
+        w1[q] = hi ? v1[q] : rcv;
+      }
+      const int colp = ti.n0 + wn * WN + (hi ? 32 : 0);  // first column of the lane's pair
+      const int col = colp + pc;
+      static_for<0, 2>([&](auto H) __attribute__((always_inline)) {
+        const int mh = wm * WM + i * 16 + 8 * H.value + (lm & 7);  // row within the tile
+        const bool ok = (RAGGED ? (mh < ti.rows) : (ti.m0 + mh < M)) && colp < N;
+        if (ok) {
+          bf16_t* out;
+          if constexpr (OP == OP_FC2_FWD || OP == OP_FC1_DGRAD) {
+            out = (bf16_t*)(OP == OP_FC2_FWD ? args.o_out : args.dXp_out) +
+                  (size_t)(ti.row0 + mh) * d + col;
+          } else if constexpr (OP == OP_FC2_WGRAD) {
+            out = (bf16_t*)args.dW2 + e * (size_t)f * d + (size_t)(ti.m0 + mh) * d + col;
+          } else {  // OP_FC1_WGRAD: each 32-column pair lies wholly in dW1 or in dW3
+            const bool first = colp < f;
+            out = (bf16_t*)(first ? args.dW1 : args.dW3) + e * (size_t)d * f +
+                  (size_t)(ti.m0 + mh) * f + (first ? col : col - f);
+          }
+          *(u32x4_t*)out = H.value == 0 ? w0 : w1;
         }
       });
     } else {
