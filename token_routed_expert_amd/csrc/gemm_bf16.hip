@@ -133,10 +133,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   constexpr int FM = WM / 16, FN = WN / 16;      // 16x16 MFMA blocks per wavefront
   constexpr int HB = FN / 2;                     // B fragments per half stage
   constexpr int DMA_PER_WAVE = DMA_PER_OPND / NW;  // per operand per stage
-  constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE;
+  using TR = OpTraits<OP>;
+  // ragged-M products (ungathered): the first row of wavefronts (wid < NW/2)
+  // issues its own DMA instructions and those of wavefront wid + NW/2, whose
+  // rows lie 128 further on (or, fc2 forward's MN-contiguous weights, whose
+  // columns do), and the second row issues none.  The second row is the one
+  // the first waits for at every barrier (it loses the SIMD's issue
+  // arbitration to the older wavefront), so moving its DMA issue to the first
+  // row shortens the stage (measured on the Qwen3 shape: fc2 forward and fc2
+  // dgrad 6-7 % faster; the weight gradients, whose first row has less slack,
+  // 4 % slower, so they keep one share per wavefront).
+  constexpr int DW = (TR::ragged_m && !GATHER) ? 2 : 1;
+  constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE * DW;  // of an issuing wavefront
   constexpr int DMA_STEP = 4 / DMA_PER_WAVE;       // MFMA steps per DMA instruction
   static_assert(FM == 8 && HB * 2 == FN && DMA_STEP * DMA_PER_WAVE == 4, "tile shape");
-  using TR = OpTraits<OP>;
   // LDS ring depth (measured on the Qwen3 shape: 3 stages cost 10-30 % on
   // every product, 5 stages, possible for the weight gradients only, made
   // them 5-10 % slower)
@@ -208,6 +218,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   struct Opnd {
     rsrc_t a_src, b_src, b_src2;
     uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
+    uint32_t a_dw, b_dw;  // DW = 2: offset of wavefront wid + NW/2's instruction from this one's
     int KT;
     int row0, rows;  // the tile's permuted rows (gathered operands)
   };
@@ -274,6 +285,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     }
     const int K = TR::ragged_m ? Kfix : ti.rows;
     o.KT = uniform((K + BK - 1) / BK);
+    // instruction t + 8 (NW = 8): K-contiguous rows 128 further on (the same
+    // chunk swizzle, which depends on row bits 1-2 only); fc1 forward's
+    // weights: the same offset in W3; fc2 forward's MN-contiguous weights:
+    // the next 128 columns, as clamped for a last, partial N-tile
+    o.a_dw = 0;
+    o.b_dw = 0;
+    if constexpr (DW == 2) {
+      static_assert(TR::a_kcontig, "ragged-M A operands are K-contiguous");
+      o.a_dw = 128u * a_ld;
+      if constexpr (TR::b_kcontig) o.b_dw = 128u * b_ld;
+      else if constexpr (OP == OP_FC2_FWD)
+        o.b_dw = (uint32_t)(min(ti.n0 + 128, N - 128) - min(ti.n0, N - 128)) * 2u;
+      o.a_dw = (uint32_t)uniform((int)o.a_dw);
+      o.b_dw = (uint32_t)uniform((int)o.b_dw);
+    }
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) {
       const int t = wid * DMA_PER_WAVE + q;
@@ -356,6 +382,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
   // for stage s of the stream, counted from the current tile's stage 0
   // TAIL = false: the caller knows that s is a stage of the current tile.
   auto issue_one = [&](int s, auto Q, auto TAIL) __attribute__((always_inline)) {
+    if constexpr (DW == 2) {
+      if (wid >= NW / 2) return;
+    }
     constexpr int q = decltype(Q)::value;
     const uint32_t st_base = lds_base + (uint32_t)(((uint32_t)(phase + s) % NS) * STAGE_BYTES);
     const bool in_cur = !decltype(TAIL)::value || s < cur.KT;
@@ -372,32 +401,39 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
         const uint32_t off = in_cur ? cur.a_off[q] : nxt.a_off[q];
         const uint32_t ka = TR::a_kcontig ? (uint32_t)k0 * 2u : (uint32_t)k0 * a_ld;
         dma16(r, off + ka, st_base + (uint32_t)(t * 1024));
+        if constexpr (DW == 2)
+          dma16(r, off + ka + (in_cur ? cur.a_dw : nxt.a_dw),
+                st_base + (uint32_t)((t + (NW / 2) * DMA_PER_WAVE) * 1024));
       }
     } else {
       const int qq = q - DMA_PER_WAVE;
-      const int t = wid * DMA_PER_WAVE + qq;
-      const uint32_t dst = st_base + (uint32_t)(OPND_BYTES + t * 1024);
       const uint32_t off = in_cur ? cur.b_off[qq] : nxt.b_off[qq];
-      rsrc_t r;
-      uint32_t voff;
-      if constexpr (OP == OP_FC1_DGRAD) {
-        // K = [da | db]: the first f columns multiply W1, the rest W3
-        const bool first = k0 < f;
-        r = pick(in_cur, pick(first, cur.b_src, cur.b_src2), pick(first, nxt.b_src, nxt.b_src2));
-        voff = off + (uint32_t)(first ? k0 : k0 - f) * 2u;
-      } else if constexpr (OP == OP_FC1_FWD) {
-        const bool second = (t >> 3) != 0;
-        r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
-        voff = off + (uint32_t)k0 * b_ld;
-      } else if constexpr (TR::b_kcontig) {
-        r = pick(in_cur, cur.b_src, nxt.b_src);
-        voff = off + (uint32_t)k0 * 2u;
-      } else {
-        r = pick(in_cur, cur.b_src, nxt.b_src);
-        voff = off + (uint32_t)k0 * b_ld;
-      }
-      r[2] = live ? r[2] : 0;
-      dma16(uniform_rsrc(r), voff, dst);
+      // instruction t of the B operand (DW = 2: t + 8 with the offset moved by b_dw)
+      auto one = [&](int t, uint32_t dw) __attribute__((always_inline)) {
+        const uint32_t dst = st_base + (uint32_t)(OPND_BYTES + t * 1024);
+        rsrc_t r;
+        uint32_t voff;
+        if constexpr (OP == OP_FC1_DGRAD) {
+          // K = [da | db]: the first f columns multiply W1, the rest W3
+          const bool first = k0 < f;
+          r = pick(in_cur, pick(first, cur.b_src, cur.b_src2), pick(first, nxt.b_src, nxt.b_src2));
+          voff = off + dw + (uint32_t)(first ? k0 : k0 - f) * 2u;
+        } else if constexpr (OP == OP_FC1_FWD) {
+          const bool second = (t >> 3) != 0;
+          r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
+          voff = off + dw + (uint32_t)k0 * b_ld;
+        } else if constexpr (TR::b_kcontig) {
+          r = pick(in_cur, cur.b_src, nxt.b_src);
+          voff = off + dw + (uint32_t)k0 * 2u;
+        } else {
+          r = pick(in_cur, cur.b_src, nxt.b_src);
+          voff = off + dw + (uint32_t)k0 * b_ld;
+        }
+        r[2] = live ? r[2] : 0;
+        dma16(uniform_rsrc(r), voff, dst);
+      };
+      one(wid * DMA_PER_WAVE + qq, 0u);
+      if constexpr (DW == 2) one((wid + NW / 2) * DMA_PER_WAVE + qq, in_cur ? cur.b_dw : nxt.b_dw);
     }
   };
 
@@ -556,7 +592,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
       });
       if constexpr (GW) gather_offsets(LOOK - 1, read_tok(LOOK - 1));
       static_for<0, DMA_PER_WAVE>([&](auto Q) __attribute__((always_inline)) { issue_one(LOOK - 1, Q, IntC<1>{}); });
-      wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE>();
+      wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE * DW>();
       block_barrier();
     }
     // (entered from the previous tile's stream, stage 0 has landed and passed
@@ -593,7 +629,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs args, in
     // whole-line stores where they do not raise register use past the
     // budget (fc1 dgrad's would spill); measured on the Qwen3 shape: fc1 and
     // fc2 weight gradients 3-4 % faster, fc2 forward 1.6 %
-    constexpr bool kLines = OP == OP_FC2_FWD || OP == OP_FC2_WGRAD || OP == OP_FC1_WGRAD;
+    constexpr bool kLines = FN == 4 && (OP == OP_FC2_FWD || OP == OP_FC2_WGRAD || OP == OP_FC1_WGRAD);
     store_tile<OP, FM, FN, WM, WN, TR::ragged_m, RS, kLines>(args, acc, ti, TR::ragged_m ? ti.rows : Mfix,
                                                                N, wm, wn, lane, dp_red);
     if (!have_next) break;
