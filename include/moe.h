@@ -14,7 +14,9 @@
  *  - All tensor pointers are DEVICE pointers, owned by the caller, row-major,
  *    16-byte aligned, and not aliased with each other unless stated.  The
  *    library never allocates or frees memory and keeps no state between
- *    calls; scratch space is the caller's `ws` buffer of `ws_bytes` bytes
+ *    calls, apart from the device array of moe_permute_noalloc (a fixed
+ *    1 MiB per GPU, see there) and a per-device cache of the compute-unit
+ *    count; scratch space is the caller's `ws` buffer of `ws_bytes` bytes
  *    (size from moe_workspace_bytes).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work on it and return: no host synchronisation, no copy of
