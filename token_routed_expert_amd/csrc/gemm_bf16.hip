@@ -724,6 +724,8 @@ int launch(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int gemm_persistent_blocks() { return persistent_blocks(); }
+
 #ifndef GEMM_NW
 #define GEMM_NW 8
 #endif

@@ -123,6 +123,9 @@ int gemm_f32_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // the same products with MXFP8 operands (hardware block-scaled MFMA)
 int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
+// Compute units of the current device rounded down to a multiple of 8 (the
+// grid of the persistent grouped-GEMM launches), or -1.
+int gemm_persistent_blocks();
 
 // quant.hip: e4m3 block quantisers
 int quant_rows_launch(const void* src, bool src_f32, int64_t rows, int64_t cols, uint8_t* codes,
