@@ -57,11 +57,13 @@ def np32bits(a):
 def edge_blocks(rows, cols, rng):
     """fp32 [rows][cols] whose 128-blocks include: all +0, all -0, exact
     rounding ties (block max 448 * 2^s, so scale = 2^s), the subnormal range
-    of the codes, values that saturate after the scale division, and plain
-    normals over a wide exponent range."""
+    of the codes, values that saturate after the scale division, blocks so
+    small that their scale lies below 2^-90 (some of them with subnormal
+    values or a subnormal scale), and plain normals over a wide exponent
+    range."""
     X = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-20, 20, (rows, 1)))
     nb = cols // 128
-    kinds = rng.integers(0, 6, size=(rows, nb))
+    kinds = rng.integers(0, 7, size=(rows, nb))
     for r in range(rows):
         for b in range(nb):
             blk = X[r, 128 * b:128 * (b + 1)]
@@ -85,6 +87,9 @@ def edge_blocks(rows, cols, rng):
             elif k == 4:   # a single non-zero value
                 blk[:] = 0.0
                 blk[rng.integers(0, 128)] = rng.standard_normal() * s
+            elif k == 5:   # tiny block: scale 2^-104 .. 2^-130, a few subnormal values
+                blk[:] = rng.standard_normal(128) * np.exp2(rng.integers(-122, -95))
+                blk[rng.integers(0, 128, 8)] *= 2.0 ** -20
     return X
 
 
@@ -112,6 +117,7 @@ def test_quantize_weights_bit_exact():
     W[1, :128, :128] = 0.0           # zero tile
     W[1, 128:, :128] = -0.0          # negative-zero tile
     W[2, :128, 128:256] = edge_blocks(128, 128, rng).astype(np.float32)
+    W[0, 128:, 256:] = rng.standard_normal((128, 128)) * 2.0 ** -110   # scale below 2^-90
     Wt = torch.from_numpy(W).cuda()
     codes = torch.empty(E, R, C, dtype=torch.uint8, device="cuda")
     codes_t = torch.empty(E, C, R, dtype=torch.uint8, device="cuda")
@@ -130,12 +136,16 @@ def test_quantize_token_blocks_bit_exact(gather):
     m = np.array([300, 0, 128, 77, 1, 256, 0, 129])
     off = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
     E, P, C = len(m), int(off[-1]), 384
+    # expert 5 reads only rows scaled by 2^-112: its blocks' scales lie below 2^-90
     if gather:
         T = 500
         src_np = edge_blocks(T, C, rng)
-        src_row = rng.integers(0, T, P).astype(np.int32)
+        src_np[:50] *= 2.0 ** -112
+        src_row = rng.integers(50, T, P).astype(np.int32)
+        src_row[off[5]:off[6]] = rng.integers(0, 50, m[5])
     else:
         src_np = edge_blocks(P, C, rng)
+        src_np[off[5]:off[6]] *= 2.0 ** -112
         src_row = None
     src = torch.from_numpy(src_np.astype(np.float32)).to(torch.bfloat16)
     cap = tre.moe_token_block_capacity(P, E)
