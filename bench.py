@@ -45,17 +45,18 @@ def log(*a):
 
 
 # The source file of each dtype's grouped-GEMM kernels.
-GEMM_SOURCE = {"bf16": "gemm_bf16.hip", "f32": "gemm_f32.hip", "e4m3": "gemm_fp8.hip",
-               "mxfp8": "gemm_fp8.hip"}
+GEMM_SOURCE = {"bf16": ["gemm_bf16.hip"], "f32": ["gemm_f32.hip"],
+               "e4m3": ["gemm_fp8.hip", "gemm_fp8_wgrad.hip"],
+               "mxfp8": ["gemm_fp8.hip", "gemm_fp8_wgrad.hip"]}
 
 
 def kernel_sources_sha256(dtype: str) -> str:
-    """Hash of the grouped-GEMM kernel source of `dtype` and of every header of
+    """Hash of the grouped-GEMM kernel sources of `dtype` and of every header of
     the library: a traffic record taken from hardware counters is valid only
     for the kernel sources it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_routed_expert_amd", "csrc")
-    for path in sorted([os.path.join(csrc, GEMM_SOURCE[dtype])] +
+    for path in sorted([os.path.join(csrc, n) for n in GEMM_SOURCE[dtype]] +
                        glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as fh:

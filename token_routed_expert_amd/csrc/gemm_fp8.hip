@@ -1,37 +1,56 @@
-// Grouped expert GEMMs with e4m3 operands and fp32 block scales on CDNA4
-// matrix cores, fp32 accumulation, bf16 outputs.
+// Grouped expert GEMMs with 8-bit float operands on CDNA4 matrix cores, fp32
+// accumulation, bf16 outputs: e4m3 codes with fp32 block scales, and MXFP8
+// (e4m3 codes with one power-of-two E8M0 scale per 32 values).
 //
 // The pages run the expert GEMMs in FP8 with blockwise scaling (German
 // technical summary of "Scalable Training of Mixture-of-Experts Models with
-// Megatron Core", section 2 E; French summary, section 2 E); the block shapes
-// are 1 x 128 along the contraction for activations, 128 x 128 for weights,
-// and 128 tokens per column for the operands of the weight gradients.  Every
-// scale block spans exactly 128 values of the contraction axis, which is the
-// K of one v_mfma_f32_16x16x128_f8f6f4: each MFMA yields the exact partial
-// product of one scale block, and the lane adds it to its fp32 accumulator
-// times the two block scales (scale promotion per 128-K block).
+// Megatron Core", section 2 E; French summary, section 2 E); the e4m3 block
+// shapes are 1 x 128 along the contraction for activations, 128 x 128 for
+// weights, and 128 tokens per column for the operands of the weight
+// gradients, so every scale block spans 128 values of the contraction axis.
 //
-// All six products read both operands with the contraction axis contiguous
-// (C[m][n] = sum_k A[m][k] B[n][k]): the weight quantiser stores transposed
-// codes for the forward products and the token-block quantiser stores the
-// weight-gradient operands transposed, so one LDS layout serves every op:
+// This file holds the four products with ragged M (an expert's permuted rows);
+// the weight gradients, whose K is an expert's few token blocks, have a kernel
+// of their own (gemm_fp8_wgrad.hip).  Both operands are read with the
+// contraction axis contiguous (C[m][n] = sum_k A[m][k] B[n][k]); the weight
+// quantiser stores the transposed codes the forward products need:
 //
 //   op          A (rows x K)                 B (rows x K)               K
 //   FC1_FWD     xp codes [P][d]              W1^T, W3^T codes [f][d]    d
 //   FC2_FWD     h codes  [P][f]              W2^T codes [d][f]          f
 //   FC2_DGRAD   dO codes [P][d]              W2 codes [f][d]            d
 //   FC1_DGRAD   dab codes [P][2f]            W1 | W3 codes [d][f]       2f
-//   FC2_WGRAD   h^T token blocks [f][.]      dO^T token blocks [d][.]   128 * blocks
-//   FC1_WGRAD   xp^T token blocks [d][.]     dab^T token blocks [2f][.] of the expert
 //
-// Tiles, schedule and epilogues are those of the bf16 kernels (256 x 256
-// block tile, 8 wavefronts of 128 x 64, device-side ragged-M schedule, fused
-// SwiGLU forward / backward epilogues, bf16 stores).  K advances 128 per
-// stage through a 2-deep LDS ring (64 KB per stage) filled by buffer_load ...
-// lds; a K-contiguous LDS row is 128 bytes (8 chunks of 16) with chunk c of
-// row r stored at c ^ ((r >> 1) & 7).  A fragment (32 K bytes of one row per
-// lane: chunks g and g + 4 for lane group g) is two ds_read_b128, free of
-// bank conflicts (measured).
+// Pipeline: that of the bf16 kernels -- 256 x 256 block tile, 8 wavefronts of
+// 128 x 64, persistent blocks walking the XCD-remapped device-side tile list
+// with the next tile's first stages streamed under the current one's last,
+// fused SwiGLU forward / backward epilogues -- with K advancing 64 codes per
+// stage through a 4-deep LDS ring (32 KB of codes per stage: 256 rows of 64
+// bytes per operand), every operand byte moved by buffer_load ... lds issued
+// up to three stages ahead.  The products are v_mfma_scale_f32_32x32x64_f8f6f4
+// (a wavefront covers its 128 x 64 sub-tile with 4 x 2 blocks of 32 x 32).
+// The 64-deep MFMA is what allows the 32 KB stage and so the 4-deep ring: the
+// 128-deep 16x16x128 form needs 64 KB per stage, two stages in the LDS.
+//
+// MFMA operand layout (measured with a probe): lane l supplies row l & 31 of
+// its operand; lane group h = l >> 5 holds K values [16 h, 16 h + 16) in bytes
+// 0..15 and [32 + 16 h, 32 + 16 h + 16) in bytes 16..31; the E8M0 scale of
+// 32-value block b of a row comes from lane group b.  Results: lane l holds
+// D[8 q + 4 h + r][l & 31] in accumulator 4 q + r.  The kernel computes
+// D = C^T (B rows as the MFMA's rows), so a lane's 16 results are 16 output
+// columns of one output row.
+//
+// Scales.  With each stage's codes come its scale words, 2 KB per stage: one
+// 32-bit word per A row and per B row (e4m3: the fp32 scale of the row's
+// 128-K block; MXFP8: the four E8M0 bytes of that block).  MXFP8 bytes go
+// straight into the MFMA.  An e4m3 scale s = 2^e * m (m in [1, 2)) is split:
+// the MFMA applies 2^e of the A row and of the B row as E8M0 scales, and the
+// accumulators are kept in units of the current block's mantissas,
+// u = m_A * m_B (all rows of a 128-row weight block share m_B): at the first
+// stage of each 128-K block they are multiplied by u_old / u_new (in
+// (1/4, 4)), and at the end of the tile by the last u.  That is one
+// multiplication per accumulator per 128-K block, as a promotion of per-block
+// partial products would take, without their registers.
 #include "gemm_common.h"
 
 namespace tre {
@@ -39,590 +58,572 @@ namespace tre {
 namespace {
 using namespace gemm;
 
-constexpr int BM = 256, BN = 256, BK = 128, NSTAGE = 2, NW = 8;
-constexpr int OPND_BYTES = 256 * BK;            // 32 KB of codes per operand and stage
-constexpr int STAGE_BYTES = 2 * OPND_BYTES;     // A then B
-constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 32 one-KB DMA instructions
-constexpr int DMA_PER_WAVE = DMA_PER_OPND / NW;  // 4 per operand and stage
+constexpr int BM = 256, BN = 256, BK = 64, NW = 8;
+constexpr int OPND_BYTES = 256 * BK;             // 16 KB of codes per operand and stage
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // A then B
+constexpr int SC_BYTES = 2048;                   // per stage: 256 A-row then 256 B-row words
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024;  // 16 one-KB DMA instructions
+constexpr int DMA_PER_WAVE = DMA_PER_OPND / NW;  // 2 per operand and stage
+constexpr int NS = 4;                            // LDS ring depth
+constexpr int LOOK = NS - 1;                     // stage kt + LOOK is issued during stage kt
+// vector-memory loads a wavefront issues per stage: A, B, one scale DMA
+constexpr int LOADS_PER_STAGE = 2 * DMA_PER_WAVE + 1;
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// Chunk swizzle of the 64-byte LDS rows: 16-byte chunk c of row r is stored
+// at chunk c ^ swz(r).  A fragment read (ds_read_b128) takes chunk h (then
+// h + 2) of rows 0..31 of a block in lane group h, so each 16 lanes read 16
+// rows of one chunk; with swz(r) = (r >> 2) & 3 those cover the 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-// The scaled MFMA's operand layout (measured): lane group g = lane >> 4 holds
-// K values [16 g, 16 g + 16) in its bytes 0..15 and [64 + 16 g, 64 + 16 g + 16)
-// in bytes 16..31, and the scale of 32-value block g of the row comes from
-// lane group g.  So a fragment takes 16-byte chunks g and g + 4 of the
-// 128-byte K row.  The e4m3 path (one 128-value scale block per MFMA) could
-// take any K order that A and B share; it takes the same one, which is free
-// of LDS bank conflicts, where chunks 2g and 2g + 1 made half of the LDS
-// cycles conflict cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.5).
-__device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int g, int sw) {
-  const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((g ^ sw) << 4));
+__device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int h, int sw) {
+  const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(row_base + ((h ^ sw) << 4));
   const i32x4_t hi =
-      *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((g + 4) ^ sw) << 4));
+      *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((h + 2) ^ sw) << 4));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& b, const i32x8_t& a) {
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, z, 0, 0, 0, 0, 0, 0);
+// e4m3 x e4m3 32x32x64 block product into c; sa scales the MFMA's rows (the
+// B operand), sb its columns (the A operand), both E8M0.
+template <int SEL_A = 0, int SEL_B = 0>
+__device__ __forceinline__ f32x16_t mma(const i32x8_t& b, const i32x8_t& a, const f32x16_t& c, int sa,
+                                        int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, SEL_A, sa, SEL_B, sb);
 }
 
-__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+// fp32 scale -> (E8M0 exponent byte, mantissa): s = m * 2^(e8 - 127) with m in
+// [1, 2) for normal s; subnormal s gives e8 = 0 and m = s * 2^127 (< 1); s = 0
+// (rows past the data) gives m = 0.
+__device__ __forceinline__ int e8_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
+__device__ __forceinline__ float mant_of(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u >> 23) ? __uint_as_float((u & 0x007fffffu) | 0x3f800000u) : s * 0x1p127f;
 }
 
-__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+// v_permlane32_swap on two registers: x keeps lanes 0-31 and takes y's lanes
+// 0-31 into its lanes 32-63; y receives x's lanes 32-63 into its lanes 0-31.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16f(float& x, float& y) {
+  uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+  swap16(a, b);
+  x = __uint_as_float(a);
+  y = __uint_as_float(b);
 }
 
-// A value loaded a stage ahead is complete once the stage's explicit
-// s_waitcnt vmcnt(0) has passed, but the compiler's wait insertion merges the
-// loop's entry and back edge and still counts it as pending: it then puts a
-// vmcnt(0) in front of the first use -- in the middle of the next stage's
-// MFMAs, where it also waits for that stage's freshly issued DMA loads.  Passing
-// the value through an empty asm at the top of the stage, while nothing is
-// outstanding, ends that chain.
-template <typename T>
-__device__ __forceinline__ void settle(T& v) {
-  asm volatile("" : "+v"(v));
+// One 32 x 32 block of D = C^T (lane l: C[l & 31][8 q + 4 (l >> 5) + r] in
+// c[4 q + r]) -> the four 16 x 16 fragments the bf16 epilogue takes
+// (fragment (i, j): lane l holds C[16 i + (l & 15)][16 j + 4 (l >> 4) + r]).
+// The value for lane l' = (b5, b4, low) of fragment (i, j) sits in lane
+// (b4, i, low), accumulator 4 (2 j + b5) + r: one exchange across lane bit 5
+// (accumulator groups 2 j and 2 j + 1), then one across lane bit 4.
+__device__ __forceinline__ void to_frags(f32x16_t c, f32x4_t& f00, f32x4_t& f01, f32x4_t& f10,
+                                         f32x4_t& f11) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = c[4 * (2 * j) + r], y = c[4 * (2 * j + 1) + r];
+      swap32(x, y);  // x: from lane bit 5 = 0, y: from bit 5 = 1
+      swap16f(x, y);  // x: fragment row 0, y: fragment row 1
+      if (j == 0) {
+        f00[r] = x;
+        f10[r] = y;
+      } else {
+        f01[r] = x;
+        f11[r] = y;
+      }
+    }
 }
 
-// MX = true: MXFP8 operands.  v_mfma_scale_f32_16x16x128_f8f6f4 takes one
-// E8M0 scale per lane and operand -- that of 32-value block (lane >> 4) of the
-// lane's row (see lds_frag for the matching fragment layout) -- so the
-// scales go straight into the MFMA, which accumulates in place: no promotion.
-// A lane's scale byte for fragment row r and stage kt is byte (lane >> 4) of
-// the word at r * ld + 4 kt.
-// RS: row-scaled epilogues (probabilities applied before W2; fc1 forward and
-// fc2 dgrad only), as in the bf16 kernels.
+__device__ __forceinline__ int bits_u32(float v) { return (int)__float_as_uint(v); }
+
+// MX = true: MXFP8 operands.  RS: row-scaled epilogues (probabilities applied
+// before W2; fc1 forward and fc2 dgrad only), as in the bf16 kernels.
 //
-// Tiles are numbered and XCD-remapped as in the bf16 kernels.  PER = false:
-// one block per tile.  PER = true (persistent, one block per compute unit):
-// a block takes tiles slot = blockIdx.x, blockIdx.x + gridDim.x, ... as one
-// stream through the 2-deep ring: the last stage of a tile loads the next
-// tile's first stage (codes and scales) into the free slot, so a tile starts
-// without waiting for its first loads.
-// Only buffer resources and scalars change from tile to tile (every DMA lane
-// offset is relative to the tile): the next tile is kept as its decoded
-// indices, and its resources are built where its first stage is issued.
-template <int OP, bool MX, bool RS, bool PER>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
+// Persistent: a block takes tiles slot = blockIdx.x, blockIdx.x + gridDim.x,
+// ... (launched with one block per compute unit, a multiple of 8; fc2 dgrad,
+// whose epilogue reads a|b and would wait behind the next tile's loads, is
+// launched with one block per tile).  The loads the pipeline issues past a
+// tile's last stage fetch the first three stages of the next tile.
+template <int OP, bool MX, bool RS>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
-  constexpr int FM = WM / 16, FN = WN / 16;      // 8 x 4 MFMA blocks
-  constexpr bool RAGGED = OP <= OP_FC1_DGRAD;
-  constexpr bool WGRAD = !RAGGED;
+  constexpr int IB = WM / 32, JB = WN / 32;      // 4 x 2 blocks of 32 x 32
+  static_assert(OP <= OP_FC1_DGRAD, "ragged-M products only");
+  constexpr int DMA_STEP = 4 / DMA_PER_WAVE;     // MFMA steps per DMA instruction
+  static_assert(IB == 4 && JB == 2 && DMA_STEP == 2, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
-  // weight-gradient products: per stage the 256 A-row and 256 B-column scales
-  __shared__ __attribute__((aligned(1024))) float sc_lds[NSTAGE][2][256];
-  // persistent: the expert offsets (weight gradients: and the token-block
-  // table), copied once so that decoding the next tile reads LDS, not global
-  // memory (a global read would make the compiler wait for every load in
-  // flight, DMAs included)
-  __shared__ int offs[PER ? 257 : 1];
-  __shared__ int blks[PER && WGRAD ? 257 : 1];
-  __shared__ int mt_incl[PER && RAGGED ? 256 : 1];  // ragged: inclusive prefix of the experts' M-tiles
-  __shared__ int sched[NW + 4];
-  __shared__ float dp_red[RS ? (NW / 2) * 256 : 1];  // row-scaled fc2 dgrad: <h, dh'> partials
+  // the stage ring, the scale ring, then the schedule scratch, the inclusive
+  // prefix of the experts' M-tile counts and (row-scaled fc2 dgrad) the
+  // per-row <h, dh'> partials
+  constexpr int EXTRA = (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + NS * SC_BYTES + EXTRA];
+  // the expert offsets, copied once: decoding a tile then reads LDS, whose
+  // wait (lgkmcnt) leaves the DMA loads in flight
+  __shared__ int offs[257];
+  char* const sc_ring = lds + NS * STAGE_BYTES;
+  int* const sched = (int*)(lds + NS * STAGE_BYTES + NS * SC_BYTES);
+  int* const mt_incl = sched + NW;
+  float* const dp_red = (float*)(mt_incl + 64 * NW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int d = args.d, f = args.f, E = args.E;
 
   // ---------------------------------------------------------------- tiles
-  const int32_t* const offv = PER ? offs : args.offsets;
-  const int32_t* const blkv = PER ? blks : args.blk;
-  int total = 0;
-  if constexpr (PER) {
-    for (int i = tid; i <= E; i += NW * 64) {
-      offs[i] = args.offsets[i];
-      if constexpr (WGRAD) blks[i] = args.blk[i];
-    }
-    __syncthreads();
-    if constexpr (RAGGED) total = mtile_prefix<BM, NW>(offs, E, mt_incl, sched) * NT;
-    else total = E * MT * NT;
-  } else if constexpr (WGRAD) {
-    total = E * MT * NT;
-  }
-  total = uniform(total);
-  int slot = blockIdx.x;
-  if ((PER || WGRAD) && slot >= total) return;
-
-  // ragged: K fixed, M = the tile's rows; weight gradients: M, N fixed, K =
-  // the expert's token blocks (zero-padded; 0 for an empty expert)
+  // M = the tile's rows, K and N fixed
+  const int N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
   const int Kr = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
-  const int N = RAGGED ? ((OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d))
-                       : ((OP == OP_FC2_WGRAD) ? d : 2 * f);
-  const int Mw = (OP == OP_FC2_WGRAD) ? f : d;
-  const uint32_t a_ld = RAGGED ? (uint32_t)Kr : (uint32_t)args.ldt;
-  uint32_t b_ld;
-  if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) b_ld = (uint32_t)d;
-  else if constexpr (OP == OP_FC2_FWD || OP == OP_FC1_DGRAD) b_ld = (uint32_t)f;
-  else b_ld = (uint32_t)args.ldt;
-  // MXFP8 ragged products: words of scale bytes per row
-  const uint32_t xa_ld = (uint32_t)(Kr / 32);
-  const uint32_t xb_ld = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)(d / 32) : (uint32_t)(f / 32);
-
-  struct FTile {
-    TileInfo ti;
-    int K, KT, M, kb0;
-    rsrc_t a_src, b_src, b_src2;
-    rsrc_t sca_src, scb_src;              // weight gradients: the stage's scale rows
-    __amdgpu_buffer_rsrc_t sa_src;        // e4m3 ragged: the A rows' block scales
-    __amdgpu_buffer_rsrc_t xa, xb, xb2;   // MXFP8 ragged: scale words of A rows and B rows
-  };
-  // (one block per tile, ragged: the whole decode in one pass over the
-  // offsets; a block past the device-side tile count returns)
-  auto decode = [&](int s, TileInfo& ti) __attribute__((always_inline)) -> bool {
-    if constexpr (RAGGED && !PER) {
-      if (!decode_ragged_m<BM, NW>(args.offsets, E, NT, sched, ti)) return false;
-      ti.n0 *= BN;
-    } else if constexpr (RAGGED) {
-      ragged_tile(offs, mt_incl, E, NT, BM, xcd_remap(s, total), ti);
-      ti.n0 *= BN;
-    } else {
-      const int logical = xcd_remap(s, total);
-      ti.e = logical / (MT * NT);
-      const int rem = logical % (MT * NT);
-      ti.m0 = (rem / NT) * BM;
-      ti.n0 = (rem % NT) * BN;
-      ti.row0 = offv[ti.e];
-      ti.rows = offv[ti.e + 1] - ti.row0;
-    }
+  for (int i = tid; i <= E; i += NW * 64) offs[i] = args.offsets[i];
+  __syncthreads();
+  const int total = uniform(mtile_prefix<BM, NW>(offs, E, mt_incl, sched) * NT);
+  auto decode = [&](int slot, TileInfo& ti) __attribute__((always_inline)) {
+    ragged_tile(offs, mt_incl, E, NT, BM, xcd_remap(slot, total), ti);
+    ti.n0 *= BN;
     ti.e = uniform(ti.e);
     ti.row0 = uniform(ti.row0);
     ti.rows = uniform(ti.rows);
     ti.m0 = uniform(ti.m0);
     ti.n0 = uniform(ti.n0);
-    return true;
   };
-  auto setup = [&](const TileInfo& ti, FTile& t) __attribute__((always_inline)) {
-    t.ti = ti;
+
+  // ---------------------------------------------------------------- operands
+  const uint32_t a_ld = (uint32_t)Kr;
+  const uint32_t b_ld = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)d : (uint32_t)f;
+  const int kbr = Kr / 128;  // 128-K blocks per row
+
+  // Per tile: buffer resources over what the tile reads (rows past an
+  // expert's end or past the matrix read as zero), the stage count, and this
+  // wavefront's scale-word source.  Wavefront w loads scale words 64 (w & 3)
+  // .. + 63 of side w >> 2 (0: A rows, 1: B rows); word i of stage kt is at
+  // sc_off + (kt / 2) * sc_kstep in sc_src (fc1 dgrad: the W3 source sc_src2
+  // from block f / 128 on, at (kt / 2 - f / 128) * sc_kstep).
+  struct Opnd {
+    rsrc_t a_src, b_src, b_src2, sc_src, sc_src2;
+    uint32_t sc_off, sc_kstep;
+    int KT;
+  };
+  const int sside = wid >> 2, sidx = 64 * (wid & 3) + lane;
+  auto setup = [&](const TileInfo& ti, Opnd& o) __attribute__((always_inline)) {
     const size_t e = (size_t)ti.e;
-    if constexpr (RAGGED) {
-      t.K = Kr;
-      t.M = ti.rows;
-      t.kb0 = 0;
-      t.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Kr, (uint32_t)ti.rows * a_ld);
-    } else {
-      t.kb0 = uniform(blkv[ti.e]);
-      t.K = uniform((blkv[ti.e + 1] - t.kb0) * BK);
-      t.M = Mw;
-      t.a_src = make_rsrc(args.a_q + (size_t)ti.m0 * args.ldt + (size_t)t.kb0 * BK,
-                          (uint32_t)(Mw - ti.m0) * a_ld);
-    }
-    t.KT = t.K / BK;
+    o.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Kr, (uint32_t)ti.rows * a_ld);
+    o.KT = Kr / BK;
     if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
       const size_t off = e * (size_t)f * d + (size_t)(ti.n0 / 2) * d;
-      t.b_src = make_rsrc(args.b_q + off, 128u * b_ld);
-      t.b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
+      o.b_src = make_rsrc(args.b_q + off, 128u * b_ld);
+      o.b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
     } else if constexpr (OP == OP_FC2_FWD) {  // W2^T [d][f]
-      t.b_src = make_rsrc(args.b_q + e * (size_t)d * f + (size_t)ti.n0 * f, (uint32_t)(d - ti.n0) * b_ld);
-      t.b_src2 = t.b_src;
+      o.b_src = make_rsrc(args.b_q + e * (size_t)d * f + (size_t)ti.n0 * f, (uint32_t)(d - ti.n0) * b_ld);
+      o.b_src2 = o.b_src;
     } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 [f][d]
-      t.b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0 * d, (uint32_t)(f - ti.n0) * b_ld);
-      t.b_src2 = t.b_src;
-    } else if constexpr (OP == OP_FC1_DGRAD) {  // W1 | W3 [d][f], K = 2f
+      o.b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0 * d, (uint32_t)(f - ti.n0) * b_ld);
+      o.b_src2 = o.b_src;
+    } else {  // FC1_DGRAD: W1 | W3 [d][f], K = 2f
       const size_t off = e * (size_t)d * f + (size_t)ti.n0 * f;
-      t.b_src = make_rsrc(args.b_q + off, (uint32_t)(d - ti.n0) * b_ld);
-      t.b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)(d - ti.n0) * b_ld);
-    } else {  // wgrad: token-block operand [N][ldt]
-      t.b_src = make_rsrc(args.b_q + (size_t)ti.n0 * args.ldt + (size_t)t.kb0 * BK,
-                          (uint32_t)(N - ti.n0) * b_ld);
-      t.b_src2 = t.b_src;
+      o.b_src = make_rsrc(args.b_q + off, (uint32_t)(d - ti.n0) * b_ld);
+      o.b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)(d - ti.n0) * b_ld);
     }
-    if constexpr (WGRAD) {
-      // the stage's scale rows ([NB][M] and [NB][N], 256 consecutive floats
-      // each); rows past the matrix read as zero.  (MXFP8: the same 4 bytes
-      // per block and row, holding the four 32-row E8M0 scales)
-      const float* as = MX ? (const float*)args.a_sx : args.a_s;
-      const float* bs = MX ? (const float*)args.b_sx : args.b_s;
-      t.sca_src = make_rsrc(as + (size_t)t.kb0 * Mw + ti.m0, (uint32_t)(t.KT * Mw - ti.m0) * 4u);
-      t.scb_src = make_rsrc(bs + (size_t)t.kb0 * N + ti.n0, (uint32_t)(t.KT * N - ti.n0) * 4u);
-    } else if constexpr (!MX) {
-      t.sa_src = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_s + (size_t)ti.row0 * (Kr / BK)), 0,
-                                                   ti.rows * (Kr / BK) * 4, 0x00020000);
-    } else {
-      t.xa = __builtin_amdgcn_make_buffer_rsrc((void*)(args.a_sx + (size_t)ti.row0 * xa_ld), 0,
-                                               ti.rows * (int)xa_ld, 0x00020000);
+    // ---- scale words (every field set first: a zero-length resource reads nothing)
+    o.sc_src = rsrc_t{0, 0, 0, 0};
+    o.sc_src2 = rsrc_t{0, 0, 0, 0};
+    o.sc_off = 0;
+    o.sc_kstep = 0;
+    if (sside == 0) {
+      // A rows: e4m3 a_s [P][K/128] floats; MXFP8 a_sx [P][K/32] bytes
+      if constexpr (MX) {
+        o.sc_src = make_rsrc(args.a_sx + (size_t)ti.row0 * (Kr / 32), (uint32_t)ti.rows * (uint32_t)(Kr / 32));
+        o.sc_off = (uint32_t)sidx * (uint32_t)(Kr / 32);
+      } else {
+        o.sc_src = make_rsrc(args.a_s + (size_t)ti.row0 * kbr, (uint32_t)ti.rows * (uint32_t)kbr * 4u);
+        o.sc_off = (uint32_t)sidx * (uint32_t)kbr * 4u;
+      }
+      o.sc_kstep = 4u;
+    } else if constexpr (MX) {
+      // B rows: the E8M0 bytes [E][n][K/32] of the weight in the orientation read
+      const int xb = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d / 32 : f / 32;
       size_t b0;
       int brows;
       if constexpr (OP == OP_FC1_FWD) {
-        b0 = (e * f + ti.n0 / 2) * xb_ld; brows = 128;
+        b0 = (e * f + ti.n0 / 2) * xb; brows = 128;
       } else if constexpr (OP == OP_FC2_FWD) {
-        b0 = (e * d + ti.n0) * xb_ld; brows = d - ti.n0;
+        b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
       } else if constexpr (OP == OP_FC2_DGRAD) {
-        b0 = (e * f + ti.n0) * xb_ld; brows = f - ti.n0;
+        b0 = (e * f + ti.n0) * xb; brows = f - ti.n0;
       } else {
-        b0 = (e * d + ti.n0) * xb_ld; brows = d - ti.n0;
+        b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
       }
-      t.xb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_sx + b0), 0, brows * (int)xb_ld, 0x00020000);
-      t.xb2 = (OP == OP_FC1_FWD || OP == OP_FC1_DGRAD)
-                  ? __builtin_amdgcn_make_buffer_rsrc((void*)(args.b_sx2 + b0), 0, brows * (int)xb_ld,
-                                                      0x00020000)
-                  : t.xb;
+      const bool w3 = OP == OP_FC1_FWD && sidx >= 128;  // fc1 forward: B rows 128.. are W3's
+      o.sc_src = make_rsrc((w3 ? args.b_sx2 : args.b_sx) + b0, (uint32_t)brows * (uint32_t)xb);
+      if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_sx2 + b0, (uint32_t)brows * (uint32_t)xb);
+      o.sc_off = (uint32_t)((OP == OP_FC1_FWD) ? (sidx & 127) : sidx) * (uint32_t)xb;
+      o.sc_kstep = 4u;
+    } else {
+      // B rows: e4m3 weight block scales, [E][d/128][f/128] (W1, W3) or
+      // [E][f/128][d/128] (W2); every B row of a 128-row block reads the same
+      // word (rows past N read past the range: zero)
+      const int db = d / 128, fb = f / 128;
+      const int nb = db * fb;
+      const float* s = (OP == OP_FC1_FWD && sidx >= 128) ? args.b_s2 : args.b_s;
+      o.sc_src = make_rsrc(s + e * (size_t)nb, (uint32_t)nb * 4u);
+      if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_s2 + e * (size_t)nb, (uint32_t)nb * 4u);
+      if constexpr (OP == OP_FC1_FWD) {  // block (kb, f-block of the tile's W1 / W3 rows)
+        o.sc_off = (uint32_t)((ti.n0 / 2) / 128) * 4u;
+        o.sc_kstep = (uint32_t)fb * 4u;
+      } else if constexpr (OP == OP_FC2_FWD) {  // W2 block (kb, d-block of the row)
+        const int nbk = (ti.n0 + sidx) / 128;
+        o.sc_off = nbk < db ? (uint32_t)nbk * 4u : 0x40000000u;
+        o.sc_kstep = (uint32_t)db * 4u;
+      } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 block (f-block of the row, kb)
+        const int nbk = (ti.n0 + sidx) / 128;
+        o.sc_off = nbk < fb ? (uint32_t)nbk * (uint32_t)db * 4u : 0x40000000u;
+        o.sc_kstep = 4u;
+      } else {  // FC1_DGRAD: W1 / W3 block (d-block of the row, kb mod f/128)
+        const int nbk = (ti.n0 + sidx) / 128;
+        o.sc_off = nbk < db ? (uint32_t)nbk * (uint32_t)fb * 4u : 0x40000000u;
+        o.sc_kstep = 4u;
+      }
     }
+    o.sc_src = uniform_rsrc(o.sc_src);
+    o.sc_src2 = uniform_rsrc(o.sc_src2);
+    o.sc_kstep = (uint32_t)uniform((int)o.sc_kstep);
   };
 
-  // DMA: instruction tt (0..31) of an operand covers tile rows 8tt..8tt+7;
-  // lane -> row 8tt + lane/8, LDS chunk lane%8 holding K chunk (lane%8) ^ swz(row).
-  // This wavefront issues tt = wid*4 + t, t < 4, for A and for B.
+  // ---- DMA lane offsets: instruction t (0..15) of an operand covers tile
+  // rows 16 t .. 16 t + 15; lane -> row 16 t + lane / 4, stored chunk lane % 4
+  // holding logical chunk (lane % 4) ^ swz(row).  This wavefront issues
+  // t = 2 wid + q, q < 2, for A and for B.
   uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
 #pragma unroll
-  for (int t = 0; t < DMA_PER_WAVE; ++t) {
-    const int tt = wid * DMA_PER_WAVE + t;
-    const int row = 8 * tt + (lane >> 3);
-    const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
-    a_off[t] = (uint32_t)row * a_ld + ch;
+  for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    const int t = wid * DMA_PER_WAVE + q;
+    const int row = 16 * t + (lane >> 2);
+    const uint32_t ch = (uint32_t)(((lane & 3) ^ swz(row)) << 4);
+    a_off[q] = (uint32_t)row * a_ld + ch;
     const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
-    b_off[t] = (uint32_t)brow * b_ld + ch;
+    b_off[q] = (uint32_t)brow * b_ld + ch;
   }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-  const uint32_t sc_base = (uint32_t)(uintptr_t)&sc_lds[0][0][0];
-  // DMA instruction p (0 .. 2 DMA_PER_WAVE - 1) of this wavefront for stage
-  // kt of tile t into ring slot rs: A instruction p, then B instruction
-  // p - DMA_PER_WAVE (weight gradients: the scale rows with the first).
-  auto issue_part = [&](const FTile& t, int kt, int rs, int p) __attribute__((always_inline)) {
-    const uint32_t st = lds_base + (uint32_t)(rs * STAGE_BYTES);
-    const uint32_t ka = (uint32_t)kt * BK;
-    if constexpr (WGRAD) {
-      if (p == 0) {
-        const uint32_t sc = sc_base + (uint32_t)(rs * 2048);
-        if (wid == 0) dma16(t.sca_src, (uint32_t)kt * (uint32_t)Mw * 4u + (uint32_t)lane * 16u, sc);
-        if (wid == 1) dma16(t.scb_src, (uint32_t)kt * (uint32_t)N * 4u + (uint32_t)lane * 16u, sc + 1024);
-      }
-    }
-    if (p < DMA_PER_WAVE) {
-      const int tt = wid * DMA_PER_WAVE + p;
-      dma16(t.a_src, a_off[p] + ka, st + tt * 1024);
-    } else {
-      const int q = p - DMA_PER_WAVE;
-      const int tt = wid * DMA_PER_WAVE + q;
-      const uint32_t m0 = st + OPND_BYTES + tt * 1024;
-      if constexpr (OP == OP_FC1_FWD) {
-        dma16(tt < 16 ? t.b_src : t.b_src2, b_off[q] + ka, m0);
-      } else if constexpr (OP == OP_FC1_DGRAD) {
-        const bool second = (int)ka >= f;
-        dma16(second ? t.b_src2 : t.b_src, b_off[q] + (second ? ka - (uint32_t)f : ka), m0);
+  const uint32_t lds_base =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)LDS_PTR(lds));
+  const uint32_t sc_base = lds_base + (uint32_t)(NS * STAGE_BYTES) + (uint32_t)(sside * 1024 + (wid & 3) * 256);
+
+  TileInfo ti, tn;
+  Opnd cur, nxt;
+  int slot = blockIdx.x;
+  if (slot >= total) return;
+  decode(slot, ti);
+  setup(ti, cur);
+  tn = ti;
+  nxt = cur;
+  int phase = 0;       // ring slot of the current tile's stage 0
+  bool cross = false;  // stages past the current tile's last fetch the next tile's first three
+
+  // DMA instruction Q of this wavefront for stage s of the stream, counted
+  // from the current tile's stage 0: Q < 2 A, Q == 2 the scale words, Q > 2 B.
+  // TAIL = false: the caller knows that s is a stage of the current tile.
+  auto issue_one = [&](int s, auto Q, auto TAIL) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value;
+    const uint32_t slot_s = (uint32_t)(phase + s) % NS;
+    const uint32_t st_base = lds_base + slot_s * STAGE_BYTES;
+    const bool in_cur = !decltype(TAIL)::value || s < cur.KT;
+    const int kt = in_cur ? s : s - cur.KT;
+    const uint32_t k0 = (uint32_t)kt * BK;
+    const bool live = in_cur || cross;
+    if constexpr (q < DMA_PER_WAVE) {
+      const int t = wid * DMA_PER_WAVE + q;
+      rsrc_t r = pick(in_cur, cur.a_src, nxt.a_src);
+      r[2] = live ? r[2] : 0;
+      dma16(uniform_rsrc(r), a_off[q] + k0, st_base + (uint32_t)(t * 1024));
+    } else if constexpr (q == DMA_PER_WAVE) {
+      const int kb = kt >> 1;
+      rsrc_t r;
+      uint32_t voff;
+      const uint32_t kstep = in_cur ? cur.sc_kstep : nxt.sc_kstep;
+      const uint32_t soff = in_cur ? cur.sc_off : nxt.sc_off;
+      if constexpr (OP == OP_FC1_DGRAD) {
+        // K = [da | db]: blocks from f / 128 on multiply W3
+        const int fbk = f / 128;
+        const bool second = sside == 1 && kb >= fbk;
+        r = pick(in_cur, pick(second, cur.sc_src2, cur.sc_src), pick(second, nxt.sc_src2, nxt.sc_src));
+        voff = soff + (uint32_t)(second ? kb - fbk : kb) * kstep;
       } else {
-        dma16(t.b_src, b_off[q] + ka, m0);
+        r = pick(in_cur, cur.sc_src, nxt.sc_src);
+        voff = soff + (uint32_t)kb * kstep;
       }
+      r[2] = live ? r[2] : 0;
+      dma4(uniform_rsrc(r), voff, sc_base + slot_s * SC_BYTES);
+    } else {
+      const int qq = q - DMA_PER_WAVE - 1;
+      const int t = wid * DMA_PER_WAVE + qq;
+      const uint32_t dst = st_base + (uint32_t)(OPND_BYTES + t * 1024);
+      rsrc_t r;
+      uint32_t voff;
+      if constexpr (OP == OP_FC1_FWD) {
+        const bool second = t >= 8;
+        r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
+        voff = b_off[qq] + k0;
+      } else if constexpr (OP == OP_FC1_DGRAD) {
+        const bool second = (int)k0 >= f;
+        r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
+        voff = b_off[qq] + (second ? k0 - (uint32_t)f : k0);
+      } else {
+        r = pick(in_cur, cur.b_src, nxt.b_src);
+        voff = b_off[qq] + k0;
+      }
+      r[2] = live ? r[2] : 0;
+      dma16(uniform_rsrc(r), voff, dst);
     }
-  };
-  auto issue_stage = [&](const FTile& t, int kt, int rs) __attribute__((always_inline)) {
-    static_for<0, 2 * DMA_PER_WAVE>([&](auto P) __attribute__((always_inline)) { issue_part(t, kt, rs, P.value); });
   };
 
-  const int lm = lane & 15, lg = lane >> 4;
-  // B rows of fragment j within the B tile (fc1 forward: W1 rows then W3 rows)
-  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (OP == OP_FC1_FWD) return (j < FN / 2 ? 0 : 128) + wn * (WN / 2) + 16 * (j % (FN / 2)) + lm;
-    else return wn * WN + 16 * j + lm;
+  // ---- fragments: block ib of A = rows wm*WM + 32 ib + (lane & 31); block jb
+  // of B = rows b_row0(jb) + (lane & 31) (fc1 forward: W1 rows, then the same
+  // W3 rows); lane group h reads chunks h and h + 2
+  const int lh = lane >> 5, l31 = lane & 31;
+  auto b_row0 = [&](int jb) __attribute__((always_inline)) -> int {
+    if constexpr (OP == OP_FC1_FWD) return jb * 128 + wn * (WN / 2);
+    else return wn * WN + 32 * jb;
+  };
+  const int fsw = swz(l31);
+  const uint32_t fc0 = (uint32_t)((lh ^ fsw) << 4), fc1 = (uint32_t)(((lh + 2) ^ fsw) << 4);
+  auto frag = [&](const char* p) __attribute__((always_inline)) -> i32x8_t {
+    const i32x4_t lo = *(const __attribute__((address_space(3))) i32x4_t*)(p + fc0);
+    const i32x4_t hi = *(const __attribute__((address_space(3))) i32x4_t*)(p + fc1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto read_a = [&](const char* st, int ib) __attribute__((always_inline)) -> i32x8_t {
+    return frag(st + (wm * WM + 32 * ib + l31) * BK);
+  };
+  auto read_b = [&](const char* st, int jb) __attribute__((always_inline)) -> i32x8_t {
+    return frag(st + OPND_BYTES + (b_row0(jb) + l31) * BK);
+  };
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
+    return lds + ((uint32_t)(phase + s) % NS) * STAGE_BYTES;
+  };
+  auto scale_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
+    return sc_ring + ((uint32_t)(phase + s) % NS) * SC_BYTES;
   };
 
   // ---------------------------------------------------------------- scales
-  // e4m3 ragged: sa[i], the scale of the A block of fragment row
-  // m = wm*WM + 16 i + (lane & 15), a_s[(row0 + m) * K/128 + kt] (0 past the
-  // expert's rows); the weight block scale is one value per wavefront and
-  // stage (fc1 forward: one for the W1 half, one for the W3 half).  nbw: the
-  // wavefront's 128-column block of B rows, clamped for wavefronts past N in
-  // a last, half-filled N-tile (their columns are never stored).
-  const uint32_t sa_off0 = (uint32_t)(wm * WM + lm) * (uint32_t)(Kr / BK) * 4u;
-  const uint32_t sa_istep = 16u * (uint32_t)(Kr / BK) * 4u;  // 16 rows
-  auto load_sa = [&](const FTile& t, int kt, float (&sa)[FM]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) sa[i] = buf_f32(t.sa_src, sa_off0 + (uint32_t)i * sa_istep + (uint32_t)kt * 4u);
-  };
-  auto weight_scale = [&](const FTile& t, int kt, int half) __attribute__((always_inline)) -> float {
-    const size_t e = (size_t)t.ti.e;
-    const int nbw = min((t.ti.n0 + wn * WN) / 128, (N - 1) / 128);
-    if constexpr (OP == OP_FC1_FWD) {  // W1s / W3s [E][d/128][f/128], block (kt, f-block)
-      const float* s = half ? args.b_s2 : args.b_s;
-      return s[(e * (d / 128) + kt) * (f / 128) + (t.ti.n0 / 2) / 128];
-    } else if constexpr (OP == OP_FC2_FWD) {  // W2s [E][f/128][d/128], block (kt, d-block)
-      return args.b_s[(e * (f / 128) + kt) * (d / 128) + nbw];
-    } else if constexpr (OP == OP_FC2_DGRAD) {  // W2s, block (f-block of n, kt)
-      return args.b_s[(e * (f / 128) + nbw) * (d / 128) + kt];
-    } else {  // FC1_DGRAD: W1s / W3s [E][d/128][f/128], block (d-block of n, kt mod f/128)
-      const int fb = f / 128;
-      const float* s = kt < fb ? args.b_s : args.b_s2;
-      return s[(e * (d / 128) + nbw) * fb + (kt < fb ? kt : kt - fb)];
-    }
-  };
-  // MXFP8 ragged: buffer loads of the lane's rows' scale words
-  auto load_mx = [&](const FTile& t, int kt, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) sa[i] = buf_u32(t.xa, (uint32_t)(wm * WM + 16 * i + lm) * xa_ld + (uint32_t)kt * 4u);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (OP == OP_FC1_FWD) {
-        sb[j] = buf_u32(j < FN / 2 ? t.xb : t.xb2, (uint32_t)(b_row(j) & 127) * xb_ld + (uint32_t)kt * 4u);
-      } else if constexpr (OP == OP_FC1_DGRAD) {
-        const int fb = f / 128;
-        sb[j] = buf_u32(kt < fb ? t.xb : t.xb2,
-                        (uint32_t)b_row(j) * xb_ld + (uint32_t)(kt < fb ? kt : kt - fb) * 4u);
-      } else {
-        sb[j] = buf_u32(t.xb, (uint32_t)b_row(j) * xb_ld + (uint32_t)kt * 4u);
-      }
-    }
-  };
-
-  // Per-lane scale registers of the current stage and of the stage loaded
-  // ahead (ragged products; weight gradients read theirs from sc_lds).
-  float fsa[FM], fsa_n[FM];  // e4m3: A scales
-  float wsc0 = 0.f, wsc1 = 0.f, wsc0_n = 0.f, wsc1_n = 0.f;  // e4m3: weight scales
-  uint32_t xsa[FM], xsb[FN], xsa_n[FM], xsb_n[FN];  // MXFP8: scale words
-  // the stage-ahead scales of stage kt of tile t
-  auto load_ahead = [&](const FTile& t, int kt) __attribute__((always_inline)) {
-    if constexpr (RAGGED) {
-      if constexpr (MX) {
-        load_mx(t, kt, xsa_n, xsb_n);
-      } else {
-        load_sa(t, kt, fsa_n);
-        wsc0_n = weight_scale(t, kt, 0);
-        wsc1_n = (OP == OP_FC1_FWD) ? weight_scale(t, kt, 1) : wsc0_n;
-      }
-    }
-  };
-  auto rotate = [&]() __attribute__((always_inline)) {
-    if constexpr (RAGGED) {
-      if constexpr (MX) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) xsa[i] = xsa_n[i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) xsb[j] = xsb_n[j];
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fsa[i] = fsa_n[i];
-        wsc0 = wsc0_n;
-        wsc1 = wsc1_n;
-      }
-    }
-  };
-  // A value loaded a stage ahead is complete once the stage's explicit
-  // vmcnt(0) has passed; the empty asm (settle) tells the compiler so, before
-  // this stage's DMAs are issued.
-  auto settle_all = [&]() __attribute__((always_inline)) {
-    if constexpr (RAGGED) {
-      if constexpr (MX) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) settle(xsa[i]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) settle(xsb[j]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) settle(fsa[i]);
-        settle(wsc0);
-        settle(wsc1);
-      }
-    }
-  };
-
-  f32x4_t acc[FM][FN];
-  // ---------------------------------------------------------------- one stage
-  auto compute = [&](int rs) __attribute__((always_inline)) {
-    const char* cur = lds + rs * STAGE_BYTES;
+  // MXFP8: ea[ib], the E8M0 byte of the lane's A row in block ib (the MFMA's
+  // column scale), eb[jb] that of its B row (the row scale).  e4m3: the same
+  // bytes packed into ea_pk (byte ib) and eb_pk (byte jb), taken by the MFMA's
+  // byte select, and ma / mb, the mantissas the accumulators are in units of;
+  // every B row of a 128-row weight block has the same scale, so eb_pk and mb
+  // are uniform.
+  i32x8_t af[IB], b0, b1;
+  int ea[IB], eb[JB];
+  int ea_pk = 0, eb_pk = 0;
+  float ma[IB], mb[JB];
+  f32x16_t acc[IB][JB];
+  // The scales of stage kt; e4m3, at the first stage of a 128-K block: the
+  // new exponents and mantissas, and the accumulators times u_old / u_new
+  // (not at a tile's first stage, where they are zero).  Measured faster than
+  // multiplying each block right before its first MFMA, which keeps the
+  // factors in registers through the stage.
+  auto stage_scales = [&](int kt, const char* sc) __attribute__((always_inline)) {
+    const uint32_t* wa = (const uint32_t*)sc;
+    const uint32_t* wb = (const uint32_t*)(sc + 1024);
     if constexpr (MX) {
-      const int sh8 = 8 * lg;
-      uint32_t sa[FM], sb[FN];
-      if constexpr (WGRAD) {
-        const uint32_t* sct = (const uint32_t*)&sc_lds[rs][0][0];
+      const int sh = 8 * (2 * (kt & 1) + lh);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = sct[wm * WM + 16 * i + lm];
+      for (int ib = 0; ib < IB; ++ib) ea[ib] = (int)((wa[wm * WM + 32 * ib + l31] >> sh) & 0xffu);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sb[j] = sct[256 + b_row(j)];
-      } else {
+      for (int jb = 0; jb < JB; ++jb) eb[jb] = (int)((wb[b_row0(jb) + l31] >> sh) & 0xffu);
+    } else if ((kt & 1) == 0) {
+      float ra[IB], rb[JB];
+      ea_pk = 0;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = xsa[i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) sb[j] = xsb[j];
+      for (int ib = 0; ib < IB; ++ib) {
+        const float s = __uint_as_float(wa[wm * WM + 32 * ib + l31]);
+        ea_pk |= e8_of(s) << (8 * ib);
+        const float m = mant_of(s);
+        ra[ib] = ma[ib] * __builtin_amdgcn_rcpf(m);
+        ma[ib] = m;
       }
-      i32x8_t bf[FN];
-      int sbb[FN];
-      static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
-        const int r = b_row(J.value);
-        bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, lg, swz(r));
-        sbb[J.value] = (int)((sb[J.value] >> sh8) & 0xffu);
-      });
-      // the next row's A fragment is read while this row's MFMAs run
-      i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
-      static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = I.value;
-        i32x8_t af_next;
-        if constexpr (i + 1 < FM) {
-          const int r = wm * WM + 16 * (i + 1) + lm;
-          af_next = lds_frag(cur + r * BK, lg, swz(r));
-        }
-        const int sab = (int)((sa[i] >> sh8) & 0xffu);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
-          constexpr int j = J.value;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbb[j],
-                                                                         0, sab);
-        });
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (i + 1 < FM) af = af_next;
-      });
-    } else {
-      float sa[FM];
-      f32x4_t sb[FN];  // weight gradients: this stage's B scales (4 columns per fragment)
-      if constexpr (WGRAD) {
-        const float* sct = &sc_lds[rs][0][0];
+      eb_pk = 0;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = sct[wm * WM + 16 * i + lm];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) sb[j] = *(const f32x4_t*)&sct[256 + wn * WN + 16 * j + 4 * lg];
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = fsa[i];
+      for (int jb = 0; jb < JB; ++jb) {
+        const float s = __uint_as_float((uint32_t)uniform((int)wb[b_row0(jb)]));
+        eb_pk |= e8_of(s) << (8 * jb);
+        const float m = mant_of(s);
+        rb[jb] = mb[jb] * __builtin_amdgcn_rcpf(m);
+        mb[jb] = m;
       }
-      i32x8_t bf[FN];
-      static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
-        const int r = b_row(J.value);
-        bf[J.value] = lds_frag(cur + OPND_BYTES + r * BK, lg, swz(r));
-      });
-      // Software pipeline over the FM fragment rows: the FN MFMAs of row i go
-      // to their own product registers while the scale FMAs of row i-1 (whose
-      // MFMAs have completed meanwhile) and the read of row i+1's A fragment
-      // are issued; the sched barriers keep the compiler from pulling each
-      // product's FMAs up against its MFMA.
-      auto scale_row = [&](int i, const f32x4_t (&p)[FN]) __attribute__((always_inline)) {
-        static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
-          constexpr int j = J.value;
-          if constexpr (RAGGED) {
-            const float s = sa[i] * (j < FN / 2 ? wsc0 : wsc1);
+      eb_pk = uniform(eb_pk);
+      if (kt > 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], s, acc[i][j][q]);
-          } else {
+        for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], sa[i] * sb[j][q], acc[i][j][q]);
+          for (int jb = 0; jb < JB; ++jb) {
+            const float g = ra[ib] * rb[jb];
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[ib][jb][x] *= g;
           }
-        });
-      };
-      f32x4_t pc[FN], pp[FN];
-      i32x8_t af = lds_frag(cur + (wm * WM + lm) * BK, lg, swz(wm * WM + lm));
-      static_for<0, FM>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = I.value;
-        i32x8_t af_next;
-        if constexpr (i + 1 < FM) {
-          const int r = wm * WM + 16 * (i + 1) + lm;
-          af_next = lds_frag(cur + r * BK, lg, swz(r));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, FN>([&](auto J) __attribute__((always_inline)) { pc[J.value] = mfma_fp8(bf[J.value], af); });
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (i > 0) scale_row(i - 1, pp);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, FN>([&](auto J) __attribute__((always_inline)) { pp[J.value] = pc[J.value]; });
-        if constexpr (i + 1 < FM) af = af_next;
-      });
-      scale_row(FM - 1, pp);
+      }
     }
   };
+  // block product (ib, jb) of this stage
+  auto product = [&](auto IBc, auto JBc, const i32x8_t& b) __attribute__((always_inline)) {
+    constexpr int ib = decltype(IBc)::value, jb = decltype(JBc)::value;
+    if constexpr (MX) acc[ib][jb] = mma(b, af[ib], acc[ib][jb], eb[jb], ea[ib]);
+    else acc[ib][jb] = mma<jb, ib>(b, af[ib], acc[ib][jb], eb_pk, ea_pk);
+  };
 
-  // ---------------------------------------------------------------- tile loop
-  FTile cur;
-  TileInfo tn;
-  if (!decode(slot, tn)) return;
-  setup(tn, cur);
-  int base = 0;       // ring slot of the current tile's stage 0
-  bool fresh = true;  // the current tile's first stage is not yet loaded
+  // ---------------------------------------------------------------- main loop
+  // Per stage the first half multiplies the four A blocks by B block 0 (read
+  // during the previous stage), the second half by B block 1 (read at the
+  // start of this one).  The wait + barrier that releases the next stage (and
+  // frees the oldest buffer for stage kt+3) sits between the halves; right
+  // after it B block 0 of the next stage is read, and each A block is
+  // replaced by the next stage's as soon as its second MFMA is issued.  The
+  // refill of a freed buffer is spread over the stage: B operand of stage kt+2
+  // in the first half, A operand and scale words of stage kt+3 in the second.
+  // (Rows past a ragged tile's end are multiplied like the others: a second
+  // copy of the loop that skips their blocks, as the bf16 fc1 products have,
+  // pushes the fc1 products here past the register budget -- they spill, and
+  // the reloads before the loop make every stage wait for all loads.)
+  auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst, auto TAIL)
+      __attribute__((always_inline)) {
+    stage_scales(kt, scale_ptr(kt));
+    b1 = read_b(st, 1);
+    static_for<0, IB>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U.value;
+      __builtin_amdgcn_sched_barrier(0);
+      product(IntC<u>{}, IntC<0>{}, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1)
+        issue_one(kt + LOOK - 1, IntC<DMA_PER_WAVE + 1 + u / DMA_STEP>{}, TAIL);
+    });
+    // stage kt+1 has landed for this wavefront; after the barrier it has for
+    // all, and every wavefront is done with stage kt-1, whose buffer now
+    // takes stage kt+3
+    wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2)>();
+    block_barrier();
+    b0 = read_b(nst, 0);
+    static_for<0, IB>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U.value;
+      __builtin_amdgcn_sched_barrier(0);
+      product(IntC<u>{}, IntC<1>{}, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      af[u] = read_a(nst, u);
+      if constexpr (u % DMA_STEP == DMA_STEP - 1) issue_one(kt + LOOK, IntC<u / DMA_STEP>{}, TAIL);
+      if constexpr (u == IB - 1) issue_one(kt + LOOK, IntC<DMA_PER_WAVE>{}, TAIL);
+    });
+  };
+
+  bool fresh = true;  // the current tile's first stages are not yet issued
   for (;;) {
     const int nslot = slot + (int)gridDim.x;
-    const bool have_next = PER && nslot < total;
-    int nKT = 0;
+    const bool have_next = nslot < total;
     if (have_next) {
       decode(nslot, tn);
-      if constexpr (RAGGED) nKT = Kr / BK;
-      else nKT = uniform(blkv[tn.e + 1] - blkv[tn.e]);
+      setup(tn, nxt);
     }
-    // the next tile's first stage is loaded during this tile's last one
-    const bool chain = have_next && cur.KT > 0 && nKT > 0;
-    if (fresh && cur.KT > 0) {
-      load_ahead(cur, 0);
-      issue_stage(cur, 0, base);
-      wait_vmcnt<0>();
+    cross = OP != OP_FC2_DGRAD && have_next && cur.KT >= 1 && nxt.KT >= LOOK;
+    if (fresh) {
+      // stages 0 .. LOOK-2 and stage LOOK-1's A operand and scale words in
+      // flight (its B operand follows in stage 0); wait for stage 0
+      static_for<0, LOOK - 1>([&](auto S) __attribute__((always_inline)) {
+        static_for<0, LOADS_PER_STAGE>([&](auto Q) __attribute__((always_inline)) {
+          issue_one(S.value, Q, IntC<1>{});
+        });
+      });
+      static_for<0, DMA_PER_WAVE + 1>([&](auto Q) __attribute__((always_inline)) {
+        issue_one(LOOK - 1, Q, IntC<1>{});
+      });
+      wait_vmcnt<LOADS_PER_STAGE * (LOOK - 2) + DMA_PER_WAVE + 1>();
       block_barrier();
-      rotate();
+    }
+    {
+      const char* st0 = stage_ptr(0);
+      static_for<0, IB>([&](auto I) __attribute__((always_inline)) { af[I.value] = read_a(st0, I.value); });
+      b0 = read_b(st0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int ib = 0; ib < IB; ++ib) {
+      ma[ib] = 1.0f;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < cur.KT; ++kt) {
-      const int rs = (base + kt) & 1;
-      settle_all();
-      if (kt + 1 < cur.KT) {
-        load_ahead(cur, kt + 1);
-        issue_stage(cur, kt + 1, rs ^ 1);
-      } else if (chain) {
-        FTile nxt;
-        setup(tn, nxt);
-        load_ahead(nxt, 0);
-        issue_stage(nxt, 0, rs ^ 1);
-      }
-      compute(rs);
-      wait_vmcnt<0>();
-      block_barrier();
-      rotate();
+      for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = f32x16_t{};
     }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) mb[jb] = 1.0f;
+    // the last LOOK stages issue the loads that may fall past the tile
+    const int kt_tail = max(cur.KT - LOOK, 0);
+    for (int kt = 0; kt < kt_tail; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<0>{});
+    for (int kt = kt_tail; kt < cur.KT; ++kt) stage_body(kt, stage_ptr(kt), stage_ptr(kt + 1), IntC<1>{});
 
     // ---------------------------------------------------------------- epilogue
-    store_tile<OP, FM, FN, WM, WN, RAGGED, RS>(args, acc, cur.ti, cur.M, N, wm, wn, lane, dp_red);
+    // e4m3: back from units of the last block's mantissas
+    if constexpr (!MX) {
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float g = ma[ib] * mb[jb];
+#pragma unroll
+          for (int x = 0; x < 16; ++x) acc[ib][jb][x] *= g;
+        }
+    }
+    {
+      f32x4_t frg[2 * IB][2 * JB];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+          to_frags(acc[ib][jb], frg[2 * ib][2 * jb], frg[2 * ib][2 * jb + 1], frg[2 * ib + 1][2 * jb],
+                   frg[2 * ib + 1][2 * jb + 1]);
+      store_tile<OP, 2 * IB, 2 * JB, WM, WN, true, RS>(args, frg, ti, ti.rows, N, wm, wn, lane, dp_red);
+    }
     if (!have_next) break;
-    base = (base + cur.KT) & 1;
-    fresh = !chain;
+    if (cross) {
+      phase = (int)((uint32_t)(phase + cur.KT) % NS);
+      fresh = false;
+    } else {
+      // the past-the-end loads read nothing but still write the ring: drain
+      // them (and every LDS read) before the next tile's prologue
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      block_barrier();
+      fresh = true;
+    }
     slot = nslot;
-    setup(tn, cur);
+    ti = tn;
+    cur = nxt;
   }
+  wait_vmcnt<0>();  // no LDS write may be in flight when the block ends
 }
-
-// Products launched persistent: the weight gradients, whose tiles have only
-// an expert's few 128-row token blocks of K, so that a first load per tile
-// weighs most.  (The ragged-M products, with 12-32 stages per tile, run out
-// of scalar registers when persistent: the compiler then spills.)
-// (Measured on the skewed shape: MXFP8 fc1 / fc2 wgrad 4 % / 3 % faster, e4m3
-// fc1 wgrad 3 % faster; the persistent e4m3 fc2 wgrad spills and was 13 %
-// slower, so it keeps one block per tile.)
-template <int OP, bool MX>
-constexpr bool kPersistent = OP == OP_FC1_WGRAD || (MX && OP == OP_FC2_WGRAD);
 
 template <int OP, bool MX>
 int launch(const GemmArgs& a, hipStream_t s) {
-  int NT, MT = 0;
-  int64_t grid;
-  if (OP <= OP_FC1_DGRAD) {
-    const int N = (OP == OP_FC1_FWD) ? 2 * a.f : (OP == OP_FC2_DGRAD ? a.f : a.d);
-    NT = (N + BN - 1) / BN;
-    grid = ((int64_t)a.P / BM + a.E) * NT;  // upper bound of the device-side tile count
-  } else {
-    const int M = (OP == OP_FC2_WGRAD) ? a.f : a.d;
-    const int N = (OP == OP_FC2_WGRAD) ? a.d : 2 * a.f;
-    MT = (M + BM - 1) / BM;
-    NT = (N + BN - 1) / BN;
-    grid = (int64_t)a.E * MT * NT;
-  }
-  if (grid == 0) return MOE_OK;
+  const int N = (OP == OP_FC1_FWD) ? 2 * a.f : (OP == OP_FC2_DGRAD ? a.f : a.d);
+  const int NT = (N + BN - 1) / BN;
+  int64_t grid = ((int64_t)a.P / BM + a.E) * NT;  // upper bound of the device-side tile count
+  if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  constexpr bool PER = kPersistent<OP, MX>;
-  if (PER) {
+  // persistent blocks, one per compute unit (a multiple of 8), except fc2
+  // dgrad (see the kernel)
+  if (OP != OP_FC2_DGRAD) {
     const int ncu = gemm_persistent_blocks();
     if (ncu <= 0) return MOE_ERR_HIP;
     if (grid > ncu) grid = ncu;
   }
+  const unsigned g = (unsigned)grid;
   bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
   if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
     if (a.row_prob) {
-      gemm_fp8_kernel<OP, MX, true, PER><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+      gemm_fp8_kernel<OP, MX, true><<<g, NW * 64, 0, s>>>(a, NT);
       scaled = true;
     }
   }
-  if (!scaled) gemm_fp8_kernel<OP, MX, false, PER><<<dim3((unsigned)grid), NW * 64, 0, s>>>(a, NT, MT);
+  if (!scaled) gemm_fp8_kernel<OP, MX, false><<<g, NW * 64, 0, s>>>(a, NT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -635,8 +636,8 @@ int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
     case OP_FC2_FWD: return launch<OP_FC2_FWD, false>(a, s);
     case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, false>(a, s);
     case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, false>(a, s);
-    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, false>(a, s);
-    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, false>(a, s);
+    case OP_FC2_WGRAD:
+    case OP_FC1_WGRAD: return gemm_fp8_wgrad_launch(op, false, a, s);
   }
   return MOE_ERR_INVALID;
 }
@@ -647,8 +648,8 @@ int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
     case OP_FC2_FWD: return launch<OP_FC2_FWD, true>(a, s);
     case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, true>(a, s);
     case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, true>(a, s);
-    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, true>(a, s);
-    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, true>(a, s);
+    case OP_FC2_WGRAD:
+    case OP_FC1_WGRAD: return gemm_fp8_wgrad_launch(op, true, a, s);
   }
   return MOE_ERR_INVALID;
 }

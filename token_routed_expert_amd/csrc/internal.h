@@ -119,10 +119,13 @@ struct GemmArgs {
 int gemm_bf16_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // gemm_f32.hip: fp32 kernels
 int gemm_f32_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
-// gemm_fp8.hip: e4m3 x e4m3 MFMA with per-128-K scale promotion, bf16 outputs
+// gemm_fp8.hip: e4m3 x e4m3 MFMA with fp32 block scales, bf16 outputs
 int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // the same products with MXFP8 operands (hardware block-scaled MFMA)
 int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
+// gemm_fp8_wgrad.hip: the two weight gradients of both (mx: MXFP8), called
+// by gemm_fp8_launch / gemm_mx_launch
+int gemm_fp8_wgrad_launch(GemmOp op, bool mx, const GemmArgs& a, hipStream_t s);
 // Compute units of the current device rounded down to a multiple of 8 (the
 // grid of the persistent grouped-GEMM launches), or -1.
 int gemm_persistent_blocks();
