@@ -343,6 +343,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       r[2] = live ? r[2] : 0;
       dma16(uniform_rsrc(r), a_off[q] + k0, st_base + (uint32_t)(t * 1024));
     } else if constexpr (q == DMA_PER_WAVE) {
+      // a 128-K block's words serve both of its stages and are loaded with
+      // the first; the second stage's DMA reads nothing (a zero-length range:
+      // no memory request, and the zeros land in its own slot, which no one
+      // reads), so that every stage issues the same loads for the waits
       const int kb = kt >> 1;
       rsrc_t r;
       uint32_t voff;
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         r = pick(in_cur, cur.sc_src, nxt.sc_src);
         voff = soff + (uint32_t)kb * kstep;
       }
-      r[2] = live ? r[2] : 0;
+      r[2] = (live && (kt & 1) == 0) ? r[2] : 0;
       dma4(uniform_rsrc(r), voff, sc_base + slot_s * SC_BYTES);
     } else {
       const int qq = q - DMA_PER_WAVE - 1;
@@ -407,8 +411,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
     return lds + ((uint32_t)(phase + s) % NS) * STAGE_BYTES;
   };
+  // the scale words of stage s: in the slot of its block's first stage
   auto scale_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
-    return sc_ring + ((uint32_t)(phase + s) % NS) * SC_BYTES;
+    return sc_ring + ((uint32_t)(phase + (s & ~1)) % NS) * SC_BYTES;
   };
 
   // ---------------------------------------------------------------- scales
