@@ -46,8 +46,8 @@ def log(*a):
 
 # The source file of each dtype's grouped-GEMM kernels.
 GEMM_SOURCE = {"bf16": ["gemm_bf16.hip"], "f32": ["gemm_f32.hip"],
-               "e4m3": ["gemm_fp8.hip", "gemm_fp8_wgrad.hip"],
-               "mxfp8": ["gemm_fp8.hip", "gemm_fp8_wgrad.hip"]}
+               "e4m3": ["gemm_fp8.hip"],
+               "mxfp8": ["gemm_fp8.hip"]}
 
 
 def kernel_sources_sha256(dtype: str) -> str:

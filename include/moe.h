@@ -372,14 +372,15 @@ int64_t moe_token_block_capacity(int64_t P, int64_t E);
  * Row r of the matrix is row src_row[r] of src (src_row NULL: row r), src
  * bf16 [.][C], C a multiple of 128.  With cap = moe_token_block_capacity:
  *   blk     out int32 [E+1]: first block of each expert, blk[E] = blocks used;
- *   codes_t out uint8 [C][128 * cap]: codes transposed; row r of expert e
- *           sits at column 128 * blk[e] + (r - offsets[e]); columns of a
- *           short block past the expert's rows, and unused blocks, hold 0
- *           (unused blocks are not written);
- *   scales  out fp32 [cap][C]: scale of block b at row b.
+ *   codes   out uint8 [P][C]: the codes of row r in row r (row-major, the
+ *           matrix's own layout; the weight-gradient GEMMs read them
+ *           MN-contiguous);
+ *   scales  out fp32 [cap][C]: scale of the expert's block j (rows
+ *           offsets[e] + 128 j ..) and column c at row blk[e] + j; rows from
+ *           blk[E] on are not written.
  */
 int moe_quantize_token_blocks(const int32_t* offsets, int64_t E, int64_t P, const void* src,
-                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes_t,
+                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes,
                               float* scales, void* stream);
 
 /*
@@ -553,9 +554,9 @@ int moe_grouped_gemm_bwd_rowscaled(const moe_shape* sh, const int32_t* offsets, 
  *    codes [E][R][C] with row-block bytes [E][R][C/32] (read by the
  *    data-gradient products), and transposed codes [E][C][R] with
  *    column-block bytes [E][C][R/32] (read by the forward products);
- *  - weight-gradient operands as moe_quantize_token_blocks lays them out,
- *    with bytes [ldt/128][C][4] (byte g of word (b, c): rows 32 g.. of
- *    128-row block b; 32-row blocks restart at each expert).
+ *  - weight-gradient operands as moe_quantize_token_blocks lays them out
+ *    (codes [P][C]), with bytes [cap][C][4] (byte g of word (b, c): rows
+ *    32 g.. of 128-row block b; 32-row blocks restart at each expert).
  * Shapes: d, f multiples of 128, no shared expert.
  */
 
@@ -580,12 +581,12 @@ int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uin
                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream);
 
 /* moe_quantize_token_blocks_mx -- as moe_quantize_token_blocks, with 32-row
- * scale blocks: codes_t [C][ldt] (ldt = 128 * capacity), scale bytes
- * [capacity][C][4] (the four 32-row blocks of each 128-row block and column
- * in one word); blocks with no rows have s = 0. */
+ * scale blocks: codes [P][C], scale bytes [capacity][C][4] (the four 32-row
+ * blocks of each 128-row block and column in one word); 32-row blocks with
+ * no rows have s = 0. */
 int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
                                  const int32_t* src_row, int64_t C, int32_t* blk,
-                                 uint8_t* codes_t, uint8_t* scales, void* stream);
+                                 uint8_t* codes, uint8_t* scales, void* stream);
 
 /* moe_permute_mx -- moe_permute_e4m3 for MXFP8 rows: codes [T][d] and scale
  * bytes [T][d/32] moved to the permuted order (bit copies). */

@@ -7,13 +7,11 @@ take a device buffer apart so that the tests can compare it with the oracle
 element by element, and check that the device's padding holds what the
 library's header promises.
 
-Device token-block layout (include/moe.h, moe_quantize_token_blocks and
-moe_quantize_token_blocks_mx): with blk128 = first 128-row block of each
-expert (prefix sum of ceil(m_e / 128)), row r of expert e is column
-128 * blk128[e] + (r - offsets[e]) of the transposed codes [C][128 cap];
-columns past the expert's rows in its last block hold code 0.  e4m3 scales
-are fp32 [cap][C], one per 128-row block; MXFP8 scale bytes are [cap][C][4],
-byte g of (block b, column c) scaling rows 32 g .. 32 g + 31 of block b.
+Device token-block scales (include/moe.h, moe_quantize_token_blocks_mx):
+with blk128 = first 128-row block of each expert (prefix sum of
+ceil(m_e / 128)), MXFP8 scale bytes are [cap][C][4], byte g of (block b,
+column c) scaling rows 32 g .. 32 g + 31 of block b (the codes are the
+operand's own [P][C] rows and need no map).
 """
 from __future__ import annotations
 
@@ -24,23 +22,6 @@ def _blocks(offsets, rows_per_block):
     offsets = np.asarray(offsets, dtype=np.int64)
     nb = (np.diff(offsets) + rows_per_block - 1) // rows_per_block
     return np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
-
-
-def token_block_codes(codes_t, offsets):
-    """Transposed device codes [C][128 cap] -> codes [P][C] in row order.
-    Asserts that the columns past each expert's rows in its last 128-row
-    block are zero."""
-    codes_t = np.asarray(codes_t)
-    offsets = np.asarray(offsets, dtype=np.int64)
-    b128 = _blocks(offsets, 128)
-    P, C = int(offsets[-1]), codes_t.shape[0]
-    out = np.zeros((P, C), dtype=codes_t.dtype)
-    for e in range(len(offsets) - 1):
-        r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        c0, c1 = 128 * int(b128[e]), 128 * int(b128[e + 1])
-        out[r0:r1] = codes_t[:, c0:c0 + (r1 - r0)].T
-        assert not codes_t[:, c0 + (r1 - r0):c1].any(), f"expert {e}: non-zero padding codes"
-    return out
 
 
 def mx_token_block_scales(sbw, offsets):

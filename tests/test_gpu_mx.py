@@ -93,17 +93,18 @@ def test_quantize_token_blocks_mx_bit_exact(gather):
     src = torch.from_numpy(src_np.astype(np.float32)).to(torch.bfloat16)
     cap = tre.moe_token_block_capacity(P, E)
     blk = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    codes_t = torch.full((C, 128 * cap), 0xAB, dtype=torch.uint8, device="cuda")
+    codes = torch.full((P, C), 0xAB, dtype=torch.uint8, device="cuda")
     sbt = torch.full((cap, C, 4), 0xCD, dtype=torch.uint8, device="cuda")
     tre.moe_quantize_token_blocks_mx(torch.from_numpy(off).cuda(), E, P, src.cuda(),
                                      None if src_row is None else torch.from_numpy(src_row).cuda(),
-                                     blk, codes_t, sbt)
+                                     blk, codes, sbt)
     vals = src.float().numpy()[src_row] if gather else src.float().numpy()
     rq, rs = oracle.quant_mx_token_blocks(vals, off)
     NB = int(oracle.token_block_offsets(off)[-1])
     assert np.array_equal(blk.cpu().numpy(), oracle.token_block_offsets(off))
-    # the device's padded, transposed layout taken apart (indexing only)
-    assert np.array_equal(device_layout.token_block_codes(u8(codes_t)[:, :128 * NB], off), rq)
+    # codes in the matrix's own row-major layout; the scale words taken apart
+    # (indexing only)
+    assert np.array_equal(u8(codes), rq)
     assert np.array_equal(device_layout.mx_token_block_scales(u8(sbt)[:NB], off), rs)
 
 

@@ -9,11 +9,10 @@
 // weights, and 128 tokens per column for the operands of the weight
 // gradients, so every scale block spans 128 values of the contraction axis.
 //
-// This file holds the four products with ragged M (an expert's permuted rows);
-// the weight gradients, whose K is an expert's few token blocks, have a kernel
-// of their own (gemm_fp8_wgrad.hip).  Both operands are read with the
-// contraction axis contiguous (C[m][n] = sum_k A[m][k] B[n][k]); the weight
-// quantiser stores the transposed codes the forward products need:
+// The four products with ragged M (an expert's permuted rows) read both
+// operands with the contraction axis contiguous (C[m][n] = sum_k A[m][k]
+// B[n][k]); the weight quantiser stores the transposed codes the forward
+// products need:
 //
 //   op          A (rows x K)                 B (rows x K)               K
 //   FC1_FWD     xp codes [P][d]              W1^T, W3^T codes [f][d]    d
@@ -21,13 +20,21 @@
 //   FC2_DGRAD   dO codes [P][d]              W2 codes [f][d]            d
 //   FC1_DGRAD   dab codes [P][2f]            W1 | W3 codes [d][f]       2f
 //
+// The weight gradients contract over an expert's rows and read both operands
+// in their row-major form, MN-contiguous (C[m][n] = sum_k A[k][m] B[k][n]),
+// with one scale per 128-row token block and column:
+//
+//   FC2_WGRAD   h codes [P][f]   (m: f)      dO codes [P][d]  (n: d)    rows of e
+//   FC1_WGRAD   xp codes [P][d]  (m: d)      dab codes [P][2f] (n: 2f)  rows of e
+//
 // Pipeline: that of the bf16 kernels -- 256 x 256 block tile, 8 wavefronts of
 // 128 x 64, persistent blocks walking the XCD-remapped device-side tile list
 // with the next tile's first stages streamed under the current one's last,
 // fused SwiGLU forward / backward epilogues -- with K advancing 64 codes per
 // stage through a 4-deep LDS ring (32 KB of codes per stage: 256 rows of 64
-// bytes per operand), every operand byte moved by buffer_load ... lds issued
-// up to three stages ahead.  The products are v_mfma_scale_f32_32x32x64_f8f6f4
+// bytes per operand, or in the weight gradients 64 k-rows of 256 bytes),
+// every operand byte moved by buffer_load ... lds issued up to three stages
+// ahead.  The products are v_mfma_scale_f32_32x32x64_f8f6f4
 // (a wavefront covers its 128 x 64 sub-tile with 4 x 2 blocks of 32 x 32).
 // The 64-deep MFMA is what allows the 32 KB stage and so the 4-deep ring: the
 // 128-deep 16x16x128 form needs 64 KB per stage, two stages in the LDS.
@@ -41,8 +48,9 @@
 // columns of one output row.
 //
 // Scales.  With each stage's codes come its scale words, 2 KB per stage: one
-// 32-bit word per A row and per B row (e4m3: the fp32 scale of the row's
-// 128-K block; MXFP8: the four E8M0 bytes of that block).  MXFP8 bytes go
+// 32-bit word per A row and per B row (weight gradients: per A and B column;
+// e4m3: the fp32 scale of the row's 128-K block; MXFP8: the four E8M0 bytes
+// of that block).  MXFP8 bytes go
 // straight into the MFMA.  An e4m3 scale s = 2^e * m (m in [1, 2)) is split:
 // the MFMA applies 2^e of the A row and of the B row as E8M0 scales, and the
 // accumulators are kept in units of the current block's mantissas,
@@ -50,7 +58,11 @@
 // stage of each 128-K block they are multiplied by u_old / u_new (in
 // (1/4, 4)), and at the end of the tile by the last u.  That is one
 // multiplication per accumulator per 128-K block, as a promotion of per-block
-// partial products would take, without their registers.
+// partial products would take, without their registers.  In the weight
+// gradients m_B varies per output column too, so a lane's factor at a block
+// change is r_A(m) * r_B(n) for each of its 16 columns n per 32 x 32 block;
+// each lane forms r_B of one of the wavefront's 64 columns, and the wavefront
+// trades them through 256 bytes of LDS of its own.
 #include "gemm_common.h"
 
 namespace tre {
@@ -85,6 +97,25 @@ __device__ __forceinline__ i32x8_t lds_frag(const char* row_base, int h, int sw)
   const i32x4_t hi =
       *(const __attribute__((address_space(3))) i32x4_t*)(row_base + (((h + 2) ^ sw) << 4));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// MN-contiguous stages of the weight gradients: 64 k-rows of 256 bytes per
+// operand; 32-byte unit u of k-row k is stored at unit u ^ (k & 7).  A
+// fragment (32 MN indices = one unit, 64 K) is four ds_read_b64_tr_b8: for each
+// 8-row group the 16 lanes of a group pass 8-byte pieces (lane i: k-row i / 2,
+// bytes 8 (i & 1) .. of the group's 16 columns) and lane i receives the 8
+// k-values of column i (measured with a probe).  Lane l takes column l & 31
+// and k-rows 16 h .. + 15 and 32 + 16 h .. + 15 (h = l >> 5), the MFMA's
+// operand layout.  Each half-wavefront reads 8 k-rows x 32 bytes, which the
+// unit swizzle spreads over all 64 banks.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ i32x2_t lds_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
+}
+__device__ __forceinline__ i32x8_t frag_tr(const char* p) {
+  const i32x2_t r0 = lds_tr8(p), r1 = lds_tr8(p + 8 * 256), r2 = lds_tr8(p + 32 * 256),
+                r3 = lds_tr8(p + 40 * 256);
+  return i32x8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
 // e4m3 x e4m3 32x32x64 block product into c; sa scales the MFMA's rows (the
@@ -153,42 +184,75 @@ __device__ __forceinline__ int bits_u32(float v) { return (int)__float_as_uint(v
 // whose epilogue reads a|b and would wait behind the next tile's loads, is
 // launched with one block per tile).  The loads the pipeline issues past a
 // tile's last stage fetch the first three stages of the next tile.
+//
+// Weight gradients (WG): the tiles are E x MT x NT (expert-major), K is the
+// expert's rows, ceil(rows / 64) stages (0 for an empty expert, which writes
+// zeros).  A 128-row token block spans two stages; its scale words come with
+// the first (the second issues a zero-length load) into one of three block
+// slots, (block number in the block's stream) mod 3, so that at a block's
+// first stage the previous block's words are still there (the words of block
+// b + 3, the next to take b's slot, are issued in the second half of b + 1's
+// first stage at the earliest, after every read of b's words); the second
+// stage's zero-length load lands in a fourth slot that no one reads.
 template <int OP, bool MX, bool RS>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT) {
+__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int NT, int MT) {
   constexpr int WAVES_N = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
   constexpr int IB = WM / 32, JB = WN / 32;      // 4 x 2 blocks of 32 x 32
-  static_assert(OP <= OP_FC1_DGRAD, "ragged-M products only");
+  constexpr bool WG = OP == OP_FC2_WGRAD || OP == OP_FC1_WGRAD;
   constexpr int DMA_STEP = 4 / DMA_PER_WAVE;     // MFMA steps per DMA instruction
   static_assert(IB == 4 && JB == 2 && DMA_STEP == 2, "tile shape");
+  static_assert(!(WG && RS), "row-scaled epilogues are ragged-M only");
 
-  // the stage ring, the scale ring, then the schedule scratch, the inclusive
-  // prefix of the experts' M-tile counts and (row-scaled fc2 dgrad) the
-  // per-row <h, dh'> partials
-  constexpr int EXTRA = (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4;
+  // the stage ring, the scale ring, then (ragged M) the schedule scratch, the
+  // inclusive prefix of the experts' M-tile counts and (row-scaled fc2 dgrad)
+  // the per-row <h, dh'> partials, or (weight gradients) 64 floats per
+  // wavefront for the column mantissas it trades
+  constexpr int EXTRA = WG ? NW * 64 * 4 : (NW + 64 * NW + (RS ? (NW / 2) * 256 : 0)) * 4;
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES + NS * SC_BYTES + EXTRA];
-  // the expert offsets, copied once: decoding a tile then reads LDS, whose
-  // wait (lgkmcnt) leaves the DMA loads in flight
+  // the expert offsets (and the token-block table), copied once: decoding a
+  // tile then reads LDS, whose wait (lgkmcnt) leaves the DMA loads in flight
   __shared__ int offs[257];
+  __shared__ int blks[WG ? 257 : 1];
   char* const sc_ring = lds + NS * STAGE_BYTES;
   int* const sched = (int*)(lds + NS * STAGE_BYTES + NS * SC_BYTES);
   int* const mt_incl = sched + NW;
   float* const dp_red = (float*)(mt_incl + 64 * NW);
+  float* const nsc = (float*)(lds + NS * STAGE_BYTES + NS * SC_BYTES);  // WG
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = uniform(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int d = args.d, f = args.f, E = args.E;
 
   // ---------------------------------------------------------------- tiles
-  // M = the tile's rows, K and N fixed
-  const int N = (OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d);
+  // Ragged M: M = the tile's rows, K and N fixed.  Weight gradients: M and N
+  // fixed, K = the expert's rows.
+  const int N = WG ? ((OP == OP_FC2_WGRAD) ? d : 2 * f)
+                   : ((OP == OP_FC1_FWD) ? 2 * f : (OP == OP_FC2_DGRAD ? f : d));
   const int Kr = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d : (OP == OP_FC2_FWD ? f : 2 * f);
-  for (int i = tid; i <= E; i += NW * 64) offs[i] = args.offsets[i];
+  const int Mw = (OP == OP_FC2_WGRAD) ? f : d;
+  for (int i = tid; i <= E; i += NW * 64) {
+    offs[i] = args.offsets[i];
+    if constexpr (WG) blks[i] = args.blk[i];
+  }
   __syncthreads();
-  const int total = uniform(mtile_prefix<BM, NW>(offs, E, mt_incl, sched) * NT);
+  int total;
+  if constexpr (WG) total = E * MT * NT;
+  else total = mtile_prefix<BM, NW>(offs, E, mt_incl, sched) * NT;
+  total = uniform(total);
   auto decode = [&](int slot, TileInfo& ti) __attribute__((always_inline)) {
-    ragged_tile(offs, mt_incl, E, NT, BM, xcd_remap(slot, total), ti);
-    ti.n0 *= BN;
+    const int logical = xcd_remap(slot, total);
+    if constexpr (WG) {
+      ti.e = logical / (MT * NT);
+      const int rem = logical % (MT * NT);
+      ti.m0 = (rem / NT) * BM;
+      ti.n0 = (rem % NT) * BN;
+      ti.row0 = offs[ti.e];
+      ti.rows = offs[ti.e + 1] - ti.row0;
+    } else {
+      ragged_tile(offs, mt_incl, E, NT, BM, logical, ti);
+      ti.n0 *= BN;
+    }
     ti.e = uniform(ti.e);
     ti.row0 = uniform(ti.row0);
     ti.rows = uniform(ti.rows);
@@ -197,8 +261,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   };
 
   // ---------------------------------------------------------------- operands
-  const uint32_t a_ld = (uint32_t)Kr;
-  const uint32_t b_ld = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)d : (uint32_t)f;
+  // row lengths in bytes: ragged M, of the K-contiguous rows; weight
+  // gradients, of the MN-contiguous k-rows
+  const uint32_t a_ld = WG ? (uint32_t)Mw : (uint32_t)Kr;
+  const uint32_t b_ld = WG ? (uint32_t)N
+                           : ((OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)d : (uint32_t)f);
   const int kbr = Kr / 128;  // 128-K blocks per row
 
   // Per tile: buffer resources over what the tile reads (rows past an
@@ -215,101 +282,134 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   const int sside = wid >> 2, sidx = 64 * (wid & 3) + lane;
   auto setup = [&](const TileInfo& ti, Opnd& o) __attribute__((always_inline)) {
     const size_t e = (size_t)ti.e;
-    o.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Kr, (uint32_t)ti.rows * a_ld);
-    o.KT = Kr / BK;
-    if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
-      const size_t off = e * (size_t)f * d + (size_t)(ti.n0 / 2) * d;
-      o.b_src = make_rsrc(args.b_q + off, 128u * b_ld);
-      o.b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
-    } else if constexpr (OP == OP_FC2_FWD) {  // W2^T [d][f]
-      o.b_src = make_rsrc(args.b_q + e * (size_t)d * f + (size_t)ti.n0 * f, (uint32_t)(d - ti.n0) * b_ld);
-      o.b_src2 = o.b_src;
-    } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 [f][d]
-      o.b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0 * d, (uint32_t)(f - ti.n0) * b_ld);
-      o.b_src2 = o.b_src;
-    } else {  // FC1_DGRAD: W1 | W3 [d][f], K = 2f
-      const size_t off = e * (size_t)d * f + (size_t)ti.n0 * f;
-      o.b_src = make_rsrc(args.b_q + off, (uint32_t)(d - ti.n0) * b_ld);
-      o.b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)(d - ti.n0) * b_ld);
-    }
-    // ---- scale words (every field set first: a zero-length resource reads nothing)
     o.sc_src = rsrc_t{0, 0, 0, 0};
     o.sc_src2 = rsrc_t{0, 0, 0, 0};
     o.sc_off = 0;
     o.sc_kstep = 0;
-    if (sside == 0) {
-      // A rows: e4m3 a_s [P][K/128] floats; MXFP8 a_sx [P][K/32] bytes
-      if constexpr (MX) {
-        o.sc_src = make_rsrc(args.a_sx + (size_t)ti.row0 * (Kr / 32), (uint32_t)ti.rows * (uint32_t)(Kr / 32));
-        o.sc_off = (uint32_t)sidx * (uint32_t)(Kr / 32);
-      } else {
-        o.sc_src = make_rsrc(args.a_s + (size_t)ti.row0 * kbr, (uint32_t)ti.rows * (uint32_t)kbr * 4u);
-        o.sc_off = (uint32_t)sidx * (uint32_t)kbr * 4u;
-      }
-      o.sc_kstep = 4u;
-    } else if constexpr (MX) {
-      // B rows: the E8M0 bytes [E][n][K/32] of the weight in the orientation read
-      const int xb = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d / 32 : f / 32;
-      size_t b0;
-      int brows;
-      if constexpr (OP == OP_FC1_FWD) {
-        b0 = (e * f + ti.n0 / 2) * xb; brows = 128;
-      } else if constexpr (OP == OP_FC2_FWD) {
-        b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
-      } else if constexpr (OP == OP_FC2_DGRAD) {
-        b0 = (e * f + ti.n0) * xb; brows = f - ti.n0;
-      } else {
-        b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
-      }
-      const bool w3 = OP == OP_FC1_FWD && sidx >= 128;  // fc1 forward: B rows 128.. are W3's
-      o.sc_src = make_rsrc((w3 ? args.b_sx2 : args.b_sx) + b0, (uint32_t)brows * (uint32_t)xb);
-      if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_sx2 + b0, (uint32_t)brows * (uint32_t)xb);
-      o.sc_off = (uint32_t)((OP == OP_FC1_FWD) ? (sidx & 127) : sidx) * (uint32_t)xb;
-      o.sc_kstep = 4u;
+    if constexpr (WG) {
+      // codes: the expert's rows from column m0 (n0) on; rows past the
+      // expert, and the columns past the matrix in its last row, read zero
+      const int64_t rows = ti.rows;
+      o.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Mw + ti.m0,
+                          (uint32_t)max(rows * Mw - ti.m0, (int64_t)0));
+      o.b_src = make_rsrc(args.b_q + (size_t)ti.row0 * N + ti.n0,
+                          (uint32_t)max(rows * N - ti.n0, (int64_t)0));
+      o.b_src2 = o.b_src;
+      o.KT = (ti.rows + BK - 1) / BK;
+      // scale words [blocks][columns] (e4m3 fp32; MXFP8 four E8M0 bytes),
+      // the expert's blocks from blks[e] on
+      const int nblk = (ti.rows + 127) / 128;
+      const int cols = sside == 0 ? Mw : N, c0 = sside == 0 ? ti.m0 : ti.n0;
+      const char* sbase = sside == 0 ? (MX ? (const char*)args.a_sx : (const char*)args.a_s)
+                                     : (MX ? (const char*)args.b_sx : (const char*)args.b_s);
+      o.sc_src = make_rsrc(sbase + ((size_t)blks[ti.e] * cols + c0) * 4,
+                           (uint32_t)max(((int64_t)nblk * cols - c0) * 4, (int64_t)0));
+      o.sc_off = (uint32_t)sidx * 4u;
+      o.sc_kstep = (uint32_t)cols * 4u;
     } else {
-      // B rows: e4m3 weight block scales, [E][d/128][f/128] (W1, W3) or
-      // [E][f/128][d/128] (W2); every B row of a 128-row block reads the same
-      // word (rows past N read past the range: zero)
-      const int db = d / 128, fb = f / 128;
-      const int nb = db * fb;
-      const float* s = (OP == OP_FC1_FWD && sidx >= 128) ? args.b_s2 : args.b_s;
-      o.sc_src = make_rsrc(s + e * (size_t)nb, (uint32_t)nb * 4u);
-      if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_s2 + e * (size_t)nb, (uint32_t)nb * 4u);
-      if constexpr (OP == OP_FC1_FWD) {  // block (kb, f-block of the tile's W1 / W3 rows)
-        o.sc_off = (uint32_t)((ti.n0 / 2) / 128) * 4u;
-        o.sc_kstep = (uint32_t)fb * 4u;
-      } else if constexpr (OP == OP_FC2_FWD) {  // W2 block (kb, d-block of the row)
-        const int nbk = (ti.n0 + sidx) / 128;
-        o.sc_off = nbk < db ? (uint32_t)nbk * 4u : 0x40000000u;
-        o.sc_kstep = (uint32_t)db * 4u;
-      } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 block (f-block of the row, kb)
-        const int nbk = (ti.n0 + sidx) / 128;
-        o.sc_off = nbk < fb ? (uint32_t)nbk * (uint32_t)db * 4u : 0x40000000u;
+      o.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Kr, (uint32_t)ti.rows * a_ld);
+      o.KT = Kr / BK;
+      if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
+        const size_t off = e * (size_t)f * d + (size_t)(ti.n0 / 2) * d;
+        o.b_src = make_rsrc(args.b_q + off, 128u * b_ld);
+        o.b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
+      } else if constexpr (OP == OP_FC2_FWD) {  // W2^T [d][f]
+        o.b_src = make_rsrc(args.b_q + e * (size_t)d * f + (size_t)ti.n0 * f, (uint32_t)(d - ti.n0) * b_ld);
+        o.b_src2 = o.b_src;
+      } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 [f][d]
+        o.b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0 * d, (uint32_t)(f - ti.n0) * b_ld);
+        o.b_src2 = o.b_src;
+      } else {  // FC1_DGRAD: W1 | W3 [d][f], K = 2f
+        const size_t off = e * (size_t)d * f + (size_t)ti.n0 * f;
+        o.b_src = make_rsrc(args.b_q + off, (uint32_t)(d - ti.n0) * b_ld);
+        o.b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)(d - ti.n0) * b_ld);
+      }
+      // ---- scale words (every field set first: a zero-length resource reads nothing)
+      if (sside == 0) {
+        // A rows: e4m3 a_s [P][K/128] floats; MXFP8 a_sx [P][K/32] bytes
+        if constexpr (MX) {
+          o.sc_src = make_rsrc(args.a_sx + (size_t)ti.row0 * (Kr / 32), (uint32_t)ti.rows * (uint32_t)(Kr / 32));
+          o.sc_off = (uint32_t)sidx * (uint32_t)(Kr / 32);
+        } else {
+          o.sc_src = make_rsrc(args.a_s + (size_t)ti.row0 * kbr, (uint32_t)ti.rows * (uint32_t)kbr * 4u);
+          o.sc_off = (uint32_t)sidx * (uint32_t)kbr * 4u;
+        }
         o.sc_kstep = 4u;
-      } else {  // FC1_DGRAD: W1 / W3 block (d-block of the row, kb mod f/128)
-        const int nbk = (ti.n0 + sidx) / 128;
-        o.sc_off = nbk < db ? (uint32_t)nbk * (uint32_t)fb * 4u : 0x40000000u;
+      } else if constexpr (MX) {
+        // B rows: the E8M0 bytes [E][n][K/32] of the weight in the orientation read
+        const int xb = (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? d / 32 : f / 32;
+        size_t b0;
+        int brows;
+        if constexpr (OP == OP_FC1_FWD) {
+          b0 = (e * f + ti.n0 / 2) * xb; brows = 128;
+        } else if constexpr (OP == OP_FC2_FWD) {
+          b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
+        } else if constexpr (OP == OP_FC2_DGRAD) {
+          b0 = (e * f + ti.n0) * xb; brows = f - ti.n0;
+        } else {
+          b0 = (e * d + ti.n0) * xb; brows = d - ti.n0;
+        }
+        const bool w3 = OP == OP_FC1_FWD && sidx >= 128;  // fc1 forward: B rows 128.. are W3's
+        o.sc_src = make_rsrc((w3 ? args.b_sx2 : args.b_sx) + b0, (uint32_t)brows * (uint32_t)xb);
+        if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_sx2 + b0, (uint32_t)brows * (uint32_t)xb);
+        o.sc_off = (uint32_t)((OP == OP_FC1_FWD) ? (sidx & 127) : sidx) * (uint32_t)xb;
         o.sc_kstep = 4u;
+      } else {
+        // B rows: e4m3 weight block scales, [E][d/128][f/128] (W1, W3) or
+        // [E][f/128][d/128] (W2); every B row of a 128-row block reads the same
+        // word (rows past N read past the range: zero)
+        const int db = d / 128, fb = f / 128;
+        const int nb = db * fb;
+        const float* s = (OP == OP_FC1_FWD && sidx >= 128) ? args.b_s2 : args.b_s;
+        o.sc_src = make_rsrc(s + e * (size_t)nb, (uint32_t)nb * 4u);
+        if constexpr (OP == OP_FC1_DGRAD) o.sc_src2 = make_rsrc(args.b_s2 + e * (size_t)nb, (uint32_t)nb * 4u);
+        if constexpr (OP == OP_FC1_FWD) {  // block (kb, f-block of the tile's W1 / W3 rows)
+          o.sc_off = (uint32_t)((ti.n0 / 2) / 128) * 4u;
+          o.sc_kstep = (uint32_t)fb * 4u;
+        } else if constexpr (OP == OP_FC2_FWD) {  // W2 block (kb, d-block of the row)
+          const int nbk = (ti.n0 + sidx) / 128;
+          o.sc_off = nbk < db ? (uint32_t)nbk * 4u : 0x40000000u;
+          o.sc_kstep = (uint32_t)db * 4u;
+        } else if constexpr (OP == OP_FC2_DGRAD) {  // W2 block (f-block of the row, kb)
+          const int nbk = (ti.n0 + sidx) / 128;
+          o.sc_off = nbk < fb ? (uint32_t)nbk * (uint32_t)db * 4u : 0x40000000u;
+          o.sc_kstep = 4u;
+        } else {  // FC1_DGRAD: W1 / W3 block (d-block of the row, kb mod f/128)
+          const int nbk = (ti.n0 + sidx) / 128;
+          o.sc_off = nbk < db ? (uint32_t)nbk * (uint32_t)fb * 4u : 0x40000000u;
+          o.sc_kstep = 4u;
+        }
       }
     }
     o.sc_src = uniform_rsrc(o.sc_src);
     o.sc_src2 = uniform_rsrc(o.sc_src2);
     o.sc_kstep = (uint32_t)uniform((int)o.sc_kstep);
+    o.KT = uniform(o.KT);
   };
 
-  // ---- DMA lane offsets: instruction t (0..15) of an operand covers tile
-  // rows 16 t .. 16 t + 15; lane -> row 16 t + lane / 4, stored chunk lane % 4
-  // holding logical chunk (lane % 4) ^ swz(row).  This wavefront issues
-  // t = 2 wid + q, q < 2, for A and for B.
+  // ---- DMA lane offsets.  Ragged M: instruction t (0..15) of an operand
+  // covers tile rows 16 t .. 16 t + 15; lane -> row 16 t + lane / 4, stored
+  // chunk lane % 4 holding logical chunk (lane % 4) ^ swz(row).  Weight
+  // gradients: instruction t covers k-rows 4 t .. 4 t + 3 (256 bytes each);
+  // lane -> k-row 4 t + lane / 16, stored 16-byte chunk p = lane % 16, i.e.
+  // half p & 1 of unit p / 2, holding logical unit (p / 2) ^ (k & 7).  This
+  // wavefront issues t = 2 wid + q, q < 2, for A and for B.
   uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
 #pragma unroll
   for (int q = 0; q < DMA_PER_WAVE; ++q) {
     const int t = wid * DMA_PER_WAVE + q;
-    const int row = 16 * t + (lane >> 2);
-    const uint32_t ch = (uint32_t)(((lane & 3) ^ swz(row)) << 4);
-    a_off[q] = (uint32_t)row * a_ld + ch;
-    const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
-    b_off[q] = (uint32_t)brow * b_ld + ch;
+    if constexpr (WG) {
+      const int k = 4 * t + (lane >> 4), p = lane & 15;
+      const uint32_t col = (uint32_t)((((p >> 1) ^ (k & 7)) << 5) | ((p & 1) << 4));
+      a_off[q] = (uint32_t)k * a_ld + col;
+      b_off[q] = (uint32_t)k * b_ld + col;
+    } else {
+      const int row = 16 * t + (lane >> 2);
+      const uint32_t ch = (uint32_t)(((lane & 3) ^ swz(row)) << 4);
+      a_off[q] = (uint32_t)row * a_ld + ch;
+      const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
+      b_off[q] = (uint32_t)brow * b_ld + ch;
+    }
   }
   const uint32_t lds_base =
       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)LDS_PTR(lds));
@@ -324,6 +424,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   tn = ti;
   nxt = cur;
   int phase = 0;       // ring slot of the current tile's stage 0
+  int bph = 0;         // weight gradients: block slot of the current tile's first block
   bool cross = false;  // stages past the current tile's last fetch the next tile's first three
 
   // DMA instruction Q of this wavefront for stage s of the stream, counted
@@ -341,12 +442,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       const int t = wid * DMA_PER_WAVE + q;
       rsrc_t r = pick(in_cur, cur.a_src, nxt.a_src);
       r[2] = live ? r[2] : 0;
-      dma16(uniform_rsrc(r), a_off[q] + k0, st_base + (uint32_t)(t * 1024));
+      dma16(uniform_rsrc(r), a_off[q] + (WG ? k0 * a_ld : k0), st_base + (uint32_t)(t * 1024));
     } else if constexpr (q == DMA_PER_WAVE) {
       // a 128-K block's words serve both of its stages and are loaded with
       // the first; the second stage's DMA reads nothing (a zero-length range:
-      // no memory request, and the zeros land in its own slot, which no one
-      // reads), so that every stage issues the same loads for the waits
+      // no memory request, and the zeros land in a slot that no one reads),
+      // so that every stage issues the same loads for the waits
       const int kb = kt >> 1;
       rsrc_t r;
       uint32_t voff;
@@ -363,7 +464,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         voff = soff + (uint32_t)kb * kstep;
       }
       r[2] = (live && (kt & 1) == 0) ? r[2] : 0;
-      dma4(uniform_rsrc(r), voff, sc_base + slot_s * SC_BYTES);
+      // weight gradients: the block's slot, or slot 3 for a block's second
+      // stage -- formed without a branch (a branch here splits the stage, and
+      // the compiler then sinks the first half's MFMAs below the barrier)
+      uint32_t sl;
+      if constexpr (WG)
+        sl = (uint32_t)((bph + (in_cur ? 0 : (cur.KT + 1) >> 1) + kb) % 3) | (3u * (uint32_t)(kt & 1));
+      else sl = slot_s;
+      dma4(uniform_rsrc(r), voff, sc_base + sl * SC_BYTES);
     } else {
       const int qq = q - DMA_PER_WAVE - 1;
       const int t = wid * DMA_PER_WAVE + qq;
@@ -380,16 +488,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         voff = b_off[qq] + (second ? k0 - (uint32_t)f : k0);
       } else {
         r = pick(in_cur, cur.b_src, nxt.b_src);
-        voff = b_off[qq] + k0;
+        voff = b_off[qq] + (WG ? k0 * b_ld : k0);
       }
       r[2] = live ? r[2] : 0;
       dma16(uniform_rsrc(r), voff, dst);
     }
   };
 
-  // ---- fragments: block ib of A = rows wm*WM + 32 ib + (lane & 31); block jb
-  // of B = rows b_row0(jb) + (lane & 31) (fc1 forward: W1 rows, then the same
-  // W3 rows); lane group h reads chunks h and h + 2
+  // ---- fragments.  Ragged M: block ib of A = rows wm*WM + 32 ib + (lane &
+  // 31); block jb of B = rows b_row0(jb) + (lane & 31) (fc1 forward: W1 rows,
+  // then the same W3 rows); lane group h reads chunks h and h + 2.  Weight
+  // gradients: block ib of A = columns wm*WM + 32 ib .. (LDS unit 4 wm + ib),
+  // block jb of B = columns wn*WN + 32 jb .. (unit 2 wn + jb), by frag_tr.
   const int lh = lane >> 5, l31 = lane & 31;
   auto b_row0 = [&](int jb) __attribute__((always_inline)) -> int {
     if constexpr (OP == OP_FC1_FWD) return jb * 128 + wn * (WN / 2);
@@ -402,18 +512,27 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     const i32x4_t hi = *(const __attribute__((address_space(3))) i32x4_t*)(p + fc1);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  // frag_tr lane address: k-row 16 h + (lane & 15) / 2 (of the first group),
+  // bytes 16 ((lane >> 4) & 1) + 8 (lane & 1) of the unit, whose stored position
+  // is u ^ ((lane & 15) / 2) (the k-row's low three bits)
+  const int ih = (lane & 15) >> 1;
+  const uint32_t tr_lane = (uint32_t)((16 * lh + ih) * 256 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1));
   auto read_a = [&](const char* st, int ib) __attribute__((always_inline)) -> i32x8_t {
-    return frag(st + (wm * WM + 32 * ib + l31) * BK);
+    if constexpr (WG) return frag_tr(st + tr_lane + (((4 * wm + ib) ^ ih) << 5));
+    else return frag(st + (wm * WM + 32 * ib + l31) * BK);
   };
   auto read_b = [&](const char* st, int jb) __attribute__((always_inline)) -> i32x8_t {
-    return frag(st + OPND_BYTES + (b_row0(jb) + l31) * BK);
+    if constexpr (WG) return frag_tr(st + OPND_BYTES + tr_lane + (((2 * wn + jb) ^ ih) << 5));
+    else return frag(st + OPND_BYTES + (b_row0(jb) + l31) * BK);
   };
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
     return lds + ((uint32_t)(phase + s) % NS) * STAGE_BYTES;
   };
   // the scale words of stage s: in the slot of its block's first stage
-  auto scale_ptr = [&](int s) __attribute__((always_inline)) -> const char* {
-    return sc_ring + ((uint32_t)(phase + (s & ~1)) % NS) * SC_BYTES;
+  // (weight gradients: its block's slot; b_back = 1: the block before)
+  auto scale_ptr = [&](int s, int b_back = 0) __attribute__((always_inline)) -> const char* {
+    if constexpr (WG) return sc_ring + ((bph + (s >> 1) + 3 - b_back) % 3) * SC_BYTES;
+    else return sc_ring + ((uint32_t)(phase + (s & ~1)) % NS) * SC_BYTES;
   };
 
   // ---------------------------------------------------------------- scales
@@ -421,19 +540,38 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // column scale), eb[jb] that of its B row (the row scale).  e4m3: the same
   // bytes packed into ea_pk (byte ib) and eb_pk (byte jb), taken by the MFMA's
   // byte select, and ma / mb, the mantissas the accumulators are in units of;
-  // every B row of a 128-row weight block has the same scale, so eb_pk and mb
-  // are uniform.
+  // in the ragged products every B row of a 128-row weight block has the same
+  // scale, so eb_pk and mb are uniform (the weight gradients keep the B-side
+  // mantissas in LDS instead, see nsc_ratio).
   i32x8_t af[IB], b0, b1;
   int ea[IB], eb[JB];
   int ea_pk = 0, eb_pk = 0;
   float ma[IB], mb[JB];
   f32x16_t acc[IB][JB];
+  // weight gradients, e4m3: the wavefront's 64 B-column values v (lane l:
+  // column wn*WN + l) traded through LDS and applied with the lane's A-side
+  // factors: acc[ib][jb][4 q + r] *= fa[ib] * v(32 jb + 8 q + 4 h + r)
+  auto apply_cols = [&](float v, const float (&fa)[IB]) __attribute__((always_inline)) {
+    nsc[wid * 64 + lane] = v;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wavefront's writes before its reads
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t vn = *(const f32x4_t*)&nsc[wid * 64 + 32 * jb + 8 * q + 4 * lh];
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ib][jb][4 * q + r] *= fa[ib] * vn[r];
+      }
+  };
   // The scales of stage kt; e4m3, at the first stage of a 128-K block: the
   // new exponents and mantissas, and the accumulators times u_old / u_new
   // (not at a tile's first stage, where they are zero).  Measured faster than
   // multiplying each block right before its first MFMA, which keeps the
   // factors in registers through the stage.
-  auto stage_scales = [&](int kt, const char* sc) __attribute__((always_inline)) {
+  auto stage_scales = [&](int kt) __attribute__((always_inline)) {
+    const char* sc = scale_ptr(kt);
     const uint32_t* wa = (const uint32_t*)sc;
     const uint32_t* wb = (const uint32_t*)(sc + 1024);
     if constexpr (MX) {
@@ -454,24 +592,35 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         ma[ib] = m;
       }
       eb_pk = 0;
+      if constexpr (WG) {
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
-        const float s = __uint_as_float((uint32_t)uniform((int)wb[b_row0(jb)]));
-        eb_pk |= e8_of(s) << (8 * jb);
-        const float m = mant_of(s);
-        rb[jb] = mb[jb] * __builtin_amdgcn_rcpf(m);
-        mb[jb] = m;
-      }
-      eb_pk = uniform(eb_pk);
-      if (kt > 0) {
+        for (int jb = 0; jb < JB; ++jb) eb_pk |= e8_of(__uint_as_float(wb[b_row0(jb) + l31])) << (8 * jb);
+        if (kt > 0) {
+          const uint32_t* wo = (const uint32_t*)(scale_ptr(kt, 1) + 1024);
+          const int n = wn * WN + lane;
+          apply_cols(mant_of(__uint_as_float(wo[n])) * __builtin_amdgcn_rcpf(mant_of(__uint_as_float(wb[n]))),
+                     ra);
+        }
+      } else {
 #pragma unroll
-        for (int ib = 0; ib < IB; ++ib)
+        for (int jb = 0; jb < JB; ++jb) {
+          const float s = __uint_as_float((uint32_t)uniform((int)wb[b_row0(jb)]));
+          eb_pk |= e8_of(s) << (8 * jb);
+          const float m = mant_of(s);
+          rb[jb] = mb[jb] * __builtin_amdgcn_rcpf(m);
+          mb[jb] = m;
+        }
+        eb_pk = uniform(eb_pk);
+        if (kt > 0) {
 #pragma unroll
-          for (int jb = 0; jb < JB; ++jb) {
-            const float g = ra[ib] * rb[jb];
+          for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) acc[ib][jb][x] *= g;
-          }
+            for (int jb = 0; jb < JB; ++jb) {
+              const float g = ra[ib] * rb[jb];
+#pragma unroll
+              for (int x = 0; x < 16; ++x) acc[ib][jb][x] *= g;
+            }
+        }
       }
     }
   };
@@ -497,7 +646,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // the reloads before the loop make every stage wait for all loads.)
   auto stage_body = [&](int kt, const char* __restrict__ st, const char* __restrict__ nst, auto TAIL)
       __attribute__((always_inline)) {
-    stage_scales(kt, scale_ptr(kt));
+    stage_scales(kt);
     b1 = read_b(st, 1);
     static_for<0, IB>([&](auto U) __attribute__((always_inline)) {
       constexpr int u = U.value;
@@ -567,7 +716,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 
     // ---------------------------------------------------------------- epilogue
     // e4m3: back from units of the last block's mantissas
-    if constexpr (!MX) {
+    if constexpr (!MX && WG) {
+      if (cur.KT > 0) {
+        const uint32_t* wl = (const uint32_t*)(scale_ptr(cur.KT - 1) + 1024);
+        apply_cols(mant_of(__uint_as_float(wl[wn * WN + lane])), ma);
+      }
+    } else if constexpr (!MX) {
 #pragma unroll
       for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
@@ -585,9 +739,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
         for (int jb = 0; jb < JB; ++jb)
           to_frags(acc[ib][jb], frg[2 * ib][2 * jb], frg[2 * ib][2 * jb + 1], frg[2 * ib + 1][2 * jb],
                    frg[2 * ib + 1][2 * jb + 1]);
-      store_tile<OP, 2 * IB, 2 * JB, WM, WN, true, RS>(args, frg, ti, ti.rows, N, wm, wn, lane, dp_red);
+      if constexpr (WG) store_tile<OP, 2 * IB, 2 * JB, WM, WN, false>(args, frg, ti, Mw, N, wm, wn, lane);
+      else store_tile<OP, 2 * IB, 2 * JB, WM, WN, true, RS>(args, frg, ti, ti.rows, N, wm, wn, lane, dp_red);
     }
     if (!have_next) break;
+    if constexpr (WG) bph = (bph + ((cur.KT + 1) >> 1)) % 3;
     if (cross) {
       phase = (int)((uint32_t)(phase + cur.KT) % NS);
       fresh = false;
@@ -608,9 +764,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
 
 template <int OP, bool MX>
 int launch(const GemmArgs& a, hipStream_t s) {
-  const int N = (OP == OP_FC1_FWD) ? 2 * a.f : (OP == OP_FC2_DGRAD ? a.f : a.d);
-  const int NT = (N + BN - 1) / BN;
-  int64_t grid = ((int64_t)a.P / BM + a.E) * NT;  // upper bound of the device-side tile count
+  constexpr bool WG = OP == OP_FC2_WGRAD || OP == OP_FC1_WGRAD;
+  int NT, MT = 0;
+  int64_t grid;
+  if constexpr (WG) {
+    const int M = (OP == OP_FC2_WGRAD) ? a.f : a.d;
+    const int N = (OP == OP_FC2_WGRAD) ? a.d : 2 * a.f;
+    MT = (M + BM - 1) / BM;
+    NT = (N + BN - 1) / BN;
+    grid = (int64_t)a.E * MT * NT;
+  } else {
+    const int N = (OP == OP_FC1_FWD) ? 2 * a.f : (OP == OP_FC2_DGRAD ? a.f : a.d);
+    NT = (N + BN - 1) / BN;
+    grid = ((int64_t)a.P / BM + a.E) * NT;  // upper bound of the device-side tile count
+  }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   // persistent blocks, one per compute unit (a multiple of 8), except fc2
@@ -624,11 +791,11 @@ int launch(const GemmArgs& a, hipStream_t s) {
   bool scaled = false;  // row-scaled variant: only fc1 forward and fc2 dgrad change
   if constexpr (OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) {
     if (a.row_prob) {
-      gemm_fp8_kernel<OP, MX, true><<<g, NW * 64, 0, s>>>(a, NT);
+      gemm_fp8_kernel<OP, MX, true><<<g, NW * 64, 0, s>>>(a, NT, MT);
       scaled = true;
     }
   }
-  if (!scaled) gemm_fp8_kernel<OP, MX, false><<<g, NW * 64, 0, s>>>(a, NT);
+  if (!scaled) gemm_fp8_kernel<OP, MX, false><<<g, NW * 64, 0, s>>>(a, NT, MT);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -641,8 +808,8 @@ int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
     case OP_FC2_FWD: return launch<OP_FC2_FWD, false>(a, s);
     case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, false>(a, s);
     case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, false>(a, s);
-    case OP_FC2_WGRAD:
-    case OP_FC1_WGRAD: return gemm_fp8_wgrad_launch(op, false, a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, false>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, false>(a, s);
   }
   return MOE_ERR_INVALID;
 }
@@ -653,8 +820,8 @@ int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s) {
     case OP_FC2_FWD: return launch<OP_FC2_FWD, true>(a, s);
     case OP_FC2_DGRAD: return launch<OP_FC2_DGRAD, true>(a, s);
     case OP_FC1_DGRAD: return launch<OP_FC1_DGRAD, true>(a, s);
-    case OP_FC2_WGRAD:
-    case OP_FC1_WGRAD: return gemm_fp8_wgrad_launch(op, true, a, s);
+    case OP_FC2_WGRAD: return launch<OP_FC2_WGRAD, true>(a, s);
+    case OP_FC1_WGRAD: return launch<OP_FC1_WGRAD, true>(a, s);
   }
   return MOE_ERR_INVALID;
 }

@@ -83,8 +83,10 @@ struct GemmArgs {
   //   ragged-M ops: A = a_q [P][K] with scales a_s [P][K/128]; B = weight
   //     codes laid out [n][k] (b_q, and b_q2 for the W3 half of fc1 products)
   //     with 128x128 block scales b_s, b_s2 as stored by the weight quantiser;
-  //   wgrad ops: A = a_q [M][ldt], B = b_q [N][ldt] (token blocks of the
-  //     expert start at column 128 * blk[e]) with scales a_s [NB][M], b_s [NB][N].
+  //   wgrad ops: A = a_q [P][M], B = b_q [P][N], row-major codes of the
+  //     permuted rows (MN-contiguous), with one scale per 128-row token block
+  //     of an expert and column: a_s [NB][M], b_s [NB][N], the expert's blocks
+  //     from row blk[e] on.
   const uint8_t* a_q;
   const float* a_s;
   const uint8_t* b_q;
@@ -92,7 +94,6 @@ struct GemmArgs {
   const float* b_s;
   const float* b_s2;
   const int32_t* blk;  // [E+1] token-block table (wgrad)
-  int64_t ldt;         // row length in bytes of the token-block operands (wgrad)
   // row-scaled products (probabilities applied before W2), bf16 only: the
   // routing probability of every permuted row, and the fc2 dgrad's partial
   // probability gradients [P][ceil(f/256)]
@@ -102,7 +103,7 @@ struct GemmArgs {
   // e4m3, with one scale byte per 32 contraction values, stored row-major per
   // operand row: A rows [.][K/32]; B: the byte array of each weight matrix in
   // the orientation read ([E][n][K/32]; fc1 forward and fc1 dgrad use b_sx2
-  // for W3).  Weight gradients: words [ldt/128][M] and [ldt/128][N], the four
+  // for W3).  Weight gradients: words [NB][M] and [NB][N], the four
   // 32-row scales of each 128-row token block and column.
   const uint8_t* a_sx;
   const uint8_t* b_sx;
@@ -123,9 +124,6 @@ int gemm_f32_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 int gemm_fp8_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
 // the same products with MXFP8 operands (hardware block-scaled MFMA)
 int gemm_mx_launch(GemmOp op, const GemmArgs& a, hipStream_t s);
-// gemm_fp8_wgrad.hip: the two weight gradients of both (mx: MXFP8), called
-// by gemm_fp8_launch / gemm_mx_launch
-int gemm_fp8_wgrad_launch(GemmOp op, bool mx, const GemmArgs& a, hipStream_t s);
 // Compute units of the current device rounded down to a multiple of 8 (the
 // grid of the persistent grouped-GEMM launches), or -1.
 int gemm_persistent_blocks();
@@ -144,11 +142,11 @@ int quant_rows_mx_launch(const void* src, bool src_f32, int64_t rows, int64_t co
 int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
                             uint8_t* sb, uint8_t* codes_t, uint8_t* sbt, hipStream_t s);
 int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
-                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
                            uint8_t* sbt, hipStream_t s);  // bound on sum_e ceil(m_e / 128)
 int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t s);
 int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
-                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
                         float* scales, hipStream_t s);
 // permute.hip: rows of e4m3 codes [T][d] and their scales [T][d/128]
 int permute_e4m3_launch(const uint8_t* codes, const float* scales, const int32_t* row_of, int T,

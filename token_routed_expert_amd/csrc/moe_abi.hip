@@ -82,7 +82,7 @@ Fwd8Ws carve_fwd8(const moe_shape* sh, void* ws, size_t* bytes) {
 }
 
 struct Bwd8Ws {
-  uint8_t *dOq, *dabq, *AT, *BT;
+  uint8_t *dOq, *dabq, *tokA, *tokB;
   float *dOs, *dabs, *sA, *sB;
   int32_t* blk;
   int64_t cap;
@@ -90,7 +90,6 @@ struct Bwd8Ws {
 Bwd8Ws carve_bwd8(const moe_shape* sh, void* ws, size_t* bytes) {
   const size_t P = (size_t)(sh->T * sh->k), d = (size_t)sh->d, f = (size_t)sh->f;
   const int64_t cap = tokblk_max_blocks((int64_t)P, sh->E);
-  const size_t Lt = 128 * (size_t)cap;
   const size_t ma = f > d ? f : d, mb = d > 2 * f ? d : 2 * f;
   Carver c{(char*)ws};
   Bwd8Ws w;
@@ -100,8 +99,8 @@ Bwd8Ws carve_bwd8(const moe_shape* sh, void* ws, size_t* bytes) {
   w.dabq = c.take<uint8_t>(P * 2 * f);
   w.dabs = c.take<float>(P * (2 * f / 128) * 4);
   w.blk = c.take<int32_t>((size_t)(sh->E + 1) * 4);
-  w.AT = c.take<uint8_t>(ma * Lt);
-  w.BT = c.take<uint8_t>(mb * Lt);
+  w.tokA = c.take<uint8_t>(P * ma);
+  w.tokB = c.take<uint8_t>(P * mb);
   w.sA = c.take<float>((size_t)cap * ma * 4);
   w.sB = c.take<float>((size_t)cap * mb * 4);
   *bytes = c.used;
@@ -158,9 +157,9 @@ int qrows8(const void* src, int64_t rows, int64_t cols, uint8_t* codes, void* sc
             : quant_rows_launch(src, false, rows, cols, codes, (float*)sc, s);
 }
 int qtok8(const void* src, const int32_t* src_row, const int32_t* offsets, const int32_t* blk,
-          int E, int64_t P, int64_t C, uint8_t* codes_t, void* sc, hipStream_t s, bool mx) {
-  return mx ? quant_tokblk_mx_launch(src, src_row, offsets, blk, E, P, C, codes_t, (uint8_t*)sc, s)
-            : quant_tokblk_launch(src, src_row, offsets, blk, E, P, C, codes_t, (float*)sc, s);
+          int E, int64_t P, int64_t C, uint8_t* codes, void* sc, hipStream_t s, bool mx) {
+  return mx ? quant_tokblk_mx_launch(src, src_row, offsets, blk, E, P, C, codes, (uint8_t*)sc, s)
+            : quant_tokblk_launch(src, src_row, offsets, blk, E, P, C, codes, (float*)sc, s);
 }
 
 int run_gemm(const moe_shape* sh, GemmOp op, const GemmArgs& a, hipStream_t s) {
@@ -314,15 +313,14 @@ int gemm_bwd8(const moe_shape* sh, const int32_t* offsets, const int32_t* token_
   // weight gradients on 128-row token blocks: dW2 = h^T dO, [dW1|dW3] = xp^T dab
   if ((st = tokblk_table_launch(offsets, (int)E, W.blk, s))) return st;
   a.blk = W.blk;
-  a.ldt = 128 * W.cap;
-  if ((st = qtok8(h, nullptr, offsets, W.blk, (int)E, P, f, W.AT, W.sA, s, mx))) return st;
-  if ((st = qtok8(dO, nullptr, offsets, W.blk, (int)E, P, d, W.BT, W.sB, s, mx))) return st;
-  a.a_q = W.AT; set_a_scales(a, W.sA, mx);
-  a.b_q = W.BT; a.b_q2 = nullptr; set_b_scales(a, W.sB, nullptr, mx);
+  if ((st = qtok8(h, nullptr, offsets, W.blk, (int)E, P, f, W.tokA, W.sA, s, mx))) return st;
+  if ((st = qtok8(dO, nullptr, offsets, W.blk, (int)E, P, d, W.tokB, W.sB, s, mx))) return st;
+  a.a_q = W.tokA; set_a_scales(a, W.sA, mx);
+  a.b_q = W.tokB; a.b_q2 = nullptr; set_b_scales(a, W.sB, nullptr, mx);
   a.dW2 = dW2;
   if ((st = gemm8(OP_FC2_WGRAD, a, s, mx))) return st;
-  if ((st = qtok8(x, token_of, offsets, W.blk, (int)E, P, d, W.AT, W.sA, s, mx))) return st;
-  if ((st = qtok8(dab, nullptr, offsets, W.blk, (int)E, P, 2 * f, W.BT, W.sB, s, mx))) return st;
+  if ((st = qtok8(x, token_of, offsets, W.blk, (int)E, P, d, W.tokA, W.sA, s, mx))) return st;
+  if ((st = qtok8(dab, nullptr, offsets, W.blk, (int)E, P, 2 * f, W.tokB, W.sB, s, mx))) return st;
   a.dW1 = dW1; a.dW3 = dW3;
   return gemm8(OP_FC1_WGRAD, a, s, mx);
 }
@@ -665,18 +663,18 @@ int64_t moe_token_block_capacity(int64_t P, int64_t E) {
 }
 
 int moe_quantize_token_blocks(const int32_t* offsets, int64_t E, int64_t P, const void* src,
-                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes_t,
+                              const int32_t* src_row, int64_t C, int32_t* blk, uint8_t* codes,
                               float* scales, void* stream) {
-  if (!offsets || !src || !blk || !codes_t || !scales) return MOE_ERR_INVALID;
+  if (!offsets || !src || !blk || !codes || !scales) return MOE_ERR_INVALID;
   if (E < 1 || P < 0 || C < 0) return MOE_ERR_INVALID;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (C % 128 != 0 || C >= (1 << 30) || P >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
-  // transposed rows are addressed with 32-bit offsets by the GEMMs
+  // the GEMMs address an expert's rows and scale blocks with 32-bit offsets
   if ((C + 256) * 128 * tokblk_max_blocks(P, E) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   int st = tokblk_table_launch(offsets, (int)E, blk, s);
   if (st) return st;
-  return quant_tokblk_launch(src, src_row, offsets, blk, (int)E, P, C, codes_t, scales, s);
+  return quant_tokblk_launch(src, src_row, offsets, blk, (int)E, P, C, codes, scales, s);
 }
 
 int moe_permute_e4m3(const moe_shape* sh, const uint8_t* codes, const float* scales,
@@ -776,8 +774,8 @@ int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uin
 
 int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
                                  const int32_t* src_row, int64_t C, int32_t* blk,
-                                 uint8_t* codes_t, uint8_t* scales, void* stream) {
-  if (!offsets || !src || !blk || !codes_t || !scales) return MOE_ERR_INVALID;
+                                 uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!offsets || !src || !blk || !codes || !scales) return MOE_ERR_INVALID;
   if (E < 1 || P < 0 || C < 0) return MOE_ERR_INVALID;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (C % 128 != 0 || C >= (1 << 30) || P >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
@@ -785,7 +783,7 @@ int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, c
   hipStream_t s = (hipStream_t)stream;
   int st = tokblk_table_launch(offsets, (int)E, blk, s);
   if (st) return st;
-  return quant_tokblk_mx_launch(src, src_row, offsets, blk, (int)E, P, C, codes_t, scales, s);
+  return quant_tokblk_mx_launch(src, src_row, offsets, blk, (int)E, P, C, codes, scales, s);
 }
 
 int moe_permute_mx(const moe_shape* sh, const uint8_t* codes, const uint8_t* scales,

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void tokblk_table_kernel(const int32_t* __rest
 // One block per (token block b, 128 columns cb): rows r0 .. r0 + nr - 1 of the
 // expert that owns block b (source row src_row[r] if src_row is given, else
 // r), columns cb*128 .. +127 of a bf16 [.][C] matrix.  Writes
-//   codes_t[c][128 b + i] for i < 128 (0 past the expert's rows), row length ldt;
+//   codes[r][c] for the block's rows r (row-major [P][C], as the source);
 //   scales[b][c].
 // Blocks with b >= blk[E] leave at once.  The grid is one-dimensional with cb
 // varying fastest: workgroups launched together read neighbouring 256-byte
@@ -269,12 +269,9 @@ __global__ __launch_bounds__(256) void tokblk_table_kernel(const int32_t* __rest
 //
 // Thread (rq, cg) = (tid / 16, tid % 16) holds rows 8 rq .. 8 rq + 7 and
 // columns 8 cg .. 8 cg + 7: a load instruction reads four 256-byte row
-// pieces, wavefront w holds rows 32 w .. 32 w + 31, and a column's eight row
-// codes leave the thread as one 8-byte LDS write into the transposed tile.
-// That tile, [column][row] with 128-byte rows, stores 16-byte unit u of
-// column c at unit u ^ (c / 8 mod 8), so the 8-byte writes of a wavefront
-// spread over 32 banks and the 16-byte row reads of the final stores over all.
-__device__ __forceinline__ int tokblk_unit(int c, int u) { return c * 128 + 16 * (u ^ ((c >> 3) & 7)); }
+// pieces, wavefront w holds rows 32 w .. 32 w + 31, and each row's eight
+// codes leave the thread as one 8-byte store (a wavefront's store covers four
+// 128-byte row pieces).
 
 // Owner expert of token block b: the last e with blk[e] <= b, which (blk being
 // non-decreasing with blk[0] = 0 <= b) is the number of e < E with
@@ -336,23 +333,11 @@ __device__ __forceinline__ void tokblk_load(const bf16_t* __restrict__ src,
   }
 }
 
-// The transposed tile to codes_t: column c's 128 codes as eight 16-byte stores.
-__device__ __forceinline__ void tokblk_store(const uint8_t* tt, uint8_t* __restrict__ dst,
-                                             int64_t ldt, int tid) {
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int id = pass * 256 + tid;
-    const int c = id >> 3, u = id & 7;
-    *(u32x4_t*)(dst + (size_t)c * ldt + 16 * u) = *(const u32x4_t*)&tt[tokblk_unit(c, u)];
-  }
-}
-
 __global__ __launch_bounds__(256) void quant_tokblk_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
-    int64_t ldt, uint8_t* __restrict__ codes_t, float* __restrict__ scales) {
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) float red[4][128];
-  __shared__ __attribute__((aligned(16))) uint8_t tt[128 * 128];
   const int ncb = C >> 7, b = (int)blockIdx.x / ncb, cb = (int)blockIdx.x - b * ncb;
   const int tid = threadIdx.x;
   if (b >= blk[E]) return;
@@ -393,24 +378,25 @@ __global__ __launch_bounds__(256) void quant_tokblk_kernel(
     *(f32x4_t*)so = f32x4_t{sc[0], sc[1], sc[2], sc[3]};
     *(f32x4_t*)(so + 4) = f32x4_t{sc[4], sc[5], sc[6], sc[7]};
   }
+  uint8_t* const dst = codes + (size_t)r0 * C + (size_t)cb * 128 + 8 * cg;
   auto emit = [&](auto fst) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int i = 0; i < 8; ++i) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= quant1s<decltype(fst)::value>(bf16_at(raw[i], q), sc[q], y[q], z[q]) << (8 * i);
-        hi |= quant1s<decltype(fst)::value>(bf16_at(raw[4 + i], q), sc[q], y[q], z[q]) << (8 * i);
+      for (int q = 0; q < 4; ++q) {
+        lo |= quant1s<decltype(fst)::value>(bf16_at(raw[i], q), sc[q], y[q], z[q]) << (8 * q);
+        hi |= quant1s<decltype(fst)::value>(bf16_at(raw[i], 4 + q), sc[4 + q], y[4 + q], z[4 + q])
+              << (8 * q);
       }
-      *(uint2*)&tt[tokblk_unit(8 * cg + q, rq >> 1) + 8 * (rq & 1)] = make_uint2(lo, hi);
+      const int r = 8 * rq + i;
+      if (r < nr) *(uint2*)(dst + (size_t)r * C) = make_uint2(lo, hi);
     }
   };
   if (__all(fast))
     emit(std::true_type{});
   else
     emit(std::false_type{});
-  __syncthreads();
-  tokblk_store(tt, codes_t + (size_t)cb * 128 * ldt + (size_t)b * 128, ldt, tid);
 }
 
 // ================================================================ MXFP8
@@ -561,8 +547,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void q
 }
 
 // Token blocks in MX form: as quant_tokblk_kernel, with four 32-row scale
-// blocks per column in each 128-row block.  codes_t [C][ldt] as there; scale
-// bytes sbt [ldt / 128][C][4]: byte g of word (b, c) for rows 32 g .. 32 g + 31
+// blocks per column in each 128-row block.  codes [P][C] as there; scale
+// bytes sbt [NB][C][4]: byte g of word (b, c) for rows 32 g .. 32 g + 31
 // of block b (groups past the expert's rows: s = 0) -- one 4-byte word per
 // (block, column), block-major like the e4m3 token-block scales, so a GEMM
 // stage's words for 256 columns are 1 KB in a row.  With the thread layout of
@@ -571,9 +557,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void q
 __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
-    int64_t ldt, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ sbt) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ sbt) {
   __shared__ __attribute__((aligned(4))) uint8_t cs[128][4];  // [column][group]
-  __shared__ __attribute__((aligned(16))) uint8_t tt[128 * 128];
   const int ncb = C >> 7, b = (int)blockIdx.x / ncb, cb = (int)blockIdx.x - b * ncb;
   const int tid = threadIdx.x;
   if (b >= blk[E]) return;
@@ -584,24 +569,30 @@ __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
   u32x4_t raw[8];
   float m[8];
   tokblk_load(src, src_row, r0, nr, C, cb, rq, cg, raw, m);
+  float inv[8];
+  bool z[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int s = mx_exp(m[q]);
-    const float inv = mx_inv(s);
-    const bool z = m[q] == 0.0f;
+    inv[q] = mx_inv(s);
+    z[q] = m[q] == 0.0f;
+    if ((tid & 63) < 16) cs[8 * cg + q][g] = (uint8_t)(s + 127);
+  }
+  uint8_t* const dst = codes + (size_t)r0 * C + (size_t)cb * 128 + 8 * cg;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= mx_code(bf16_at(raw[i], q), inv, z) << (8 * i);
-      hi |= mx_code(bf16_at(raw[4 + i], q), inv, z) << (8 * i);
+    for (int q = 0; q < 4; ++q) {
+      lo |= mx_code(bf16_at(raw[i], q), inv[q], z[q]) << (8 * q);
+      hi |= mx_code(bf16_at(raw[i], 4 + q), inv[4 + q], z[4 + q]) << (8 * q);
     }
-    *(uint2*)&tt[tokblk_unit(8 * cg + q, rq >> 1) + 8 * (rq & 1)] = make_uint2(lo, hi);
-    if ((tid & 63) < 16) cs[8 * cg + q][g] = (uint8_t)(s + 127);
+    const int r = 8 * rq + i;
+    if (r < nr) *(uint2*)(dst + (size_t)r * C) = make_uint2(lo, hi);
   }
   __syncthreads();
   if (tid < 128)
     *(uint32_t*)&sbt[((size_t)b * C + (size_t)cb * 128 + tid) * 4] = *(const uint32_t*)&cs[tid][0];
-  tokblk_store(tt, codes_t + (size_t)cb * 128 * ldt + (size_t)b * 128, ldt, tid);
 }
 
 }  // namespace
@@ -631,13 +622,13 @@ int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uin
 }
 
 int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
-                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                           const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
                            uint8_t* sbt, hipStream_t s) {
   const int64_t nb = tokblk_max_blocks(P, E);
   if (nb == 0) return MOE_OK;
   if (nb * (C / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // one block per (b, cb)
   quant_tokblk_mx_kernel<<<dim3((unsigned)(nb * (C / 128))), 256, 0, s>>>(
-      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, nb * 128, codes_t, sbt);
+      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, codes, sbt);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -675,13 +666,13 @@ int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t
 }
 
 int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
-                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes_t,
+                        const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
                         float* scales, hipStream_t s) {
   const int64_t nb = tokblk_max_blocks(P, E);
   if (nb == 0) return MOE_OK;
   if (nb * (C / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // one block per (b, cb)
   quant_tokblk_kernel<<<dim3((unsigned)(nb * (C / 128))), 256, 0, s>>>(
-      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, nb * 128, codes_t, scales);
+      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, codes, scales);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -146,12 +146,12 @@ def moe_token_block_capacity(P, E) -> int:
     return int(N.lib().moe_token_block_capacity(int(P), int(E)))
 
 
-def moe_quantize_token_blocks(offsets, E, P, src, src_row, blk, codes_t, scales, stream=None):
-    """Per-expert 128-row e4m3 blocks of a bf16 [.][C] matrix, written transposed."""
+def moe_quantize_token_blocks(offsets, E, P, src, src_row, blk, codes, scales, stream=None):
+    """Per-expert 128-row e4m3 blocks of a bf16 [.][C] matrix: codes [P][C], scales [cap][C]."""
     Cc = src.shape[1]
     _check(N.lib().moe_quantize_token_blocks(_ptr(offsets, I32), int(E), int(P), _ptr(src),
                                              _ptr(src_row, I32), Cc, _ptr(blk, I32),
-                                             _ptr(codes_t), _ptr(scales, F32), _stream(stream)),
+                                             _ptr(codes), _ptr(scales, F32), _stream(stream)),
            "moe_quantize_token_blocks")
 
 
@@ -214,12 +214,12 @@ def moe_quantize_weights_mx(W, codes, scales, codes_t, scales_t, stream=None):
            "moe_quantize_weights_mx")
 
 
-def moe_quantize_token_blocks_mx(offsets, E, P, src, src_row, blk, codes_t, scales, stream=None):
-    """Per-expert token blocks with 32-row MXFP8 scale blocks, written transposed."""
+def moe_quantize_token_blocks_mx(offsets, E, P, src, src_row, blk, codes, scales, stream=None):
+    """Per-expert token blocks with 32-row MXFP8 scale blocks: codes [P][C], bytes [cap][C][4]."""
     Cc = src.shape[1]
     _check(N.lib().moe_quantize_token_blocks_mx(_ptr(offsets, I32), int(E), int(P), _ptr(src),
                                                 _ptr(src_row, I32), Cc, _ptr(blk, I32),
-                                                _ptr(codes_t, U8), _ptr(scales, U8),
+                                                _ptr(codes, U8), _ptr(scales, U8),
                                                 _stream(stream)), "moe_quantize_token_blocks_mx")
 
 
