@@ -4,7 +4,7 @@
 * codes: lossless on inputs built on the grid (every 32-value block holds
   e4m3 values times 2^s with its largest magnitude in (224, 448] * 2^s),
   within half an e4m3 step of the block scale otherwise, never saturated;
-* layouts: both weight orientations and the padded token-block layout against
+* layouts: both weight orientations and the per-expert token-block layout against
   a per-block construction by hand;
 * products: on grid inputs whose block exponents differ from block to block,
   every MXFP8 product equals the plain fp64 product of oracle/moe.py exactly,
@@ -119,8 +119,9 @@ def test_token_block_layout():
     compare with quant_mx_rows on the block's values, built here by slicing."""
     off = small_offsets()
     P, C = int(off[-1]), 64
-    X = RNG.standard_normal((P, C)).astype(np.float32)
+    X = np.random.default_rng(7).standard_normal((P, C)).astype(np.float32)
     X[100:132, 5] = 0.0                                      # an all-zero block (expert 2's first)
+    X[224:228] *= 1000.0                                     # expert 2's last rows: large values
     q, sb = quant_mx_token_blocks(X, off)
     b32 = token_block_offsets(off, 32)
     assert q.shape == (P, C) and sb.shape == (int(b32[-1]), C)
@@ -140,6 +141,7 @@ def test_token_block_layout():
     assert np.abs(D - X).max() <= np.abs(X).max() * 2.0 ** -4
     # blocks restart at each expert: expert 3 (rows 228..260) has blocks
     # 228..259 and 260, not the fixed-stride blocks 224..255 and 256..287
+    # (whose scales the large rows 224..227 of expert 2 would raise)
     assert off[3] == 228 and off[4] == 261
     alt_q, alt_s = quant_mx_rows(np.ascontiguousarray(X[224:256].T))
     assert not (np.array_equal(sb[8], alt_s[:, 0]) and np.array_equal(q[228:256], alt_q.T[4:]))
