@@ -338,7 +338,8 @@ int moe_layer_bwd(const moe_shape* sh, const moe_layer_io* io, void* ws, size_t 
 /* Quantised expert weights as written by moe_quantize_weights. */
 typedef struct moe_e4m3_weights {
   const uint8_t *W1, *W3, *W2;    /* codes [E][d][f], [E][d][f], [E][f][d] */
-  const uint8_t *W1t, *W3t, *W2t; /* transposed codes [E][f][d], [E][f][d], [E][d][f] */
+  const uint8_t *W1t, *W3t, *W2t; /* not read (may be NULL): the products take every weight in the
+                                     orientation above, the forward ones MN-contiguous */
   const float *W1s, *W3s, *W2s;   /* tile scales [E][d/128][f/128] (W1, W3), [E][f/128][d/128] (W2) */
 } moe_e4m3_weights;
 

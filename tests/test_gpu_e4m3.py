@@ -124,6 +124,10 @@ def test_quantize_weights_bit_exact():
     scales = torch.empty(E, R // 128, C // 128, dtype=torch.float32, device="cuda")
     tre.moe_quantize_weights(Wt, codes, codes_t, scales)
     rq, rs = oracle.quant_expert_weights(W)
+    # without the transposed copy (what the layer writes): the same codes
+    codes1 = torch.empty_like(codes)
+    tre.moe_quantize_weights(Wt, codes1, None, torch.empty_like(scales))
+    assert torch.equal(codes1, codes)
     assert np.array_equal(u8(codes), rq)
     assert np.array_equal(u8(codes_t), rq.transpose(0, 2, 1))
     assert np.array_equal(f32bits(scales), np32bits(rs))
@@ -219,7 +223,7 @@ def check_layer_e4m3(wl, inp, b, tol=TOL8):
     for n in ("W1", "W3", "W2"):
         rq, rs = oracle.quant_expert_weights(inp[n].cpu().numpy())
         assert np.array_equal(u8(wq[n]), rq), n
-        assert np.array_equal(u8(wq[n + "t"]), rq.transpose(0, 2, 1)), n + "t"
+        assert wq[n + "t"] is None            # the products read one orientation
         assert np.array_equal(f32bits(wq[n + "s"]), np32bits(rs)), n + "s"
         Wd[n] = oracle.dequant_expert_weights(rq, rs)
     f = wl.f
@@ -337,7 +341,6 @@ def test_layer_e4m3_full_size_sampled():
         for n in ("W1", "W3", "W2"):
             rq, rs = oracle.quant_tiles(inp[n][e].cpu().numpy())
             assert np.array_equal(u8(wq[n][e]), rq), n
-            assert np.array_equal(u8(wq[n + "t"][e]), rq.T), n + "t"
             assert np.array_equal(f32bits(wq[n + "s"][e]), np32bits(rs)), n + "s"
             Wd[n] = oracle.dequant_tiles(rq, rs)[None]
         ab = to_f64(b["ab"][r0:r1]); a_g, b_g = ab[:, :f], ab[:, f:]

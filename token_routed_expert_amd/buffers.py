@@ -70,15 +70,17 @@ def layer_buffers(T, d, E, k, f, f_shared=0, dtype="bf16", device="cuda", inputs
     return sh, b, ws_f, ws_b
 
 
-def quantized_weights(W1, W3, W2, stream=None) -> E4M3Weights:
-    """e4m3 codes, transposed codes and 128 x 128 scales of fp32 expert weights
-    (W1, W3 [E][d][f], W2 [E][f][d]), made by moe_quantize_weights."""
+def quantized_weights(W1, W3, W2, stream=None, transposed=False) -> E4M3Weights:
+    """e4m3 codes and 128 x 128 scales of fp32 expert weights (W1, W3
+    [E][d][f], W2 [E][f][d]), made by moe_quantize_weights; transposed=True
+    also writes the transposed codes (which the products do not read)."""
     E, d, f = W1.shape
     dev = W1.device
     t = {}
     for name, W, R, Cc in (("W1", W1, d, f), ("W3", W3, d, f), ("W2", W2, f, d)):
         t[name] = torch.empty(E, R, Cc, dtype=torch.uint8, device=dev)
-        t[name + "t"] = torch.empty(E, Cc, R, dtype=torch.uint8, device=dev)
+        if transposed:
+            t[name + "t"] = torch.empty(E, Cc, R, dtype=torch.uint8, device=dev)
         t[name + "s"] = torch.empty(E, R // 128, Cc // 128, dtype=torch.float32, device=dev)
     wq = E4M3Weights(t)
     requantize_weights(wq, W1, W3, W2, stream)
@@ -93,7 +95,7 @@ def requantize_weights(wq, W1, W3, W2, stream=None):
             moe_quantize_weights_mx(W, wq[name], wq[name + "s"], wq[name + "t"], wq[name + "ts"],
                                     stream)
         else:
-            moe_quantize_weights(W, wq[name], wq[name + "t"], wq[name + "s"], stream)
+            moe_quantize_weights(W, wq[name], wq[name + "t"], wq[name + "s"], stream)  # t may be None
 
 
 def quantized_weights_mx(W1, W3, W2, stream=None) -> MXWeights:

@@ -20,6 +20,12 @@
 //   FC2_DGRAD   dO codes [P][d]              W2 codes [f][d]            d
 //   FC1_DGRAD   dab codes [P][2f]            W1 | W3 codes [d][f]       2f
 //
+// (e4m3 forward products: B is read in the weights' own orientation instead,
+// MN-contiguous -- W1, W3 [d][f] and W2 [f][d] -- as the weight gradients
+// read their operands: a 128 x 128 scale block holds for both orientations,
+// so the weight quantiser writes one copy.  MXFP8 scales run along the
+// contraction, so its forward products keep the transposed codes.)
+//
 // The weight gradients contract over an expert's rows and read both operands
 // in their row-major form, MN-contiguous (C[m][n] = sum_k A[k][m] B[k][n]),
 // with one scale per 128-row token block and column:
@@ -118,6 +124,15 @@ __device__ __forceinline__ i32x8_t frag_tr(const char* p) {
   return i32x8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
+// The same from 128-byte k-rows (fc1 forward's W1 and W3 halves, 64 k-rows
+// of 128 bytes each; unit u of k-row k at u ^ ((k >> 1) & 3), which spreads a
+// half-wavefront's 8 k-rows x 32 bytes over all 64 banks).
+__device__ __forceinline__ i32x8_t frag_tr_half(const char* p) {
+  const i32x2_t r0 = lds_tr8(p), r1 = lds_tr8(p + 8 * 128), r2 = lds_tr8(p + 32 * 128),
+                r3 = lds_tr8(p + 40 * 128);
+  return i32x8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
 // e4m3 x e4m3 32x32x64 block product into c; sa scales the MFMA's rows (the
 // B operand), sb its columns (the A operand), both E8M0.
 template <int SEL_A = 0, int SEL_B = 0>
@@ -200,6 +215,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 64
   constexpr int IB = WM / 32, JB = WN / 32;      // 4 x 2 blocks of 32 x 32
   constexpr bool WG = OP == OP_FC2_WGRAD || OP == OP_FC1_WGRAD;
+  // B read MN-contiguous: the weight gradients, and the e4m3 forward products
+  // (weights in their own orientation); fc1 forward's B is two 128-column
+  // halves (W1 and W3), each stored [64 k][128 bytes]
+  constexpr bool BMN = WG || (!MX && (OP == OP_FC1_FWD || OP == OP_FC2_FWD));
+  constexpr bool BHALF = BMN && OP == OP_FC1_FWD;
   constexpr int DMA_STEP = 4 / DMA_PER_WAVE;     // MFMA steps per DMA instruction
   static_assert(IB == 4 && JB == 2 && DMA_STEP == 2, "tile shape");
   static_assert(!(WG && RS), "row-scaled epilogues are ragged-M only");
@@ -265,7 +285,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
   // gradients, of the MN-contiguous k-rows
   const uint32_t a_ld = WG ? (uint32_t)Mw : (uint32_t)Kr;
   const uint32_t b_ld = WG ? (uint32_t)N
-                           : ((OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)d : (uint32_t)f);
+                           : (BMN ? (OP == OP_FC1_FWD ? (uint32_t)f : (uint32_t)d)
+                                  : ((OP == OP_FC1_FWD || OP == OP_FC2_DGRAD) ? (uint32_t)d : (uint32_t)f));
   const int kbr = Kr / 128;  // 128-K blocks per row
 
   // Per tile: buffer resources over what the tile reads (rows past an
@@ -309,7 +330,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     } else {
       o.a_src = make_rsrc(args.a_q + (size_t)ti.row0 * Kr, (uint32_t)ti.rows * a_ld);
       o.KT = Kr / BK;
-      if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
+      if constexpr (BMN && OP == OP_FC1_FWD) {  // W1 / W3 [d][f] from column n0/2
+        const size_t off = e * (size_t)d * f + (size_t)(ti.n0 / 2);
+        o.b_src = make_rsrc(args.b_q + off, (uint32_t)d * b_ld - (uint32_t)(ti.n0 / 2));
+        o.b_src2 = make_rsrc(args.b_q2 + off, (uint32_t)d * b_ld - (uint32_t)(ti.n0 / 2));
+      } else if constexpr (BMN && OP == OP_FC2_FWD) {  // W2 [f][d] from column n0
+        o.b_src = make_rsrc(args.b_q + e * (size_t)f * d + (size_t)ti.n0, (uint32_t)f * b_ld - (uint32_t)ti.n0);
+        o.b_src2 = o.b_src;
+      } else if constexpr (OP == OP_FC1_FWD) {  // W1^T / W3^T rows n0/2 .. +128
         const size_t off = e * (size_t)f * d + (size_t)(ti.n0 / 2) * d;
         o.b_src = make_rsrc(args.b_q + off, 128u * b_ld);
         o.b_src2 = make_rsrc(args.b_q2 + off, 128u * b_ld);
@@ -407,8 +435,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       const int row = 16 * t + (lane >> 2);
       const uint32_t ch = (uint32_t)(((lane & 3) ^ swz(row)) << 4);
       a_off[q] = (uint32_t)row * a_ld + ch;
-      const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
-      b_off[q] = (uint32_t)brow * b_ld + ch;
+      if constexpr (BHALF) {
+        // instruction t: half t / 8 (W1, W3), k-rows 8 (t % 8) .. + 7 of 128
+        // bytes; lane -> k-row 8 (t % 8) + lane / 8, stored 16-byte chunk
+        // p = lane % 8, i.e. half p & 1 of unit p / 2, holding logical unit
+        // (p / 2) ^ ((k / 2) & 3)
+        const int k = 8 * (t & 7) + (lane >> 3), p = lane & 7;
+        b_off[q] = (uint32_t)k * b_ld + (uint32_t)((((p >> 1) ^ ((k >> 1) & 3)) << 5) | ((p & 1) << 4));
+      } else if constexpr (BMN) {
+        const int k = 4 * t + (lane >> 4), p = lane & 15;
+        b_off[q] = (uint32_t)k * b_ld + (uint32_t)((((p >> 1) ^ (k & 7)) << 5) | ((p & 1) << 4));
+      } else {
+        const int brow = (OP == OP_FC1_FWD) ? (row & 127) : row;  // fc1: rows 128.. come from W3
+        b_off[q] = (uint32_t)brow * b_ld + ch;
+      }
     }
   }
   const uint32_t lds_base =
@@ -481,14 +521,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
       if constexpr (OP == OP_FC1_FWD) {
         const bool second = t >= 8;
         r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
-        voff = b_off[qq] + k0;
+        voff = b_off[qq] + (BMN ? k0 * b_ld : k0);
       } else if constexpr (OP == OP_FC1_DGRAD) {
         const bool second = (int)k0 >= f;
         r = pick(in_cur, pick(second, cur.b_src2, cur.b_src), pick(second, nxt.b_src2, nxt.b_src));
         voff = b_off[qq] + (second ? k0 - (uint32_t)f : k0);
       } else {
         r = pick(in_cur, cur.b_src, nxt.b_src);
-        voff = b_off[qq] + (WG ? k0 * b_ld : k0);
+        voff = b_off[qq] + (BMN ? k0 * b_ld : k0);
       }
       r[2] = live ? r[2] : 0;
       dma16(uniform_rsrc(r), voff, dst);
@@ -521,8 +561,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(GemmArgs args, int
     if constexpr (WG) return frag_tr(st + tr_lane + (((4 * wm + ib) ^ ih) << 5));
     else return frag(st + (wm * WM + 32 * ib + l31) * BK);
   };
+  // fc1 forward's halves: k-row 16 h + (lane & 15) / 2 of 128 bytes, unit
+  // position wn ^ ((lane & 15) / 4) (the k-row's bits 1..2), the same bytes
+  const uint32_t trh_lane = (uint32_t)((16 * lh + ih) * 128 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1));
   auto read_b = [&](const char* st, int jb) __attribute__((always_inline)) -> i32x8_t {
-    if constexpr (WG) return frag_tr(st + OPND_BYTES + tr_lane + (((2 * wn + jb) ^ ih) << 5));
+    if constexpr (BHALF) return frag_tr_half(st + OPND_BYTES + jb * 8192 + trh_lane + ((wn ^ (ih >> 1)) << 5));
+    else if constexpr (BMN) return frag_tr(st + OPND_BYTES + tr_lane + (((2 * wn + jb) ^ ih) << 5));
     else return frag(st + OPND_BYTES + (b_row0(jb) + l31) * BK);
   };
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> const char* {

@@ -119,7 +119,9 @@ size_t bwd8_ws_bytes(const moe_shape* sh) {
 }
 
 bool weights_ok(const moe_e4m3_weights* w) {
-  return w && w->W1 && w->W3 && w->W2 && w->W1t && w->W3t && w->W2t && w->W1s && w->W3s && w->W2s;
+  // (the transposed codes W1t, W3t, W2t are not read: the forward products take
+  // B in the weights' own orientation)
+  return w && w->W1 && w->W3 && w->W2 && w->W1s && w->W3s && w->W2s;
 }
 bool weights_ok(const moe_mx_weights* w) {
   return w && w->W1 && w->W3 && w->W2 && w->W1t && w->W3t && w->W2t && w->W1s && w->W3s &&
@@ -266,14 +268,16 @@ int gemm_fwd8(const moe_shape* sh, const int32_t* offsets, const uint8_t* xpq, c
   const int64_t P = sh->T * sh->k;
   GemmArgs a = expert_args(sh, offsets);
   a.a_q = xpq; set_a_scales(a, xps, mx);
-  a.b_q = w.W1t; a.b_q2 = w.W3t; set_b_scales(a, w.s1t, w.s3t, mx);
+  // B: MXFP8 the transposed codes (its scale blocks run along the contraction);
+  // e4m3 the codes in their own orientation, read MN-contiguous
+  a.b_q = mx ? w.W1t : w.W1; a.b_q2 = mx ? w.W3t : w.W3; set_b_scales(a, w.s1t, w.s3t, mx);
   a.ab_out = ab; a.h_out = h;
   a.row_prob = row_prob;
   if ((st = gemm8(OP_FC1_FWD, a, s, mx))) return st;
   a.row_prob = nullptr;
   if ((st = qrows8(h, P, sh->f, W.hq, W.hs, s, mx))) return st;
   a.a_q = W.hq; set_a_scales(a, W.hs, mx);
-  a.b_q = w.W2t; a.b_q2 = nullptr; set_b_scales(a, w.s2t, nullptr, mx);
+  a.b_q = mx ? w.W2t : w.W2; a.b_q2 = nullptr; set_b_scales(a, w.s2t, nullptr, mx);
   a.o_out = o;
   return gemm8(OP_FC2_FWD, a, s, mx);
 }

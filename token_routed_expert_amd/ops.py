@@ -170,8 +170,10 @@ class E4M3Weights:
     NAMES = ("W1", "W3", "W2", "W1t", "W3t", "W2t", "W1s", "W3s", "W2s")
 
     def __init__(self, tensors: dict):
-        self.tensors = {n: tensors[n] for n in self.NAMES}
-        self.struct = N.moe_e4m3_weights(*[_ptr(self.tensors[n]).value for n in self.NAMES])
+        # the transposed codes (W1t, W3t, W2t) are optional: the library does not read them
+        self.tensors = {n: tensors.get(n) for n in self.NAMES}
+        self.struct = N.moe_e4m3_weights(*[(_ptr(self.tensors[n]) or C.c_void_p(0)).value
+                                           for n in self.NAMES])
 
     def __getitem__(self, name):
         return self.tensors[name]
