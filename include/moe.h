@@ -385,6 +385,19 @@ int moe_quantize_token_blocks(const int32_t* offsets, int64_t E, int64_t P, cons
                               float* scales, void* stream);
 
 /*
+ * moe_quantize_token_blocks_with_rows -- moe_quantize_token_blocks and, in
+ * the same pass over the matrix, moe_quantize_rows of its rows: row_codes
+ * uint8 [P][C] and row_scales fp32 [P][C/128], bit-identical to
+ * moe_quantize_rows (the backward's dO and [da db] feed both a data gradient
+ * and a weight gradient, German §2 E / French §2 E).  Arguments and errors as
+ * moe_quantize_token_blocks; row_codes and row_scales must not be NULL.
+ */
+int moe_quantize_token_blocks_with_rows(const int32_t* offsets, int64_t E, int64_t P,
+                                        const void* src, const int32_t* src_row, int64_t C,
+                                        int32_t* blk, uint8_t* codes, float* scales,
+                                        uint8_t* row_codes, float* row_scales, void* stream);
+
+/*
  * moe_permute_e4m3 -- moe_permute for rows of e4m3 codes: codes [T][d] and
  * their scales [T][d/128] (from moe_quantize_rows of x) are copied bit for
  * bit to dst_codes [P][d] and dst_scales [P][d/128] at row row_of[t][j];
@@ -588,6 +601,14 @@ int moe_quantize_weights_mx(const float* W, int64_t E, int64_t R, int64_t C, uin
 int moe_quantize_token_blocks_mx(const int32_t* offsets, int64_t E, int64_t P, const void* src,
                                  const int32_t* src_row, int64_t C, int32_t* blk,
                                  uint8_t* codes, uint8_t* scales, void* stream);
+
+/* moe_quantize_token_blocks_with_rows_mx -- moe_quantize_token_blocks_mx and,
+ * in the same pass, moe_quantize_rows_mx of its rows: row_codes uint8 [P][C],
+ * row_scales E8M0 bytes [P][C/32], bit-identical to moe_quantize_rows_mx. */
+int moe_quantize_token_blocks_with_rows_mx(const int32_t* offsets, int64_t E, int64_t P,
+                                           const void* src, const int32_t* src_row, int64_t C,
+                                           int32_t* blk, uint8_t* codes, uint8_t* scales,
+                                           uint8_t* row_codes, uint8_t* row_scales, void* stream);
 
 /* moe_permute_mx -- moe_permute_e4m3 for MXFP8 rows: codes [T][d] and scale
  * bytes [T][d/32] moved to the permuted order (bit copies). */

@@ -266,3 +266,22 @@ def test_probe_mfma_validation():
     assert lib.moe_probe_mfma(N.MOE_BF16, 1 << 25, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_INVALID
     assert lib.moe_probe_mfma(N.MOE_F32, 16, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_UNSUPPORTED
     assert lib.moe_probe_mfma(N.MOE_MXFP8, 16, P, P, C.byref(f), C.byref(khz), None) == N.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["moe_quantize_token_blocks", "moe_quantize_token_blocks_mx",
+                                  "moe_quantize_token_blocks_with_rows",
+                                  "moe_quantize_token_blocks_with_rows_mx"])
+def test_token_block_quantiser_validation(name):
+    """The token-block quantisers (with or without the row blocks) check their
+    arguments before they touch the device."""
+    fn = getattr(N.lib(), name)
+    rows = name.endswith("with_rows") or name.endswith("with_rows_mx")
+    extra = (P, P) if rows else ()
+    assert fn(None, 8, 1024, P, None, 256, P, P, P, *extra, None) == N.MOE_ERR_INVALID
+    assert fn(P, 8, 1024, P, None, 256, P, None, P, *extra, None) == N.MOE_ERR_INVALID
+    assert fn(P, 0, 1024, P, None, 256, P, P, P, *extra, None) == N.MOE_ERR_INVALID
+    assert fn(P, 8, 1024, P, None, 200, P, P, P, *extra, None) == N.MOE_ERR_UNSUPPORTED
+    assert fn(P, 300, 1024, P, None, 256, P, P, P, *extra, None) == N.MOE_ERR_UNSUPPORTED
+    if rows:
+        assert fn(P, 8, 1024, P, None, 256, P, P, P, None, P, None) == N.MOE_ERR_INVALID
+        assert fn(P, 8, 1024, P, None, 256, P, P, P, P, None, None) == N.MOE_ERR_INVALID

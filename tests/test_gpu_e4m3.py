@@ -167,6 +167,19 @@ def test_quantize_token_blocks_bit_exact(gather):
     assert np.array_equal(f32bits(scales)[:NB], np32bits(rs))
     # codes in the matrix's own row-major layout: every row written
     assert np.array_equal(u8(codes), rq)
+    # the same pass with the row blocks: token blocks unchanged, rows as moe_quantize_rows
+    codes2 = torch.full((P, C), 0xAB, dtype=torch.uint8, device="cuda")
+    scales2 = torch.empty(cap, C, dtype=torch.float32, device="cuda")
+    rcodes = torch.full((P, C), 0xCD, dtype=torch.uint8, device="cuda")
+    rscales = torch.empty(P, C // 128, dtype=torch.float32, device="cuda")
+    tre.moe_quantize_token_blocks_with_rows(
+        torch.from_numpy(off).cuda(), E, P, src.cuda(),
+        None if src_row is None else torch.from_numpy(src_row).cuda(), blk, codes2, scales2,
+        rcodes, rscales)
+    assert torch.equal(codes2, codes) and torch.equal(scales2[:NB], scales[:NB])
+    rowq, rows_s = oracle.quant_rows(vals)
+    assert np.array_equal(u8(rcodes), rowq)
+    assert np.array_equal(f32bits(rscales), np32bits(rows_s))
 
 
 def test_permute_e4m3_bit_exact():

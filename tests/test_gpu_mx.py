@@ -106,6 +106,18 @@ def test_quantize_token_blocks_mx_bit_exact(gather):
     # (indexing only)
     assert np.array_equal(u8(codes), rq)
     assert np.array_equal(device_layout.mx_token_block_scales(u8(sbt)[:NB], off), rs)
+    # the same pass with the 1 x 32 row blocks: rows as moe_quantize_rows_mx
+    codes2 = torch.full((P, C), 0xAB, dtype=torch.uint8, device="cuda")
+    sbt2 = torch.full((cap, C, 4), 0xCD, dtype=torch.uint8, device="cuda")
+    rcodes = torch.full((P, C), 0xEF, dtype=torch.uint8, device="cuda")
+    rsb = torch.full((P, C // 32), 0x11, dtype=torch.uint8, device="cuda")
+    tre.moe_quantize_token_blocks_with_rows_mx(
+        torch.from_numpy(off).cuda(), E, P, src.cuda(),
+        None if src_row is None else torch.from_numpy(src_row).cuda(), blk, codes2, sbt2, rcodes, rsb)
+    assert torch.equal(codes2, codes) and torch.equal(sbt2[:NB], sbt[:NB])
+    rowq, rows_b = oracle.quant_mx_rows(vals)
+    assert np.array_equal(u8(rcodes), rowq)
+    assert np.array_equal(u8(rsb), rows_b)
 
 
 def test_permute_mx_bit_exact():

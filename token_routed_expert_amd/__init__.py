@@ -14,7 +14,8 @@ from .ops import (E4M3Weights, MXWeights, MoeError, make_shape, moe_aux_loss, mo
                   moe_layer_bwd, moe_layer_fwd, moe_permute, moe_permute_e4m3, moe_permute_noalloc,
                   moe_quantize_rows, moe_quantize_token_blocks, moe_quantize_weights, moe_route,
                   moe_status_str, moe_token_block_capacity, moe_unpermute, moe_workspace_bytes,
-                  moe_probe_mfma)
+                  moe_probe_mfma, moe_quantize_token_blocks_with_rows,
+                  moe_quantize_token_blocks_with_rows_mx)
 
 __all__ = ["MoeError", "make_shape", "moe_route", "moe_permute", "moe_unpermute",
            "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_layer_fwd", "moe_layer_bwd",
@@ -27,4 +28,5 @@ __all__ = ["MoeError", "make_shape", "moe_route", "moe_permute", "moe_unpermute"
            "moe_grouped_gemm_fwd_mx", "moe_grouped_gemm_bwd_mx", "moe_probe_mfma",
            "moe_permute_noalloc", "moe_grouped_gemm_fwd_gather",
            "moe_grouped_gemm_bwd_gather", "moe_route_aux",
-           "moe_aux_loss_final", "_native"]
+           "moe_aux_loss_final", "moe_quantize_token_blocks_with_rows",
+           "moe_quantize_token_blocks_with_rows_mx", "_native"]

@@ -76,6 +76,8 @@ _PROTOS = {
     "moe_quantize_weights": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "moe_token_block_capacity": (C.c_int64, [_I64, _I64]),
     "moe_quantize_token_blocks": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "moe_quantize_token_blocks_with_rows": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                                      _P]),
     "moe_permute_e4m3": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
                                    C.c_size_t, _P]),
     "moe_grouped_gemm_fwd_e4m3": (C.c_int, [_SH, _P, _P, _P, C.POINTER(moe_e4m3_weights), _P, _P,
@@ -86,6 +88,8 @@ _PROTOS = {
     "moe_quantize_rows_mx": (C.c_int, [_P, C.c_int32, _I64, _I64, _P, _P, _P]),
     "moe_quantize_weights_mx": (C.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "moe_quantize_token_blocks_mx": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "moe_quantize_token_blocks_with_rows_mx": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P,
+                                                         _P, _P]),
     "moe_permute_mx": (C.c_int, [_SH, _P, _P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
                                  C.c_size_t, _P]),
     "moe_grouped_gemm_fwd_mx": (C.c_int, [_SH, _P, _P, _P, C.POINTER(moe_mx_weights), _P, _P,

@@ -141,13 +141,19 @@ int quant_rows_mx_launch(const void* src, bool src_f32, int64_t rows, int64_t co
                          uint8_t* codes, uint8_t* sb, hipStream_t s);
 int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uint8_t* codes,
                             uint8_t* sb, uint8_t* codes_t, uint8_t* sbt, hipStream_t s);
+// (rcodes != NULL: the same pass also writes the rows' 1 x 32 blocks, rcodes
+// [P][C] and bytes rsb [P][C/32], as quant_rows_mx_launch would)
 int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
                            const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
-                           uint8_t* sbt, hipStream_t s);  // bound on sum_e ceil(m_e / 128)
+                           uint8_t* sbt, hipStream_t s, uint8_t* rcodes = nullptr,
+                           uint8_t* rsb = nullptr);  // bound on sum_e ceil(m_e / 128)
 int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t s);
+// (rcodes != NULL: the same pass also writes the rows' 1 x 128 blocks, rcodes
+// [P][C] and rscales [P][C/128], as quant_rows_launch would)
 int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
                         const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
-                        float* scales, hipStream_t s);
+                        float* scales, hipStream_t s, uint8_t* rcodes = nullptr,
+                        float* rscales = nullptr);
 // permute.hip: rows of e4m3 codes [T][d] and their scales [T][d/128]
 int permute_e4m3_launch(const uint8_t* codes, const float* scales, const int32_t* row_of, int T,
                         int k, int d, uint8_t* dst_codes, float* dst_scales, hipStream_t s);

@@ -333,10 +333,16 @@ __device__ __forceinline__ void tokblk_load(const bf16_t* __restrict__ src,
   }
 }
 
+// ROWS: the same pass also writes the 1 x 128 row blocks of its rows (the
+// blocks of moe_quantize_rows: each row's 128 columns of the workgroup are one
+// block), rcodes [P][C] and rscales [P][C/128], bit-identical to
+// quant_rows_kernel's.  A row's maximum comes from the 16 lanes that hold it.
+template <bool ROWS>
 __global__ __launch_bounds__(256) void quant_tokblk_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
-    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    uint8_t* __restrict__ codes, float* __restrict__ scales, uint8_t* __restrict__ rcodes,
+    float* __restrict__ rscales) {
   __shared__ __attribute__((aligned(16))) float red[4][128];
   const int ncb = C >> 7, b = (int)blockIdx.x / ncb, cb = (int)blockIdx.x - b * ncb;
   const int tid = threadIdx.x;
@@ -397,6 +403,44 @@ __global__ __launch_bounds__(256) void quant_tokblk_kernel(
     emit(std::true_type{});
   else
     emit(std::false_type{});
+  if constexpr (ROWS) {
+    float rsc[8], ry[8];
+    bool rz[8], rfast = true;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(bf16_at(raw[i], q)));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      rsc[i] = block_scale(mx);
+      ry[i] = 1.0f / rsc[i];
+      rz[i] = mx == 0.0f;
+      rfast = rfast && rsc[i] >= kFastDivMin;
+    }
+    uint8_t* const rdst = rcodes + (size_t)r0 * C + (size_t)cb * 128 + 8 * cg;
+    float* const rsdst = rscales + (size_t)r0 * (C >> 7) + cb;
+    auto emit_rows = [&](auto fst) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          lo |= quant1s<decltype(fst)::value>(bf16_at(raw[i], q), rsc[i], ry[i], rz[i]) << (8 * q);
+          hi |= quant1s<decltype(fst)::value>(bf16_at(raw[i], 4 + q), rsc[i], ry[i], rz[i]) << (8 * q);
+        }
+        const int r = 8 * rq + i;
+        if (r < nr) {
+          *(uint2*)(rdst + (size_t)r * C) = make_uint2(lo, hi);
+          if (cg == 0) rsdst[(size_t)r * (C >> 7)] = rsc[i];
+        }
+      }
+    };
+    if (__all(rfast))
+      emit_rows(std::true_type{});
+    else
+      emit_rows(std::false_type{});
+  }
 }
 
 // ================================================================ MXFP8
@@ -554,10 +598,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void q
 // stage's words for 256 columns are 1 KB in a row.  With the thread layout of
 // quant_tokblk_kernel, wavefront w holds exactly the rows of group w, so each
 // group's maxima need only shuffles within the wavefront.
+// ROWS: also the 1 x 32 row blocks of its rows, rcodes [P][C] and bytes
+// rsb [P][C/32], bit-identical to quant_rows_mx_kernel's (a block is 4 lanes).
+template <bool ROWS>
 __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ blk, int E, int C,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ sbt) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ sbt, uint8_t* __restrict__ rcodes,
+    uint8_t* __restrict__ rsb) {
   __shared__ __attribute__((aligned(4))) uint8_t cs[128][4];  // [column][group]
   const int ncb = C >> 7, b = (int)blockIdx.x / ncb, cb = (int)blockIdx.x - b * ncb;
   const int tid = threadIdx.x;
@@ -589,6 +637,32 @@ __global__ __launch_bounds__(256) void quant_tokblk_mx_kernel(
     }
     const int r = 8 * rq + i;
     if (r < nr) *(uint2*)(dst + (size_t)r * C) = make_uint2(lo, hi);
+  }
+  if constexpr (ROWS) {
+    uint8_t* const rdst = rcodes + (size_t)r0 * C + (size_t)cb * 128 + 8 * cg;
+    uint8_t* const rsdst = rsb + (size_t)r0 * (C >> 5) + cb * 4 + (cg >> 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(bf16_at(raw[i], q)));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 4));
+      const int s = mx_exp(mx);
+      const float rinv = mx_inv(s);
+      const bool rz = mx == 0.0f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo |= mx_code(bf16_at(raw[i], q), rinv, rz) << (8 * q);
+        hi |= mx_code(bf16_at(raw[i], 4 + q), rinv, rz) << (8 * q);
+      }
+      const int r = 8 * rq + i;
+      if (r < nr) {
+        *(uint2*)(rdst + (size_t)r * C) = make_uint2(lo, hi);
+        if ((cg & 3) == 0) rsdst[(size_t)r * (C >> 5)] = (uint8_t)(s + 127);
+      }
+    }
   }
   __syncthreads();
   if (tid < 128)
@@ -623,12 +697,17 @@ int quant_weights_mx_launch(const float* W, int64_t E, int64_t R, int64_t C, uin
 
 int quant_tokblk_mx_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
                            const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
-                           uint8_t* sbt, hipStream_t s) {
+                           uint8_t* sbt, hipStream_t s, uint8_t* rcodes, uint8_t* rsb) {
   const int64_t nb = tokblk_max_blocks(P, E);
   if (nb == 0) return MOE_OK;
   if (nb * (C / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // one block per (b, cb)
-  quant_tokblk_mx_kernel<<<dim3((unsigned)(nb * (C / 128))), 256, 0, s>>>(
-      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, codes, sbt);
+  const dim3 grid((unsigned)(nb * (C / 128)));
+  if (rcodes)
+    quant_tokblk_mx_kernel<true><<<grid, 256, 0, s>>>((const bf16_t*)src, src_row, offsets, blk, E,
+                                                      (int)C, codes, sbt, rcodes, rsb);
+  else
+    quant_tokblk_mx_kernel<false><<<grid, 256, 0, s>>>((const bf16_t*)src, src_row, offsets, blk, E,
+                                                       (int)C, codes, sbt, nullptr, nullptr);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -667,12 +746,17 @@ int tokblk_table_launch(const int32_t* offsets, int E, int32_t* blk, hipStream_t
 
 int quant_tokblk_launch(const void* src, const int32_t* src_row, const int32_t* offsets,
                         const int32_t* blk, int E, int64_t P, int64_t C, uint8_t* codes,
-                        float* scales, hipStream_t s) {
+                        float* scales, hipStream_t s, uint8_t* rcodes, float* rscales) {
   const int64_t nb = tokblk_max_blocks(P, E);
   if (nb == 0) return MOE_OK;
   if (nb * (C / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // one block per (b, cb)
-  quant_tokblk_kernel<<<dim3((unsigned)(nb * (C / 128))), 256, 0, s>>>(
-      (const bf16_t*)src, src_row, offsets, blk, E, (int)C, codes, scales);
+  const dim3 grid((unsigned)(nb * (C / 128)));
+  if (rcodes)
+    quant_tokblk_kernel<true><<<grid, 256, 0, s>>>((const bf16_t*)src, src_row, offsets, blk, E,
+                                                   (int)C, codes, scales, rcodes, rscales);
+  else
+    quant_tokblk_kernel<false><<<grid, 256, 0, s>>>((const bf16_t*)src, src_row, offsets, blk, E,
+                                                    (int)C, codes, scales, nullptr, nullptr);
   TRE_LAUNCH_CHECK();
   return MOE_OK;
 }

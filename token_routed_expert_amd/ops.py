@@ -155,6 +155,16 @@ def moe_quantize_token_blocks(offsets, E, P, src, src_row, blk, codes, scales, s
            "moe_quantize_token_blocks")
 
 
+def moe_quantize_token_blocks_with_rows(offsets, E, P, src, src_row, blk, codes, scales, row_codes,
+                                        row_scales, stream=None):
+    """moe_quantize_token_blocks plus the 1 x 128 row blocks of the same rows, in one pass."""
+    Cc = src.shape[1]
+    _check(N.lib().moe_quantize_token_blocks_with_rows(
+        _ptr(offsets, I32), int(E), int(P), _ptr(src), _ptr(src_row, I32), Cc, _ptr(blk, I32),
+        _ptr(codes), _ptr(scales, F32), _ptr(row_codes), _ptr(row_scales, F32), _stream(stream)),
+        "moe_quantize_token_blocks_with_rows")
+
+
 def moe_permute_e4m3(sh, codes, scales, topk_idx, build_map, counts, offsets, row_of, token_of,
                      dst_codes, dst_scales, ws, stream=None):
     _check(N.lib().moe_permute_e4m3(C.byref(sh), _ptr(codes), _ptr(scales, F32),
@@ -223,6 +233,16 @@ def moe_quantize_token_blocks_mx(offsets, E, P, src, src_row, blk, codes, scales
                                                 _ptr(src_row, I32), Cc, _ptr(blk, I32),
                                                 _ptr(codes, U8), _ptr(scales, U8),
                                                 _stream(stream)), "moe_quantize_token_blocks_mx")
+
+
+def moe_quantize_token_blocks_with_rows_mx(offsets, E, P, src, src_row, blk, codes, scales,
+                                           row_codes, row_scales, stream=None):
+    """moe_quantize_token_blocks_mx plus the 1 x 32 row blocks of the same rows, in one pass."""
+    Cc = src.shape[1]
+    _check(N.lib().moe_quantize_token_blocks_with_rows_mx(
+        _ptr(offsets, I32), int(E), int(P), _ptr(src), _ptr(src_row, I32), Cc, _ptr(blk, I32),
+        _ptr(codes, U8), _ptr(scales, U8), _ptr(row_codes, U8), _ptr(row_scales, U8),
+        _stream(stream)), "moe_quantize_token_blocks_with_rows_mx")
 
 
 def moe_permute_mx(sh, codes, scales, topk_idx, build_map, counts, offsets, row_of, token_of,
