@@ -9,10 +9,10 @@
 // weights, and 128 tokens per column for the operands of the weight
 // gradients, so every scale block spans 128 values of the contraction axis.
 //
-// The four products with ragged M (an expert's permuted rows) read both
-// operands with the contraction axis contiguous (C[m][n] = sum_k A[m][k]
-// B[n][k]); the weight quantiser stores the transposed codes the forward
-// products need:
+// The four products with ragged M (an expert's permuted rows) read A with the
+// contraction axis contiguous (C[m][n] = sum_k A[m][k] B[n][k]), and B as
+// listed (the MXFP8 weight quantiser stores the transposed codes its forward
+// products read):
 //
 //   op          A (rows x K)                 B (rows x K)               K
 //   FC1_FWD     xp codes [P][d]              W1^T, W3^T codes [f][d]    d

@@ -16,13 +16,14 @@
 // Three block shapes, one kernel each:
 //  * rows (1 x 128 along a row): activation operands of the forward and
 //    data-gradient GEMMs, whose contraction runs along the row;
-//  * tiles (128 x 128): expert weights, from fp32 masters; the kernel also
-//    writes the transposed codes, so that every GEMM can read its weight
-//    operand with the contraction axis contiguous;
+//  * tiles (128 x 128): expert weights, from fp32 masters; one copy serves
+//    both orientations (the forward GEMMs read it MN-contiguous), and the
+//    kernel can also write the transposed codes;
 //  * token blocks (128 consecutive rows of one expert, per column): operands
 //    of the weight-gradient GEMMs, whose contraction runs over the expert's
-//    rows; written transposed (column-major over a padded row axis in which
-//    every expert starts at a multiple of 128 and padding codes are 0).
+//    rows; written row-major [P][C] like the source (the GEMMs read them
+//    MN-contiguous), optionally with the rows' 1 x 128 blocks in the same
+//    pass.
 #include <type_traits>
 
 #include "common.h"
