@@ -69,8 +69,6 @@ def check_dot(name, got, dY, o, row_of):
                                      (17, 4, 2, 16384)])
 def test_combine_bwd(dtype, T, E, k, d):
     import token_routed_expert_amd as tre
-    if dtype == "f32" and d == 16384:
-        pytest.skip("fp32 rows of 16384 exceed the 32 KiB row limit")
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
     _, _, idx, prob, counts, row_of, _ = routed(T, E, k, seed=T + d)
     P = T * k
@@ -81,6 +79,12 @@ def test_combine_bwd(dtype, T, E, k, d):
     ro = torch.from_numpy(row_of).cuda()
     dO = torch.full((P, d), float("nan"), dtype=dt, device="cuda")
     dprob = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    if dtype == "f32" and d == 16384:
+        # fp32 rows of 16384 values (64 KiB) exceed what one block keeps of
+        # dY[t]: the call is refused before anything is launched
+        with pytest.raises(tre.MoeError, match="MOE_ERR_UNSUPPORTED"):
+            tre.moe_combine_bwd(sh, dY.cuda(), o.cuda(), ro, prob, dO, dprob)
+        return
     tre.moe_combine_bwd(sh, dY.cuda(), o.cuda(), ro, prob, dO, dprob)
     # dO: exactly the scaled permutation
     dO_ref = torch.empty_like(dO)
